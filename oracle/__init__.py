@@ -1,0 +1,12 @@
+"""TEST INFRASTRUCTURE ONLY: the reference (oracle) for the verification step.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  It shares no code with the GPU library
+(``hierarchical_sparse_kv_verify_amd``) and never imports it.
+"""
+from .model import (  # noqa: F401
+    CLS_HOT, CLS_MISS, CLS_RESIDENT, HOT, RESIDENT, STAGED,
+    HierOracle, OracleConfig, StepResult, loc_code, ring_addr, ring_rows, staging_bytes,
+    to_bf16_bits,
+)
+from . import native  # noqa: F401
