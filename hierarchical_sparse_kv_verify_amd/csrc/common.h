@@ -1,0 +1,108 @@
+// Internal declarations shared by the HIP sources of libkvhier.so (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvh {
+
+// ---------------------------------------------------------------- location codes
+// tier in bits 30..29, index in bits 28..0, -1 = none (see include/kv_hier.h)
+constexpr int kTierShift = 29;
+constexpr int32_t kIndexMask = (1 << kTierShift) - 1;
+constexpr int32_t kTierHot = 0, kTierStaged = 1, kTierResident = 2, kTierRing = 3;
+__host__ __device__ inline int32_t make_loc(int32_t tier, int32_t idx) { return (tier << kTierShift) | idx; }
+__host__ __device__ inline int32_t loc_tier(int32_t code) { return code >> kTierShift; }
+__host__ __device__ inline int32_t loc_index(int32_t code) { return code & kIndexMask; }
+
+// ---------------------------------------------------------------- counters
+// Per-request last-step counters and the per-group cumulative counters use
+// the same order as the counter fields of kv_hier_stats.
+enum Counter {
+  C_ACTIVE_REQ = 0, C_ACTIVE_Q, C_SEL, C_PAD, C_INVALID, C_UNION, C_U_RES, C_U_HOT, C_U_MISS,
+  C_PROMOTED, C_OVERFLOW, C_S_RES, C_S_HOT, C_S_MISS, C_NUM
+};
+
+// per-request info written by the plan kernel
+enum ReqInfo { I_NUNION = 0, I_NMISS, I_NPROMOTE, I_NACTIVE, I_NR, I_NUM = 8 };
+
+// ---------------------------------------------------------------- plan
+struct PlanArgs {
+  const int32_t* topk;       // [N][Q][k]
+  const int32_t* causal;     // [N][Q]
+  const int32_t* res_map;    // [N][L] row -> resident pool index or -1
+  int32_t* slot_map;         // [N][L] row -> hot slot or -1
+  int32_t* slot_row;         // [N][B]
+  int32_t* slot_lu;          // [N][B]
+  int32_t* union_rows;       // [N][Q*k]
+  int32_t* union_loc;        // [N][Q*k]
+  int32_t* miss_rows;        // [N][Q*k]
+  int32_t* victims;          // [N][Q*k]
+  int32_t* loc;              // [N][Q][k]
+  int32_t* req_info;         // [N][I_NUM]
+  int64_t* req_counts;       // [N][C_NUM] last step
+  unsigned long long* cum;   // [C_NUM] cumulative
+  int N, Q, k, B, L, t;
+  int chunk_words;           // bitmap words per row chunk (rows per chunk = 32 * chunk_words)
+  int sort_cap;              // power of two >= B
+};
+size_t plan_lds_bytes(int Q, int k, int B, int chunk_words, int sort_cap);
+hipError_t launch_plan(const PlanArgs& a, size_t lds, hipStream_t s);
+
+// ---------------------------------------------------------------- copies
+struct HostRowSrc {
+  const uint4* const* prefix;   // device array [n_prefix] of host-mapped prefix bases
+  const uint4* tails;           // host-mapped base of [N][tail_rows][row]
+  int n_prefix, prefix_len, tail_rows, row16;   // row16 = 16-byte chunks per row
+};
+
+// miss gather: for r in [r0, r1), i < req_info[r][I_NMISS]:
+//   staging[(r*QK + i)] = host row miss_rows[r][i]
+hipError_t launch_miss_gather(const HostRowSrc& src, const int32_t* miss_rows, const int32_t* req_info,
+                              uint4* staging, int QK, int r0, int r1, int wg_per_req, hipStream_t s);
+// promote: hot[(r*B + victims[r][i])] = staging[r*QK + i], i < req_info[r][I_NPROMOTE]
+hipError_t launch_promote(const uint4* staging, const int32_t* victims, const int32_t* req_info,
+                          uint4* hot, int QK, int B, int row16, int r0, int r1, hipStream_t s);
+// ring write: ring[r*Rd + causal[r][j] % Rd] = rows[r][j] for active j
+hipError_t launch_ring_write(const uint4* rows, const int32_t* causal, uint4* ring, int N, int Q,
+                             int Rd, int row16, hipStream_t s);
+// setup gather from host: dst[dst_idx[i]] = host row (req[i], row[i]), i < n
+hipError_t launch_host_rows_to_dev(const HostRowSrc& src, const int32_t* req, const int32_t* rows,
+                                   const int64_t* dst_idx, int n, uint4* dst, hipStream_t s);
+// commit: for r with acc[r] >= 0, rows pos = nbefore[r] .. nbefore[r]+acc[r] of every group:
+//   host tail row (pos - prefix_len) of r = ring row
+struct CommitGroup { const uint4* ring; uint4* tails; };
+hipError_t launch_commit(const CommitGroup* groups, int G, const int32_t* nbefore, const int32_t* acc,
+                         int N, int Qmax, int Rd, int prefix_len, int tail_rows, int row16, hipStream_t s);
+// read rows at location codes into dst [n][row]
+struct PoolView { const uint4* hot; const uint4* staging; const uint4* resident; const uint4* ring; };
+hipError_t launch_read_rows(const PoolView& pv, const int32_t* locs, int n, uint4* dst, int row16,
+                            hipStream_t s);
+// fill 32-bit words with a value (used instead of memset inside the step)
+hipError_t launch_fill32(uint32_t* p, uint32_t v, size_t n, hipStream_t s);
+
+// ---------------------------------------------------------------- attention
+struct AttnArgs {
+  const uint16_t* q;          // [N][Q][H][d_qk]
+  const int32_t* loc;         // [N][Q][k]
+  const int32_t* causal;      // [N][Q]
+  const int32_t* ring_lo;     // [N]
+  const uint16_t* hot;        // hot pool of the group
+  const uint16_t* staging;    // arena of the group
+  const uint16_t* resident;   // resident pool (may be null)
+  const uint16_t* ring;       // ring of the group
+  uint16_t* out;              // [N][Q][H][d_v]
+  float* part_o;              // [N*Q*HG*S][32*HB][d_v] partial numerators (splits > 1)
+  float* part_ml;             // [N*Q*HG*S][32*HB][2]
+  int N, Q, k, H, W, Rd, block_only;
+  int r0, r1;                 // request range of this launch
+  int splits, head_groups;
+  float scale_log2;           // softmax scale * log2(e)
+};
+// supported layouts; returns hipErrorInvalidValue for others
+bool attn_layout_supported(int row_elems, int d_qk, int v_off, int d_v);
+int attn_heads_per_wg(int H);
+hipError_t launch_attn(const AttnArgs& a, int row_elems, int d_qk, int v_off, int d_v, hipStream_t s);
+hipError_t launch_attn_combine(const AttnArgs& a, int d_v, hipStream_t s);
+
+}  // namespace kvh

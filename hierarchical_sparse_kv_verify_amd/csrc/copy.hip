@@ -1,0 +1,206 @@
+// Row movement kernels of the verification step (gfx950).
+//
+//  - miss gather: each distinct missing row is read once from pinned host
+//    memory (mapped into the GPU address space) and written to its staging
+//    row ("Adaptive DHiSparse", §3.3 and Figure 3 callout 2; the pages'
+//    resolver copies over a grid that scales with the batch, §3.2).  Reads
+//    are whole 1152-byte (or 512-byte) rows split in 16-byte lanes, so every
+//    PCIe read request covers full 64/128-byte lines; the host side of the
+//    link measured the same rate for this pattern as for a bulk copy.
+//  - promote: staged rows that took a victim slot are copied back to their
+//    stable hot-cache address after the step's readers finish (§3.4).
+//  - ring write: the new KV row of every active query goes to
+//    phi(r, p) = r*R_d + (p mod R_d) (eq. 10; Figure 3 callout 4).
+//  - commit: committed ring rows get their host copy (eq. 7 and the text
+//    after eq. 8: host backup of committed rows follows verification).
+// Loop bounds come from device-side counts, so no host round trip is needed
+// between resolution and movement.
+#include "common.h"
+
+namespace kvh {
+namespace {
+
+__device__ inline const uint4* host_row(const HostRowSrc& s, int r, int row) {
+  if (row < s.prefix_len)
+    return s.prefix[r % s.n_prefix] + size_t(row) * s.row16;
+  return s.tails + (size_t(r) * s.tail_rows + (row - s.prefix_len)) * s.row16;
+}
+
+__global__ __launch_bounds__(256) void miss_gather_kernel(HostRowSrc src, const int32_t* __restrict__ miss_rows,
+                                                          const int32_t* __restrict__ req_info,
+                                                          uint4* __restrict__ staging, int QK, int r0) {
+  const int r = r0 + blockIdx.y;
+  const int n = req_info[r * I_NUM + I_NMISS];
+  const int row16 = src.row16;
+  const size_t total = size_t(n) * row16;
+  const int32_t* mr = miss_rows + size_t(r) * QK;
+  uint4* dst = staging + size_t(r) * QK * row16;
+  const size_t stride = size_t(gridDim.x) * blockDim.x;
+  size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < total; i += 4 * stride) {
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const size_t ii = i + u * stride;
+      const int row = static_cast<int>(ii / row16), c = static_cast<int>(ii % row16);
+      v[u] = host_row(src, r, mr[row])[c];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) dst[i + u * stride] = v[u];
+  }
+  for (; i < total; i += stride) {
+    const int row = static_cast<int>(i / row16), c = static_cast<int>(i % row16);
+    dst[i] = host_row(src, r, mr[row])[c];
+  }
+}
+
+__global__ __launch_bounds__(256) void promote_kernel(const uint4* __restrict__ staging,
+                                                      const int32_t* __restrict__ victims,
+                                                      const int32_t* __restrict__ req_info,
+                                                      uint4* __restrict__ hot, int QK, int B, int row16, int r0) {
+  const int r = r0 + blockIdx.y;
+  const int n = req_info[r * I_NUM + I_NPROMOTE];
+  const size_t total = size_t(n) * row16;
+  const size_t stride = size_t(gridDim.x) * blockDim.x;
+  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int row = static_cast<int>(i / row16), c = static_cast<int>(i % row16);
+    const int slot = victims[size_t(r) * QK + row];
+    hot[(size_t(r) * B + slot) * row16 + c] = staging[(size_t(r) * QK + row) * row16 + c];
+  }
+}
+
+__global__ __launch_bounds__(256) void ring_write_kernel(const uint4* __restrict__ rows,
+                                                         const int32_t* __restrict__ causal,
+                                                         uint4* __restrict__ ring, int N, int Q, int Rd, int row16) {
+  const size_t total = size_t(N) * Q * row16;
+  const size_t stride = size_t(gridDim.x) * blockDim.x;
+  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const size_t rj = i / row16;
+    const int c = static_cast<int>(i % row16);
+    const int pos = causal[rj];
+    if (pos < 0) continue;
+    const size_t r = rj / Q;
+    ring[(r * Rd + size_t(pos % Rd)) * row16 + c] = rows[i];
+  }
+}
+
+__global__ __launch_bounds__(256) void host_rows_to_dev_kernel(HostRowSrc src, const int32_t* __restrict__ req,
+                                                               const int32_t* __restrict__ rows,
+                                                               const int64_t* __restrict__ dst_idx, int n,
+                                                               uint4* __restrict__ dst) {
+  const int row16 = src.row16;
+  const size_t total = size_t(n) * row16;
+  const size_t stride = size_t(gridDim.x) * blockDim.x;
+  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int x = static_cast<int>(i / row16), c = static_cast<int>(i % row16);
+    dst[size_t(dst_idx[x]) * row16 + c] = host_row(src, req[x], rows[x])[c];
+  }
+}
+
+__global__ __launch_bounds__(256) void commit_kernel(const CommitGroup* __restrict__ groups,
+                                                     const int32_t* __restrict__ nbefore,
+                                                     const int32_t* __restrict__ acc, int Qmax, int Rd,
+                                                     int prefix_len, int tail_rows, int row16) {
+  const int r = blockIdx.y, g = blockIdx.z;
+  const int a = acc[r];
+  if (a < 0) return;
+  const int n0 = nbefore[r];
+  const int total = (a + 1) * row16;
+  const uint4* ring = groups[g].ring;
+  uint4* tails = groups[g].tails;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x) {
+    const int d = i / row16, c = i % row16;
+    const int pos = n0 + d;
+    tails[(size_t(r) * tail_rows + (pos - prefix_len)) * row16 + c] =
+        ring[(size_t(r) * Rd + size_t(pos % Rd)) * row16 + c];
+  }
+  __threadfence_system();
+}
+
+__global__ __launch_bounds__(256) void read_rows_kernel(PoolView pv, const int32_t* __restrict__ locs, int n,
+                                                        uint4* __restrict__ dst, int row16) {
+  const size_t total = size_t(n) * row16;
+  const size_t stride = size_t(gridDim.x) * blockDim.x;
+  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int x = static_cast<int>(i / row16), c = static_cast<int>(i % row16);
+    const int code = locs[x];
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (code >= 0) {
+      const int tier = loc_tier(code);
+      const size_t idx = size_t(loc_index(code));
+      const uint4* base = tier == kTierHot ? pv.hot : tier == kTierStaged ? pv.staging
+                          : tier == kTierResident ? pv.resident : pv.ring;
+      if (base) v = base[idx * row16 + c];
+    }
+    dst[i] = v;
+  }
+}
+
+__global__ __launch_bounds__(256) void fill32_kernel(uint32_t* p, uint32_t v, size_t n) {
+  const size_t stride = size_t(gridDim.x) * blockDim.x;
+  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = v;
+}
+
+inline unsigned grid_for(size_t work, unsigned cap) {
+  size_t g = (work + 255) / 256;
+  if (g < 1) g = 1;
+  return static_cast<unsigned>(g < cap ? g : cap);
+}
+
+}  // namespace
+
+hipError_t launch_miss_gather(const HostRowSrc& src, const int32_t* miss_rows, const int32_t* req_info,
+                              uint4* staging, int QK, int r0, int r1, int wg_per_req, hipStream_t s) {
+  if (r1 <= r0) return hipSuccess;
+  hipLaunchKernelGGL(miss_gather_kernel, dim3(wg_per_req, r1 - r0), dim3(256), 0, s, src, miss_rows,
+                     req_info, staging, QK, r0);
+  return hipGetLastError();
+}
+
+hipError_t launch_promote(const uint4* staging, const int32_t* victims, const int32_t* req_info, uint4* hot,
+                          int QK, int B, int row16, int r0, int r1, hipStream_t s) {
+  if (r1 <= r0) return hipSuccess;
+  hipLaunchKernelGGL(promote_kernel, dim3(4, r1 - r0), dim3(256), 0, s, staging, victims, req_info, hot, QK,
+                     B, row16, r0);
+  return hipGetLastError();
+}
+
+hipError_t launch_ring_write(const uint4* rows, const int32_t* causal, uint4* ring, int N, int Q, int Rd,
+                             int row16, hipStream_t s) {
+  const size_t work = size_t(N) * Q * row16;
+  hipLaunchKernelGGL(ring_write_kernel, dim3(grid_for(work, 2048)), dim3(256), 0, s, rows, causal, ring, N, Q,
+                     Rd, row16);
+  return hipGetLastError();
+}
+
+hipError_t launch_host_rows_to_dev(const HostRowSrc& src, const int32_t* req, const int32_t* rows,
+                                   const int64_t* dst_idx, int n, uint4* dst, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(host_rows_to_dev_kernel, dim3(grid_for(size_t(n) * src.row16, 128)), dim3(256), 0, s,
+                     src, req, rows, dst_idx, n, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_commit(const CommitGroup* groups, int G, const int32_t* nbefore, const int32_t* acc, int N,
+                         int Qmax, int Rd, int prefix_len, int tail_rows, int row16, hipStream_t s) {
+  const unsigned gx = static_cast<unsigned>((Qmax * row16 + 255) / 256);
+  hipLaunchKernelGGL(commit_kernel, dim3(gx, N, G), dim3(256), 0, s, groups, nbefore, acc, Qmax, Rd,
+                     prefix_len, tail_rows, row16);
+  return hipGetLastError();
+}
+
+hipError_t launch_read_rows(const PoolView& pv, const int32_t* locs, int n, uint4* dst, int row16,
+                            hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(read_rows_kernel, dim3(grid_for(size_t(n) * row16, 1024)), dim3(256), 0, s, pv, locs, n,
+                     dst, row16);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill32(uint32_t* p, uint32_t v, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(fill32_kernel, dim3(grid_for(n, 4096)), dim3(256), 0, s, p, v, n);
+  return hipGetLastError();
+}
+
+}  // namespace kvh

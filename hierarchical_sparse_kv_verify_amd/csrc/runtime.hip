@@ -1,0 +1,954 @@
+// Host runtime of libkvhier.so: the C ABI declared in include/kv_hier.h.
+//
+// One handle holds, per layer group (payload source), the hot caches, slot
+// tables, row->slot and row->resident maps, the draft ring and the pinned host
+// backing, plus chi staging arenas shared by all groups ("Adaptive
+// DHiSparse", §3.4: arenas are reused across layer groups once readers and
+// copy-back finish).  A step enqueues, on the caller's stream: ring write,
+// resolution plan, then per request chunk the attention and the copy-back;
+// the host fetch of each chunk runs on a side stream and is ordered with
+// events, so the fetch of chunk c+1 overlaps the attention of chunk c.
+// No host synchronisation happens inside a step.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "common.h"
+#include "kv_hier.h"
+
+using namespace kvh;
+
+namespace {
+
+enum TimedKind { K_RING = 0, K_PLAN, K_GATHER, K_ATTN, K_COMBINE, K_PROMOTE, K_NUM };
+
+struct Group {
+  uint16_t* hot = nullptr;
+  int32_t* slot_row = nullptr;
+  int32_t* slot_lu = nullptr;
+  int32_t* slot_map = nullptr;
+  int32_t* res_map = nullptr;
+  uint16_t* resident = nullptr;
+  int64_t res_cursor = 0;
+  std::vector<char> res_set;
+  uint16_t* ring = nullptr;
+  int32_t* ring_lo = nullptr;
+  int32_t *union_rows = nullptr, *union_loc = nullptr, *miss_rows = nullptr, *victims = nullptr;
+  int32_t *loc = nullptr, *req_info = nullptr;
+  int64_t* req_counts = nullptr;
+  unsigned long long* cum = nullptr;
+  std::vector<void*> prefix_host;
+  void* tails_host = nullptr;
+  const uint4** prefix_table = nullptr;   // device array of host-mapped prefix bases
+  const uint4* tails_dev = nullptr;       // host-mapped tails
+  int t = 0;
+  int64_t calls = 0;
+  double ms[K_NUM] = {0};
+  int64_t nt[K_NUM] = {0};
+};
+
+struct Timed {
+  int kind, g;
+  hipEvent_t a, b;
+};
+
+}  // namespace
+
+struct kv_hier {
+  kv_hier_config cfg{};
+  int device = 0;
+  int Rd = 0, QK = 0, row16 = 0, plen = 0, n_prefix = 0, tail_rows = 0, L = 0;
+  size_t row_bytes = 0;
+  std::vector<Group> grp;
+  std::vector<uint16_t*> arena;
+  float* part_o = nullptr;
+  float* part_ml = nullptr;
+  int splits = 1, head_groups = 1, n_chunks = 1;
+  std::vector<int> chunk_lo;
+  int chunk_words = 0, sort_cap = 1;
+  size_t plan_lds = 0;
+  hipStream_t side = nullptr;
+  hipEvent_t ev_plan = nullptr;
+  std::vector<hipEvent_t> ev_fetched;
+  std::vector<std::vector<hipEvent_t>> ev_free;
+  std::vector<std::vector<char>> free_recorded;
+  std::vector<int32_t> hist_len;
+  int32_t* d_commit = nullptr;
+  int32_t* h_commit = nullptr;
+  hipEvent_t ev_commit = nullptr;
+  bool commit_pending = false;
+  CommitGroup* d_commit_groups = nullptr;
+  std::vector<Timed> pending;
+  std::vector<hipEvent_t> pool;
+  std::string err;
+  int64_t bytes_hot = 0, bytes_staging = 0, bytes_ring = 0, bytes_maps = 0, bytes_res = 0, bytes_host = 0;
+};
+
+namespace {
+
+int fail(kv_hier* h, int code, const char* fmt, ...) {
+  if (h) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    h->err = buf;
+  }
+  return code;
+}
+
+#define HIPCHK(h, call)                                                                          \
+  do {                                                                                           \
+    hipError_t e_ = (call);                                                                      \
+    if (e_ != hipSuccess) return fail((h), KV_EHIP, "%s failed: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+template <class T>
+int dev_alloc(kv_hier* h, T** p, size_t count, int64_t* acct) {
+  *p = nullptr;
+  if (count == 0) return KV_OK;
+  void* v = nullptr;
+  if (hipMalloc(&v, count * sizeof(T)) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(h, KV_ENOMEM, "hipMalloc of %zu bytes failed", count * sizeof(T));
+  }
+  *p = static_cast<T*>(v);
+  if (acct) *acct += int64_t(count * sizeof(T));
+  return KV_OK;
+}
+
+int host_alloc(kv_hier* h, void** p, size_t bytes) {
+  *p = nullptr;
+  if (bytes == 0) return KV_OK;
+  if (hipHostMalloc(p, bytes, hipHostMallocDefault) != hipSuccess) {
+    (void)hipGetLastError();
+    *p = nullptr;
+    return fail(h, KV_ENOMEM, "hipHostMalloc of %zu bytes failed", bytes);
+  }
+  h->bytes_host += int64_t(bytes);
+  return KV_OK;
+}
+
+HostRowSrc host_src(const kv_hier* h, const Group& G) {
+  HostRowSrc s;
+  s.prefix = G.prefix_table;
+  s.tails = G.tails_dev;
+  s.n_prefix = h->n_prefix > 0 ? h->n_prefix : 1;
+  s.prefix_len = h->plen;
+  s.tail_rows = h->tail_rows;
+  s.row16 = h->row16;
+  return s;
+}
+
+hipEvent_t take_event(kv_hier* h) {
+  if (!h->pool.empty()) {
+    hipEvent_t e = h->pool.back();
+    h->pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Records a start event when timing is on; returns the pending index or -1.
+int time_begin(kv_hier* h, int kind, int g, hipStream_t s) {
+  if (!(h->cfg.flags & KV_FLAG_TIMING)) return -1;
+  Timed t{kind, g, take_event(h), take_event(h)};
+  if (!t.a || !t.b || hipEventRecord(t.a, s) != hipSuccess) return -1;
+  h->pending.push_back(t);
+  return int(h->pending.size()) - 1;
+}
+
+void time_end(kv_hier* h, int idx, hipStream_t s) {
+  if (idx < 0) return;
+  (void)hipEventRecord(h->pending[idx].b, s);
+}
+
+int drain_timing(kv_hier* h) {
+  for (const Timed& t : h->pending) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, t.a, t.b) == hipSuccess) {
+      h->grp[t.g].ms[t.kind] += ms;
+      h->grp[t.g].nt[t.kind] += 1;
+    } else {
+      (void)hipGetLastError();
+    }
+    h->pool.push_back(t.a);
+    h->pool.push_back(t.b);
+  }
+  h->pending.clear();
+  return KV_OK;
+}
+
+int sync_all(kv_hier* h) {
+  HIPCHK(h, hipDeviceSynchronize());
+  return drain_timing(h);
+}
+
+int check_group(kv_hier* h, int g) {
+  if (!h) return KV_EINVAL;
+  if (g < 0 || g >= h->cfg.n_groups) return fail(h, KV_ESTATE, "group %d outside [0, %d)", g, h->cfg.n_groups);
+  return KV_OK;
+}
+
+int check_req(kv_hier* h, int r) {
+  if (r < 0 || r >= h->cfg.n_req) return fail(h, KV_EINVAL, "request %d outside [0, %d)", r, h->cfg.n_req);
+  return KV_OK;
+}
+
+// Ring size of "Adaptive DHiSparse" §3.4 eq. (9): page-rounded window plus block.
+int ring_size(int W, int p, int kmax) { return p * ((W + p - 1 + kmax + p - 1) / p); }
+
+int upload(kv_hier* h, void* dst, const void* src, size_t bytes) {
+  if (bytes == 0) return KV_OK;
+  HIPCHK(h, hipMemcpy(dst, src, bytes, hipMemcpyHostToDevice));
+  return KV_OK;
+}
+
+int download(kv_hier* h, void* dst, const void* src, size_t bytes) {
+  if (bytes == 0) return KV_OK;
+  HIPCHK(h, hipMemcpy(dst, src, bytes, hipMemcpyDeviceToHost));
+  return KV_OK;
+}
+
+// Scatters values into an int32 device array: base[idx[i]] = val[i] (set-up path).
+__global__ void scatter32_kernel(int32_t* base, const int64_t* idx, const int32_t* val, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) base[idx[i]] = val[i];
+}
+
+int scatter32(kv_hier* h, int32_t* base, const std::vector<int64_t>& idx, const std::vector<int32_t>& val) {
+  const int n = int(idx.size());
+  if (n == 0) return KV_OK;
+  int64_t* di = nullptr;
+  int32_t* dv = nullptr;
+  int rc = dev_alloc(h, &di, size_t(n), nullptr);
+  if (rc) return rc;
+  rc = dev_alloc(h, &dv, size_t(n), nullptr);
+  if (rc) { (void)hipFree(di); return rc; }
+  rc = upload(h, di, idx.data(), size_t(n) * 8);
+  if (!rc) rc = upload(h, dv, val.data(), size_t(n) * 4);
+  if (!rc) {
+    hipLaunchKernelGGL(scatter32_kernel, dim3(std::min(1024, (n + 255) / 256)), dim3(256), 0, nullptr, base, di,
+                       dv, n);
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) rc = fail(h, KV_EHIP, "scatter: %s", hipGetErrorString(e));
+  }
+  (void)hipFree(di);
+  (void)hipFree(dv);
+  return rc;
+}
+
+// Copies host-backing rows (req[i], rows[i]) to dst rows dst_idx[i] (set-up path).
+int rows_from_host(kv_hier* h, const Group& G, const std::vector<int32_t>& req, const std::vector<int32_t>& rows,
+                   const std::vector<int64_t>& dst_idx, uint16_t* dst) {
+  const int n = int(rows.size());
+  if (n == 0) return KV_OK;
+  int32_t *dq = nullptr, *dr = nullptr;
+  int64_t* di = nullptr;
+  int rc = dev_alloc(h, &dq, size_t(n), nullptr);
+  if (!rc) rc = dev_alloc(h, &dr, size_t(n), nullptr);
+  if (!rc) rc = dev_alloc(h, &di, size_t(n), nullptr);
+  if (!rc) rc = upload(h, dq, req.data(), size_t(n) * 4);
+  if (!rc) rc = upload(h, dr, rows.data(), size_t(n) * 4);
+  if (!rc) rc = upload(h, di, dst_idx.data(), size_t(n) * 8);
+  if (!rc) {
+    hipError_t e = launch_host_rows_to_dev(host_src(h, G), dq, dr, di, n, reinterpret_cast<uint4*>(dst), nullptr);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) rc = fail(h, KV_EHIP, "host row copy: %s", hipGetErrorString(e));
+  }
+  (void)hipFree(dq);
+  (void)hipFree(dr);
+  (void)hipFree(di);
+  return rc;
+}
+
+void free_all(kv_hier* h) {
+  for (Group& G : h->grp) {
+    (void)hipFree(G.hot);
+    (void)hipFree(G.slot_row);
+    (void)hipFree(G.slot_lu);
+    (void)hipFree(G.slot_map);
+    (void)hipFree(G.res_map);
+    (void)hipFree(G.resident);
+    (void)hipFree(G.ring);
+    (void)hipFree(G.ring_lo);
+    (void)hipFree(G.union_rows);
+    (void)hipFree(G.union_loc);
+    (void)hipFree(G.miss_rows);
+    (void)hipFree(G.victims);
+    (void)hipFree(G.loc);
+    (void)hipFree(G.req_info);
+    (void)hipFree(G.req_counts);
+    (void)hipFree(G.cum);
+    (void)hipFree(const_cast<uint4**>(G.prefix_table));
+    for (void* p : G.prefix_host) if (p) (void)hipHostFree(p);
+    if (G.tails_host) (void)hipHostFree(G.tails_host);
+  }
+  for (uint16_t* a : h->arena) (void)hipFree(a);
+  (void)hipFree(h->part_o);
+  (void)hipFree(h->part_ml);
+  (void)hipFree(h->d_commit);
+  (void)hipFree(h->d_commit_groups);
+  if (h->h_commit) (void)hipHostFree(h->h_commit);
+  for (auto& t : h->pending) { (void)hipEventDestroy(t.a); (void)hipEventDestroy(t.b); }
+  for (hipEvent_t e : h->pool) (void)hipEventDestroy(e);
+  if (h->ev_plan) (void)hipEventDestroy(h->ev_plan);
+  if (h->ev_commit) (void)hipEventDestroy(h->ev_commit);
+  for (hipEvent_t e : h->ev_fetched) (void)hipEventDestroy(e);
+  for (auto& v : h->ev_free) for (hipEvent_t e : v) (void)hipEventDestroy(e);
+  if (h->side) (void)hipStreamDestroy(h->side);
+}
+
+int validate(kv_hier* h, const kv_hier_config& c) {
+  if (c.n_req <= 0 || c.n_groups <= 0 || c.n_arenas <= 0 || c.hist_cap <= 0 || c.row_elems <= 0 ||
+      c.d_qk <= 0 || c.d_v <= 0 || c.v_off < 0 || c.n_heads <= 0 || c.q_max <= 0 || c.topk <= 0 ||
+      c.hot_slots <= 0 || c.ring_window <= 0 || c.ring_page <= 0 || c.n_prefix < 0 || c.prefix_len < 0 ||
+      c.n_chunks < 0 || c.resident_cap < 0)
+    return fail(h, KV_EINVAL, "non-positive size in config");
+  if (c.q_max > 32) return fail(h, KV_EUNSUPPORTED, "q_max %d > 32", c.q_max);
+  if (int64_t(c.q_max) * c.topk > 65535) return fail(h, KV_EUNSUPPORTED, "q_max*topk > 65535");
+  if (c.d_qk > c.row_elems || c.v_off + c.d_v > c.row_elems) return fail(h, KV_EINVAL, "K/V outside the row");
+  if (c.n_prefix > 0 && (c.prefix_len <= 0 || c.prefix_len > c.hist_cap))
+    return fail(h, KV_EINVAL, "prefix_len must be in (0, hist_cap] with shared prefixes");
+  if (c.n_prefix == 0 && c.prefix_len != 0) return fail(h, KV_EINVAL, "prefix_len without prefixes");
+  if (!attn_layout_supported(c.row_elems, c.d_qk, c.v_off, c.d_v))
+    return fail(h, KV_EUNSUPPORTED, "row layout (%d, %d, %d, %d) has no attention kernel", c.row_elems, c.d_qk,
+                c.v_off, c.d_v);
+  const int64_t lim = int64_t(1) << kTierShift;
+  if (int64_t(c.n_req) * c.hot_slots >= lim || int64_t(c.n_req) * c.q_max * c.topk >= lim ||
+      c.resident_cap >= lim || int64_t(c.hist_cap) >= lim)
+    return fail(h, KV_EUNSUPPORTED, "an index space exceeds 2^29 rows");
+  if (c.hot_slots > 16384) return fail(h, KV_EUNSUPPORTED, "hot_slots > 16384");
+  return KV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kv_hier_last_error(const kv_hier_t* h) { return h ? h->err.c_str() : "null handle"; }
+
+void kv_hier_destroy(kv_hier_t* h) {
+  if (!h) return;
+  (void)hipDeviceSynchronize();
+  free_all(h);
+  delete h;
+}
+
+static int create_impl(kv_hier* h) {
+  int rc = KV_OK;
+  const kv_hier_config& c = h->cfg;
+  (void)hipGetDevice(&h->device);
+  const int N = c.n_req, B = c.hot_slots, L = c.hist_cap;
+  h->L = L;
+  h->QK = c.q_max * c.topk;
+  h->row_bytes = size_t(c.row_elems) * 2;
+  h->row16 = c.row_elems / 8;
+  h->Rd = ring_size(c.ring_window, c.ring_page, c.q_max);
+  h->n_prefix = c.n_prefix;
+  h->plen = c.n_prefix > 0 ? c.prefix_len : 0;
+  h->tail_rows = L - h->plen;
+  h->hist_len.assign(N, 0);
+
+  // plan kernel shared memory: row-chunk bitmap, word prefixes and union codes
+  int sc = 1;
+  while (sc < B) sc <<= 1;
+  h->sort_cap = sc;
+  {
+    const size_t budget = 160 * 1024 - 1024 - ((size_t(B + 31) / 32) * 4 + 16);
+    const size_t qk_bytes = (size_t(h->QK) * 4 + 15) & ~size_t(15);
+    if (qk_bytes + 64 > budget || size_t(sc) * 8 > budget) return fail(h, KV_EUNSUPPORTED, "plan LDS");
+    size_t cw_max = (budget - qk_bytes - 32) / 6;
+    size_t cw = (size_t(L) + 31) / 32;
+    if (cw > cw_max) cw = cw_max;
+    h->chunk_words = int(cw);
+    h->plan_lds = plan_lds_bytes(c.q_max, c.topk, B, h->chunk_words, sc);
+    if (h->plan_lds > 160 * 1024) return fail(h, KV_EUNSUPPORTED, "plan LDS %zu", h->plan_lds);
+  }
+  // request chunks for the fetch/attention pipeline
+  h->n_chunks = c.n_chunks > 0 ? std::min(c.n_chunks, N) : (N >= 64 ? 8 : (N >= 16 ? 4 : 1));
+  for (int i = 0; i <= h->n_chunks; ++i) h->chunk_lo.push_back(int(int64_t(N) * i / h->n_chunks));
+  {
+    const int hpw = attn_heads_per_wg(c.n_heads);
+    h->head_groups = (c.n_heads + hpw - 1) / hpw;
+    const int nc = (N + h->n_chunks - 1) / h->n_chunks;
+    const int64_t wgs = int64_t(nc) * c.q_max * h->head_groups;
+    const int tiles = (c.topk + c.ring_window + 31) / 32;
+    int s = 1;
+    if (wgs < 512) s = int(std::min<int64_t>(8, (512 + wgs - 1) / wgs));
+    s = std::max(1, std::min(s, tiles / 4));
+    h->splits = s;
+    if (s > 1) {
+      const size_t blocks = size_t(N) * c.q_max * h->head_groups * s;
+      rc = dev_alloc(h, &h->part_o, blocks * hpw * c.d_v, &h->bytes_maps);
+      if (!rc) rc = dev_alloc(h, &h->part_ml, blocks * hpw * 2, &h->bytes_maps);
+      if (rc) return rc;
+    }
+  }
+  h->grp.resize(c.n_groups);
+  for (int g = 0; g < c.n_groups; ++g) {
+    Group& G = h->grp[g];
+    G.res_set.assign(N, 0);
+    const size_t NB = size_t(N) * B, NL = size_t(N) * L, NQK = size_t(N) * h->QK;
+    if ((rc = dev_alloc(h, &G.hot, NB * c.row_elems, &h->bytes_hot))) return rc;
+    if ((rc = dev_alloc(h, &G.slot_row, NB, &h->bytes_maps))) return rc;
+    if ((rc = dev_alloc(h, &G.slot_lu, NB, &h->bytes_maps))) return rc;
+    if ((rc = dev_alloc(h, &G.slot_map, NL, &h->bytes_maps))) return rc;
+    if ((rc = dev_alloc(h, &G.res_map, NL, &h->bytes_maps))) return rc;
+    if (c.resident_cap > 0 && (rc = dev_alloc(h, &G.resident, size_t(c.resident_cap) * c.row_elems, &h->bytes_res)))
+      return rc;
+    if ((rc = dev_alloc(h, &G.ring, size_t(N) * h->Rd * c.row_elems, &h->bytes_ring))) return rc;
+    if ((rc = dev_alloc(h, &G.ring_lo, size_t(N), &h->bytes_maps))) return rc;
+    if ((rc = dev_alloc(h, &G.union_rows, NQK, &h->bytes_maps))) return rc;
+    if ((rc = dev_alloc(h, &G.union_loc, NQK, &h->bytes_maps))) return rc;
+    if ((rc = dev_alloc(h, &G.miss_rows, NQK, &h->bytes_maps))) return rc;
+    if ((rc = dev_alloc(h, &G.victims, NQK, &h->bytes_maps))) return rc;
+    if ((rc = dev_alloc(h, &G.loc, NQK, &h->bytes_maps))) return rc;
+    if ((rc = dev_alloc(h, &G.req_info, size_t(N) * I_NUM, &h->bytes_maps))) return rc;
+    if ((rc = dev_alloc(h, &G.req_counts, size_t(N) * C_NUM, &h->bytes_maps))) return rc;
+    if ((rc = dev_alloc(h, &G.cum, size_t(C_NUM), &h->bytes_maps))) return rc;
+    const uint32_t neg = 0xffffffffu;
+    if (launch_fill32(reinterpret_cast<uint32_t*>(G.slot_row), neg, NB, nullptr) != hipSuccess ||
+        launch_fill32(reinterpret_cast<uint32_t*>(G.slot_lu), 0, NB, nullptr) != hipSuccess ||
+        launch_fill32(reinterpret_cast<uint32_t*>(G.slot_map), neg, NL, nullptr) != hipSuccess ||
+        launch_fill32(reinterpret_cast<uint32_t*>(G.res_map), neg, NL, nullptr) != hipSuccess ||
+        launch_fill32(reinterpret_cast<uint32_t*>(G.ring), 0, size_t(N) * h->Rd * c.row_elems / 2, nullptr) !=
+            hipSuccess ||
+        launch_fill32(reinterpret_cast<uint32_t*>(G.ring_lo), 0, size_t(N), nullptr) != hipSuccess ||
+        launch_fill32(reinterpret_cast<uint32_t*>(G.req_info), 0, size_t(N) * I_NUM, nullptr) != hipSuccess ||
+        launch_fill32(reinterpret_cast<uint32_t*>(G.req_counts), 0, size_t(N) * C_NUM * 2, nullptr) !=
+            hipSuccess ||
+        launch_fill32(reinterpret_cast<uint32_t*>(G.cum), 0, size_t(C_NUM) * 2, nullptr) != hipSuccess) {
+      return fail(h, KV_EHIP, "initial fill failed");
+    }
+    // pinned host backing, mapped into the device address space
+    const int np = c.n_prefix;
+    G.prefix_host.assign(np > 0 ? np : 0, nullptr);
+    std::vector<const uint4*> table(np > 0 ? np : 1, nullptr);
+    for (int p = 0; p < np; ++p) {
+      if ((rc = host_alloc(h, &G.prefix_host[p], size_t(h->plen) * h->row_bytes))) return rc;
+      std::memset(G.prefix_host[p], 0, size_t(h->plen) * h->row_bytes);
+      void* dp = nullptr;
+      HIPCHK(h, hipHostGetDevicePointer(&dp, G.prefix_host[p], 0));
+      table[p] = static_cast<const uint4*>(dp);
+    }
+    if ((rc = host_alloc(h, &G.tails_host, size_t(N) * h->tail_rows * h->row_bytes))) return rc;
+    std::memset(G.tails_host, 0, size_t(N) * h->tail_rows * h->row_bytes);
+    {
+      void* dp = nullptr;
+      HIPCHK(h, hipHostGetDevicePointer(&dp, G.tails_host, 0));
+      G.tails_dev = static_cast<const uint4*>(dp);
+    }
+    const uint4** dt = nullptr;
+    if ((rc = dev_alloc(h, &dt, table.size(), nullptr))) return rc;
+    G.prefix_table = dt;
+    if ((rc = upload(h, dt, table.data(), table.size() * sizeof(void*)))) return rc;
+  }
+  h->arena.assign(c.n_arenas, nullptr);
+  for (int a = 0; a < c.n_arenas; ++a)
+    if ((rc = dev_alloc(h, &h->arena[a], size_t(N) * h->QK * c.row_elems, &h->bytes_staging))) return rc;
+  {
+    std::vector<CommitGroup> cg(c.n_groups);
+    for (int g = 0; g < c.n_groups; ++g) {
+      cg[g].ring = reinterpret_cast<const uint4*>(h->grp[g].ring);
+      cg[g].tails = const_cast<uint4*>(h->grp[g].tails_dev);
+    }
+    if ((rc = dev_alloc(h, &h->d_commit_groups, cg.size(), nullptr))) return rc;
+    if ((rc = upload(h, h->d_commit_groups, cg.data(), cg.size() * sizeof(CommitGroup)))) return rc;
+    if ((rc = dev_alloc(h, &h->d_commit, size_t(2) * N, nullptr))) return rc;
+    void* hc = nullptr;
+    if (hipHostMalloc(&hc, size_t(2) * N * 4, hipHostMallocDefault) != hipSuccess) {
+      return fail(h, KV_ENOMEM, "pinned commit buffer");
+    }
+    h->h_commit = static_cast<int32_t*>(hc);
+  }
+  HIPCHK(h, hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking));
+  HIPCHK(h, hipEventCreateWithFlags(&h->ev_plan, hipEventDisableTiming));
+  HIPCHK(h, hipEventCreateWithFlags(&h->ev_commit, hipEventDisableTiming));
+  h->ev_fetched.assign(h->n_chunks, nullptr);
+  for (auto& e : h->ev_fetched) HIPCHK(h, hipEventCreateWithFlags(&e, hipEventDisableTiming));
+  h->ev_free.assign(c.n_arenas, std::vector<hipEvent_t>(h->n_chunks, nullptr));
+  h->free_recorded.assign(c.n_arenas, std::vector<char>(h->n_chunks, 0));
+  for (auto& v : h->ev_free)
+    for (auto& e : v) HIPCHK(h, hipEventCreateWithFlags(&e, hipEventDisableTiming));
+  HIPCHK(h, hipDeviceSynchronize());
+  return rc;
+}
+
+int kv_hier_create(const kv_hier_config* cfg, kv_hier_t** out) {
+  if (!cfg || !out) return KV_EINVAL;
+  *out = nullptr;
+  kv_hier* h = new kv_hier();
+  h->cfg = *cfg;
+  int rc = validate(h, *cfg);
+  if (!rc) rc = create_impl(h);
+  if (rc) {
+    (void)hipDeviceSynchronize();
+    free_all(h);
+    delete h;
+    return rc;
+  }
+  *out = h;
+  return KV_OK;
+}
+
+
+int kv_hier_info_get(kv_hier_t* h, kv_hier_info* out) {
+  if (!h || !out) return KV_EINVAL;
+  out->ring_rows = h->Rd;
+  out->n_chunks = h->n_chunks;
+  out->bytes_hot = h->bytes_hot;
+  out->bytes_staging = h->bytes_staging;
+  out->bytes_ring = h->bytes_ring;
+  out->bytes_maps = h->bytes_maps;
+  out->bytes_resident = h->bytes_res;
+  out->bytes_host = h->bytes_host;
+  out->attn_splits = h->splits;
+  out->attn_head_groups = h->head_groups;
+  return KV_OK;
+}
+
+int kv_hier_host_rows(kv_hier_t* h, int g, int kind, int index, void** rows, int64_t* n_rows) {
+  int rc = check_group(h, g);
+  if (rc) return rc;
+  if (!rows || !n_rows) return fail(h, KV_EINVAL, "null output");
+  Group& G = h->grp[g];
+  if (kind == 0) {
+    if (index < 0 || index >= h->n_prefix) return fail(h, KV_EINVAL, "prefix %d outside [0, %d)", index, h->n_prefix);
+    *rows = G.prefix_host[index];
+    *n_rows = h->plen;
+  } else if (kind == 1) {
+    if ((rc = check_req(h, index))) return rc;
+    *rows = static_cast<char*>(G.tails_host) + size_t(index) * h->tail_rows * h->row_bytes;
+    *n_rows = h->tail_rows;
+  } else {
+    return fail(h, KV_EINVAL, "kind %d", kind);
+  }
+  return KV_OK;
+}
+
+int kv_hier_set_hist_len(kv_hier_t* h, const int32_t* hist_len) {
+  if (!h || !hist_len) return KV_EINVAL;
+  for (int r = 0; r < h->cfg.n_req; ++r)
+    if (hist_len[r] < 0 || hist_len[r] > h->cfg.hist_cap)
+      return fail(h, KV_EINVAL, "hist_len[%d] = %d outside [0, %d]", r, hist_len[r], h->cfg.hist_cap);
+  int rc = sync_all(h);
+  if (rc) return rc;
+  h->hist_len.assign(hist_len, hist_len + h->cfg.n_req);
+  for (Group& G : h->grp)
+    if ((rc = upload(h, G.ring_lo, hist_len, size_t(h->cfg.n_req) * 4))) return rc;
+  return KV_OK;
+}
+
+int kv_hier_hist_len(kv_hier_t* h, int32_t* hist_len) {
+  if (!h || !hist_len) return KV_EINVAL;
+  std::copy(h->hist_len.begin(), h->hist_len.end(), hist_len);
+  return KV_OK;
+}
+
+int kv_hier_set_hot(kv_hier_t* h, int g, int r, const int32_t* rows, const int32_t* last_used, int n) {
+  int rc = check_group(h, g);
+  if (rc) return rc;
+  if ((rc = check_req(h, r))) return rc;
+  const int B = h->cfg.hot_slots, L = h->L;
+  if (n < 0 || n > B || (n > 0 && (!rows || !last_used))) return fail(h, KV_EINVAL, "bad hot set size %d", n);
+  std::vector<int32_t> nrow(B, -1), nlu(B, 0);
+  std::vector<char> seen(size_t(L), 0);
+  int maxlu = 0;
+  for (int s = 0; s < n; ++s) {
+    if (rows[s] < -1 || rows[s] >= L) return fail(h, KV_EINVAL, "hot row %d outside [-1, %d)", rows[s], L);
+    if (last_used[s] < 0) return fail(h, KV_EINVAL, "negative last_used");
+    if (rows[s] >= 0) {
+      if (seen[rows[s]]) return fail(h, KV_EINVAL, "hot row %d repeated", rows[s]);
+      seen[rows[s]] = 1;
+    }
+    nrow[s] = rows[s];
+    nlu[s] = last_used[s];
+    maxlu = std::max(maxlu, last_used[s]);
+  }
+  if ((rc = sync_all(h))) return rc;
+  Group& G = h->grp[g];
+  std::vector<int32_t> old(B);
+  if ((rc = download(h, old.data(), G.slot_row + size_t(r) * B, size_t(B) * 4))) return rc;
+  std::vector<int64_t> idx;
+  std::vector<int32_t> val;
+  for (int s = 0; s < B; ++s)
+    if (old[s] >= 0) { idx.push_back(int64_t(r) * L + old[s]); val.push_back(-1); }
+  if ((rc = scatter32(h, G.slot_map, idx, val))) return rc;
+  idx.clear();
+  val.clear();
+  std::vector<int32_t> req, src;
+  std::vector<int64_t> dst;
+  for (int s = 0; s < B; ++s)
+    if (nrow[s] >= 0) {
+      idx.push_back(int64_t(r) * L + nrow[s]);
+      val.push_back(s);
+      req.push_back(r);
+      src.push_back(nrow[s]);
+      dst.push_back(int64_t(r) * B + s);
+    }
+  if ((rc = scatter32(h, G.slot_map, idx, val))) return rc;
+  if ((rc = upload(h, G.slot_row + size_t(r) * B, nrow.data(), size_t(B) * 4))) return rc;
+  if ((rc = upload(h, G.slot_lu + size_t(r) * B, nlu.data(), size_t(B) * 4))) return rc;
+  if ((rc = rows_from_host(h, G, req, src, dst, G.hot))) return rc;
+  G.t = std::max(G.t, maxlu);
+  return KV_OK;
+}
+
+int kv_hier_set_resident(kv_hier_t* h, int g, int r, const uint8_t* bitmap) {
+  int rc = check_group(h, g);
+  if (rc) return rc;
+  if ((rc = check_req(h, r))) return rc;
+  if (!bitmap) return fail(h, KV_EINVAL, "null bitmap");
+  Group& G = h->grp[g];
+  if (G.res_set[r]) return fail(h, KV_ESTATE, "resident set of request %d already given", r);
+  const int lim = std::min(h->hist_len[r], h->L);
+  std::vector<int64_t> idx, dst;
+  std::vector<int32_t> val, req, src;
+  for (int s = 0; s < lim; ++s)
+    if (bitmap[s]) {
+      idx.push_back(int64_t(r) * h->L + s);
+      val.push_back(int32_t(G.res_cursor + int64_t(val.size())));
+      req.push_back(r);
+      src.push_back(s);
+      dst.push_back(G.res_cursor + int64_t(dst.size()));
+    }
+  if (G.res_cursor + int64_t(val.size()) > h->cfg.resident_cap)
+    return fail(h, KV_ENOMEM, "resident pool full (%lld of %lld rows)", (long long)(G.res_cursor + val.size()),
+                (long long)h->cfg.resident_cap);
+  if ((rc = sync_all(h))) return rc;
+  if ((rc = scatter32(h, G.res_map, idx, val))) return rc;
+  if ((rc = rows_from_host(h, G, req, src, dst, G.resident))) return rc;
+  G.res_cursor += int64_t(val.size());
+  G.res_set[r] = 1;
+  return KV_OK;
+}
+
+int kv_hier_clear_resident(kv_hier_t* h, int g) {
+  int rc = check_group(h, g);
+  if (rc) return rc;
+  if ((rc = sync_all(h))) return rc;
+  Group& G = h->grp[g];
+  HIPCHK(h, launch_fill32(reinterpret_cast<uint32_t*>(G.res_map), 0xffffffffu, size_t(h->cfg.n_req) * h->L, nullptr));
+  HIPCHK(h, hipDeviceSynchronize());
+  G.res_cursor = 0;
+  std::fill(G.res_set.begin(), G.res_set.end(), 0);
+  return KV_OK;
+}
+
+int kv_hier_ring_load(kv_hier_t* h, int g, int r, int32_t first_pos, const void* rows, int n) {
+  int rc = check_group(h, g);
+  if (rc) return rc;
+  if ((rc = check_req(h, r))) return rc;
+  if (n < 0 || first_pos < 0 || n > h->Rd || (n > 0 && !rows) || int64_t(first_pos) + n != h->hist_len[r])
+    return fail(h, KV_EINVAL, "ring_load must cover [first_pos, n_r) with at most R_d=%d rows", h->Rd);
+  if ((rc = sync_all(h))) return rc;
+  Group& G = h->grp[g];
+  const char* src = static_cast<const char*>(rows);
+  int done = 0;
+  while (done < n) {
+    const int pos = first_pos + done;
+    const int slot = pos % h->Rd;
+    const int run = std::min(n - done, h->Rd - slot);
+    char* dst = reinterpret_cast<char*>(G.ring) + (size_t(r) * h->Rd + slot) * h->row_bytes;
+    if ((rc = upload(h, dst, src + size_t(done) * h->row_bytes, size_t(run) * h->row_bytes))) return rc;
+    done += run;
+  }
+  const int32_t lo = first_pos;
+  return upload(h, G.ring_lo + r, &lo, 4);
+}
+
+int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t* topk_idx,
+                        const int32_t* causal_pos, const void* ring_rows, void* out, void* stream) {
+  int rc = check_group(h, g);
+  if (rc) return rc;
+  if (!queries || !topk_idx || !causal_pos || !ring_rows || !out) return fail(h, KV_EINVAL, "null device pointer");
+  const kv_hier_config& c = h->cfg;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Group& G = h->grp[g];
+  const int N = c.n_req;
+  const int a = g % c.n_arenas;
+  G.t += 1;
+  G.calls += 1;
+
+  int ti = time_begin(h, K_RING, g, s);
+  HIPCHK(h, launch_ring_write(static_cast<const uint4*>(ring_rows), causal_pos, reinterpret_cast<uint4*>(G.ring), N,
+                              c.q_max, h->Rd, h->row16, s));
+  time_end(h, ti, s);
+
+  PlanArgs pa;
+  pa.topk = topk_idx;
+  pa.causal = causal_pos;
+  pa.res_map = G.res_map;
+  pa.slot_map = G.slot_map;
+  pa.slot_row = G.slot_row;
+  pa.slot_lu = G.slot_lu;
+  pa.union_rows = G.union_rows;
+  pa.union_loc = G.union_loc;
+  pa.miss_rows = G.miss_rows;
+  pa.victims = G.victims;
+  pa.loc = G.loc;
+  pa.req_info = G.req_info;
+  pa.req_counts = G.req_counts;
+  pa.cum = G.cum;
+  pa.N = N;
+  pa.Q = c.q_max;
+  pa.k = c.topk;
+  pa.B = c.hot_slots;
+  pa.L = h->L;
+  pa.t = G.t;
+  pa.chunk_words = h->chunk_words;
+  pa.sort_cap = h->sort_cap;
+  ti = time_begin(h, K_PLAN, g, s);
+  HIPCHK(h, launch_plan(pa, h->plan_lds, s));
+  time_end(h, ti, s);
+  HIPCHK(h, hipEventRecord(h->ev_plan, s));
+
+  // host fetch of every chunk on the side stream
+  HIPCHK(h, hipStreamWaitEvent(h->side, h->ev_plan, 0));
+  const HostRowSrc src = host_src(h, G);
+  for (int ch = 0; ch < h->n_chunks; ++ch) {
+    const int r0 = h->chunk_lo[ch], r1 = h->chunk_lo[ch + 1];
+    if (h->free_recorded[a][ch]) HIPCHK(h, hipStreamWaitEvent(h->side, h->ev_free[a][ch], 0));
+    const int wpr = std::max(1, 128 / std::max(1, r1 - r0));
+    ti = time_begin(h, K_GATHER, g, h->side);
+    HIPCHK(h, launch_miss_gather(src, G.miss_rows, G.req_info, reinterpret_cast<uint4*>(h->arena[a]), h->QK, r0, r1,
+                                 wpr, h->side));
+    time_end(h, ti, h->side);
+    HIPCHK(h, hipEventRecord(h->ev_fetched[ch], h->side));
+  }
+  // attention and copy-back per chunk on the caller's stream
+  AttnArgs at;
+  at.q = static_cast<const uint16_t*>(queries);
+  at.loc = G.loc;
+  at.causal = causal_pos;
+  at.ring_lo = G.ring_lo;
+  at.hot = G.hot;
+  at.staging = h->arena[a];
+  at.resident = G.resident;
+  at.ring = G.ring;
+  at.out = static_cast<uint16_t*>(out);
+  at.part_o = h->part_o;
+  at.part_ml = h->part_ml;
+  at.N = N;
+  at.Q = c.q_max;
+  at.k = c.topk;
+  at.H = c.n_heads;
+  at.W = c.ring_window;
+  at.Rd = h->Rd;
+  at.block_only = c.ring_block_only ? 1 : 0;
+  at.splits = h->splits;
+  at.head_groups = h->head_groups;
+  const float scale = c.softmax_scale > 0.f ? c.softmax_scale : 1.0f / std::sqrt(float(c.d_qk));
+  at.scale_log2 = scale * 1.4426950408889634f;
+  for (int ch = 0; ch < h->n_chunks; ++ch) {
+    at.r0 = h->chunk_lo[ch];
+    at.r1 = h->chunk_lo[ch + 1];
+    HIPCHK(h, hipStreamWaitEvent(s, h->ev_fetched[ch], 0));
+    ti = time_begin(h, K_ATTN, g, s);
+    HIPCHK(h, launch_attn(at, c.row_elems, c.d_qk, c.v_off, c.d_v, s));
+    time_end(h, ti, s);
+    if (h->splits > 1) {
+      ti = time_begin(h, K_COMBINE, g, s);
+      HIPCHK(h, launch_attn_combine(at, c.d_v, s));
+      time_end(h, ti, s);
+    }
+    ti = time_begin(h, K_PROMOTE, g, s);
+    HIPCHK(h, launch_promote(reinterpret_cast<const uint4*>(h->arena[a]), G.victims, G.req_info,
+                             reinterpret_cast<uint4*>(G.hot), h->QK, c.hot_slots, h->row16, at.r0, at.r1, s));
+    time_end(h, ti, s);
+    if (c.flags & KV_FLAG_POISON) {
+      const size_t words = size_t(at.r1 - at.r0) * h->QK * c.row_elems / 2;
+      HIPCHK(h, launch_fill32(reinterpret_cast<uint32_t*>(h->arena[a] + size_t(at.r0) * h->QK * c.row_elems),
+                              0x7fc07fc0u, words, s));
+    }
+    HIPCHK(h, hipEventRecord(h->ev_free[a][ch], s));
+    h->free_recorded[a][ch] = 1;
+  }
+  return KV_OK;
+}
+
+int kv_hier_commit(kv_hier_t* h, const int32_t* accepted, void* stream) {
+  if (!h || !accepted) return KV_EINVAL;
+  const kv_hier_config& c = h->cfg;
+  const int N = c.n_req;
+  for (int r = 0; r < N; ++r) {
+    const int a = accepted[r];
+    if (a < -1 || a >= c.q_max) return fail(h, KV_EINVAL, "accepted[%d] = %d outside [-1, %d)", r, a, c.q_max);
+    if (a >= 0) {
+      if (int64_t(h->hist_len[r]) + 1 + a > c.hist_cap) return fail(h, KV_EINVAL, "request %d: history full", r);
+      if (h->hist_len[r] < h->plen) return fail(h, KV_EINVAL, "request %d: frontier inside the shared prefix", r);
+    }
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (h->commit_pending) HIPCHK(h, hipEventSynchronize(h->ev_commit));
+  for (int r = 0; r < N; ++r) {
+    h->h_commit[r] = h->hist_len[r];
+    h->h_commit[N + r] = accepted[r];
+  }
+  HIPCHK(h, hipMemcpyAsync(h->d_commit, h->h_commit, size_t(2) * N * 4, hipMemcpyHostToDevice, s));
+  HIPCHK(h, hipEventRecord(h->ev_commit, s));
+  h->commit_pending = true;
+  HIPCHK(h, launch_commit(h->d_commit_groups, c.n_groups, h->d_commit, h->d_commit + N, N, c.q_max, h->Rd, h->plen,
+                          h->tail_rows, h->row16, s));
+  for (int r = 0; r < N; ++r)
+    if (accepted[r] >= 0) h->hist_len[r] += 1 + accepted[r];
+  return KV_OK;
+}
+
+int kv_hier_stats(kv_hier_t* h, int g, kv_hier_counters* cum, kv_hier_counters* last) {
+  int rc = check_group(h, g);
+  if (rc) return rc;
+  if ((rc = sync_all(h))) return rc;
+  Group& G = h->grp[g];
+  const int N = h->cfg.n_req;
+  unsigned long long cv[C_NUM];
+  std::vector<int64_t> rq(size_t(N) * C_NUM);
+  if ((rc = download(h, cv, G.cum, sizeof cv))) return rc;
+  if ((rc = download(h, rq.data(), G.req_counts, rq.size() * 8))) return rc;
+  auto fill = [&](kv_hier_counters* o, const int64_t* v, int64_t calls, bool timing) {
+    std::memset(o, 0, sizeof *o);
+    o->calls = calls;
+    o->active_requests = v[C_ACTIVE_REQ];
+    o->active_queries = v[C_ACTIVE_Q];
+    o->selections = v[C_SEL];
+    o->pads = v[C_PAD];
+    o->invalid = v[C_INVALID];
+    o->union_rows = v[C_UNION];
+    o->union_resident = v[C_U_RES];
+    o->union_hot = v[C_U_HOT];
+    o->union_miss = v[C_U_MISS];
+    o->fetched_bytes = v[C_U_MISS] * int64_t(h->row_bytes);
+    o->promoted = v[C_PROMOTED];
+    o->overflow = v[C_OVERFLOW];
+    o->sel_resident = v[C_S_RES];
+    o->sel_hot = v[C_S_HOT];
+    o->sel_miss = v[C_S_MISS];
+    if (timing) {
+      o->ms_ring = G.ms[K_RING];
+      o->ms_plan = G.ms[K_PLAN];
+      o->ms_gather = G.ms[K_GATHER];
+      o->ms_attn = G.ms[K_ATTN];
+      o->ms_combine = G.ms[K_COMBINE];
+      o->ms_promote = G.ms[K_PROMOTE];
+      o->n_ring = G.nt[K_RING];
+      o->n_plan = G.nt[K_PLAN];
+      o->n_gather = G.nt[K_GATHER];
+      o->n_attn = G.nt[K_ATTN];
+      o->n_combine = G.nt[K_COMBINE];
+      o->n_promote = G.nt[K_PROMOTE];
+    }
+  };
+  if (cum) {
+    int64_t v[C_NUM];
+    for (int i = 0; i < C_NUM; ++i) v[i] = int64_t(cv[i]);
+    fill(cum, v, G.calls, true);
+  }
+  if (last) {
+    int64_t v[C_NUM] = {0};
+    for (int r = 0; r < N; ++r)
+      for (int i = 0; i < C_NUM; ++i) v[i] += rq[size_t(r) * C_NUM + i];
+    fill(last, v, G.calls > 0 ? 1 : 0, false);
+  }
+  return KV_OK;
+}
+
+int kv_hier_reset_stats(kv_hier_t* h) {
+  if (!h) return KV_EINVAL;
+  int rc = sync_all(h);
+  if (rc) return rc;
+  for (Group& G : h->grp) {
+    HIPCHK(h, launch_fill32(reinterpret_cast<uint32_t*>(G.cum), 0, size_t(C_NUM) * 2, nullptr));
+    G.calls = 0;
+    for (int i = 0; i < K_NUM; ++i) { G.ms[i] = 0; G.nt[i] = 0; }
+  }
+  HIPCHK(h, hipDeviceSynchronize());
+  return KV_OK;
+}
+
+int kv_hier_last_lists(kv_hier_t* h, int g, int r, kv_hier_lists* o) {
+  int rc = check_group(h, g);
+  if (rc) return rc;
+  if ((rc = check_req(h, r))) return rc;
+  if (!o || !o->union_rows || !o->union_loc || !o->miss_rows || !o->victims || !o->loc)
+    return fail(h, KV_EINVAL, "null list buffer");
+  if ((rc = sync_all(h))) return rc;
+  Group& G = h->grp[g];
+  int32_t info[I_NUM];
+  if ((rc = download(h, info, G.req_info + size_t(r) * I_NUM, sizeof info))) return rc;
+  const size_t base = size_t(r) * h->QK;
+  o->n_union = info[I_NUNION];
+  o->n_miss = info[I_NMISS];
+  o->n_promote = info[I_NPROMOTE];
+  o->n_active = info[I_NACTIVE];
+  if ((rc = download(h, o->union_rows, G.union_rows + base, size_t(o->n_union) * 4))) return rc;
+  if ((rc = download(h, o->union_loc, G.union_loc + base, size_t(o->n_union) * 4))) return rc;
+  if ((rc = download(h, o->miss_rows, G.miss_rows + base, size_t(o->n_miss) * 4))) return rc;
+  if ((rc = download(h, o->victims, G.victims + base, size_t(o->n_promote) * 4))) return rc;
+  return download(h, o->loc, G.loc + base, size_t(h->QK) * 4);
+}
+
+int kv_hier_slot_table(kv_hier_t* h, int g, int r, int32_t* rows, int32_t* last_used) {
+  int rc = check_group(h, g);
+  if (rc) return rc;
+  if ((rc = check_req(h, r))) return rc;
+  if (!rows || !last_used) return fail(h, KV_EINVAL, "null output");
+  if ((rc = sync_all(h))) return rc;
+  const int B = h->cfg.hot_slots;
+  if ((rc = download(h, rows, h->grp[g].slot_row + size_t(r) * B, size_t(B) * 4))) return rc;
+  return download(h, last_used, h->grp[g].slot_lu + size_t(r) * B, size_t(B) * 4);
+}
+
+int kv_hier_read_rows(kv_hier_t* h, int g, const int32_t* locs, int n, void* rows) {
+  int rc = check_group(h, g);
+  if (rc) return rc;
+  if (n < 0 || (n > 0 && (!locs || !rows))) return fail(h, KV_EINVAL, "bad read_rows arguments");
+  if (n == 0) return KV_OK;
+  const kv_hier_config& c = h->cfg;
+  Group& G = h->grp[g];
+  for (int i = 0; i < n; ++i) {
+    const int32_t code = locs[i];
+    if (code == -1) continue;
+    if (code < 0) return fail(h, KV_EINVAL, "location code %d", code);
+    const int tier = loc_tier(code);
+    const int64_t idx = loc_index(code);
+    const int64_t lim = tier == kTierHot ? int64_t(c.n_req) * c.hot_slots
+                        : tier == kTierStaged ? int64_t(c.n_req) * h->QK
+                        : tier == kTierResident ? c.resident_cap : int64_t(c.n_req) * h->Rd;
+    if (idx >= lim) return fail(h, KV_EINVAL, "location %d beyond its pool", code);
+  }
+  if ((rc = sync_all(h))) return rc;
+  int32_t* dl = nullptr;
+  uint16_t* dr = nullptr;
+  if ((rc = dev_alloc(h, &dl, size_t(n), nullptr))) return rc;
+  if ((rc = dev_alloc(h, &dr, size_t(n) * c.row_elems, nullptr))) { (void)hipFree(dl); return rc; }
+  PoolView pv;
+  pv.hot = reinterpret_cast<const uint4*>(G.hot);
+  pv.staging = reinterpret_cast<const uint4*>(h->arena[g % c.n_arenas]);
+  pv.resident = reinterpret_cast<const uint4*>(G.resident);
+  pv.ring = reinterpret_cast<const uint4*>(G.ring);
+  rc = upload(h, dl, locs, size_t(n) * 4);
+  if (!rc) {
+    hipError_t e = launch_read_rows(pv, dl, n, reinterpret_cast<uint4*>(dr), h->row16, nullptr);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) rc = fail(h, KV_EHIP, "read_rows: %s", hipGetErrorString(e));
+  }
+  if (!rc) rc = download(h, rows, dr, size_t(n) * h->row_bytes);
+  (void)hipFree(dl);
+  (void)hipFree(dr);
+  return rc;
+}
+
+int kv_hier_sync(kv_hier_t* h) {
+  if (!h) return KV_EINVAL;
+  return sync_all(h);
+}
+
+}  // extern "C"

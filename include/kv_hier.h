@@ -1,0 +1,231 @@
+/*
+ * kv_hier.h - C ABI of libkvhier.so: one speculative verification step of
+ * sparse attention over a hierarchical KV cache, on one AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The operation follows "Adaptive DHiSparse: Speculative Decoding over a
+ * Load-Adaptive KV Hierarchy" (arXiv 2610.13708):
+ *   - §2.1 eq. (1): each query attends over the rows its top-k selected;
+ *     eq. (2): ready rows R_t and the host-recovery set D_t = S_t \ R_t.
+ *   - §2.2 "Fixed-cache offloading": per request and KV source a bounded
+ *     GPU cache of B rows, hit detection, protection of selected rows, LRU
+ *     victims, one fetch per missing row from pinned host memory.
+ *   - §3.2 / Figure 2: resolution order (1) ready optional history,
+ *     (2) hot cache, (3) host copy; locations returned in selection order.
+ *   - §3.3 eqs. (5)-(7): the K_r queries of a request keep their own causal
+ *     boundary; the union U_r of their selections is resolved once and each
+ *     distinct missing row is copied once (Figure 3 callout 2); overflow
+ *     rows beyond the hot cache are staged; acceptance commits the anchor
+ *     and A_r drafts, n' = n + 1 + A.
+ *   - §3.4 eqs. (9)-(10) and the staging paragraph: window-bounded ring of
+ *     R_d = p*ceil((W+p-1+K_max)/p) rows per request addressed
+ *     phi(i,t) = i*R_d + (t mod R_d); chi staging arenas of N*K_max*k rows
+ *     reused across layer groups after their readers finish and promoted rows
+ *     are copied back to their hot-cache slots.
+ *   - §3.5 eqs. (11)-(12): every list entry gets a location l with
+ *     KV[l] = c_{r,s}; a row held in two tiers resolves to one of them.
+ *
+ * Conventions
+ *   - Every call returns KV_OK (0) or a negative KV_E* code; no exception
+ *     crosses the ABI.  kv_hier_last_error() gives a message for the handle.
+ *   - "device" pointers are HIP device allocations owned by the caller that
+ *     must stay valid until the stream passes the step; "host" pointers are
+ *     ordinary host memory read or written before the call returns.
+ *   - Rows are bf16 (stored as uint16 bit patterns), row_elems per row.
+ *   - Out-of-range values inside device arrays (a top-k entry outside
+ *     [0, n_r), for instance) are not errors: they are counted and skipped.
+ *   - Location code (int32): tier in bits 30..29, index in bits 28..0,
+ *     -1 = none.  Tier 0: hot slot r*B + slot; tier 1: staged row
+ *     r*K_max*k + i of the group's arena; tier 2: resident pool index;
+ *     tier 3 (kv_hier_read_rows only): ring row r*R_d + (pos mod R_d).
+ */
+#ifndef KV_HIER_H
+#define KV_HIER_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  KV_OK = 0,
+  KV_EINVAL = -1,        /* bad argument or size                        */
+  KV_ENOMEM = -2,        /* device or pinned host allocation failed      */
+  KV_EHIP = -3,          /* a HIP runtime call failed                    */
+  KV_ESTATE = -4,        /* call not valid in the current state          */
+  KV_EUNSUPPORTED = -5   /* shape outside what the kernels are built for */
+};
+
+enum { KV_TIER_HOT = 0, KV_TIER_STAGED = 1, KV_TIER_RESIDENT = 2, KV_TIER_RING = 3 };
+
+enum {
+  KV_FLAG_TIMING = 1,    /* time every kernel with HIP events (kv_hier_stats ms_*) */
+  KV_FLAG_POISON = 2     /* debug: fill a staging arena with NaN after its readers finish */
+};
+
+typedef struct kv_hier kv_hier_t;  /* opaque, owned by the library */
+
+typedef struct {
+  int32_t n_req;            /* N request slots                                          */
+  int32_t n_groups;         /* G layer groups (payload sources), each with its own cache */
+  int32_t n_arenas;         /* chi staging arenas; group g stages into arena g % chi     */
+  int32_t hist_cap;         /* L: history rows per request (host backing, maps)          */
+  int32_t n_prefix;         /* shared host prefixes; 0 = every request owns rows [0, L)  */
+  int32_t prefix_len;       /* rows [0, prefix_len) of request r live in prefix r % n_prefix */
+  int32_t row_elems;        /* bf16 elements per row (d_KV = 2*row_elems bytes)          */
+  int32_t d_qk;             /* key: K = row[0 : d_qk]                                    */
+  int32_t v_off;            /* value: V = row[v_off : v_off + d_v]                       */
+  int32_t d_v;
+  int32_t n_heads;          /* query heads sharing each row                              */
+  int32_t q_max;            /* K_max verification queries per request (<= 32)           */
+  int32_t topk;             /* k selections per query                                    */
+  int32_t hot_slots;        /* B                                                         */
+  int32_t ring_window;      /* W                                                         */
+  int32_t ring_page;        /* p                                                         */
+  int32_t ring_block_only;  /* 1: ring branch limited to positions >= n_r (eq. 5 literal) */
+  int32_t n_chunks;         /* request chunks pipelined fetch -> attention (0 = auto)    */
+  int64_t resident_cap;     /* rows of the resident pool per group (0 = no resident tier) */
+  float softmax_scale;      /* <= 0 selects 1/sqrt(d_qk)                                 */
+  int32_t flags;            /* KV_FLAG_*                                                 */
+} kv_hier_config;
+
+/* Counters of one layer group (kv_hier_stats).  "union_*" count distinct rows
+ * of U_r, "sel_*" count list entries (selections). */
+typedef struct {
+  int64_t calls;
+  int64_t active_requests;
+  int64_t active_queries;   /* verified query tokens                                     */
+  int64_t selections;       /* valid list entries                                        */
+  int64_t pads;
+  int64_t invalid;
+  int64_t union_rows;
+  int64_t union_resident;
+  int64_t union_hot;
+  int64_t union_miss;       /* = rows fetched from host, once each                       */
+  int64_t fetched_bytes;
+  int64_t promoted;         /* missing rows given a hot-cache slot                       */
+  int64_t overflow;         /* missing rows staged only                                  */
+  int64_t sel_resident;
+  int64_t sel_hot;
+  int64_t sel_miss;         /* missing selections (sum over queries)                     */
+  /* kernel time in ms summed over timed calls (KV_FLAG_TIMING), and launch counts */
+  double ms_ring, ms_plan, ms_gather, ms_attn, ms_combine, ms_promote;
+  int64_t n_ring, n_plan, n_gather, n_attn, n_combine, n_promote;
+} kv_hier_counters;
+
+/* Per-request lists of the last verify_step of a group (kv_hier_last_lists).
+ * Every array is caller-owned host memory of q_max*topk elements. */
+typedef struct {
+  int32_t *union_rows;      /* U_r ascending                                             */
+  int32_t *union_loc;       /* location code of each union row                           */
+  int32_t *miss_rows;       /* D_r ascending = staging order                             */
+  int32_t *victims;         /* hot slot taken by miss i, i < n_promote                   */
+  int32_t *loc;             /* [q_max][topk] location of every list entry                */
+  int32_t n_union, n_miss, n_promote, n_active;
+} kv_hier_lists;
+
+typedef struct {
+  int32_t ring_rows;        /* R_d of eq. (9)                                            */
+  int32_t n_chunks;
+  int64_t bytes_hot, bytes_staging, bytes_ring, bytes_maps, bytes_resident, bytes_host;
+  int32_t attn_splits;      /* key splits per query chosen for this shape                */
+  int32_t attn_head_groups;
+} kv_hier_info;
+
+/* Creates a handle: allocates hot caches, slot tables, maps, rings, staging
+ * arenas, plan buffers, a side stream and events on the current HIP device,
+ * and pinned host history for every group.  Returns KV_EINVAL for
+ * inconsistent sizes, KV_EUNSUPPORTED for a row layout without kernels,
+ * KV_ENOMEM when an allocation fails. */
+int kv_hier_create(const kv_hier_config *cfg, kv_hier_t **out);
+
+/* Frees everything; waits for outstanding work first.  NULL is accepted. */
+void kv_hier_destroy(kv_hier_t *h);
+
+/* Message of the last failing call on h (never NULL). */
+const char *kv_hier_last_error(const kv_hier_t *h);
+
+/* Sizes of what create allocated.  Host out-pointer. */
+int kv_hier_info_get(kv_hier_t *h, kv_hier_info *out);
+
+/* Pinned host rows of group g that the caller fills before the first step:
+ * kind 0 = prefix `index` (prefix_len rows), kind 1 = tail of request `index`
+ * (rows prefix_len .. hist_cap-1, i.e. hist_cap - prefix_len rows).  The
+ * pointer stays owned by the library (valid until destroy). */
+int kv_hier_host_rows(kv_hier_t *h, int g, int kind, int index, void **rows, int64_t *n_rows);
+
+/* Committed frontier n_r of every request (host int32[n_req]); also marks the
+ * ring of every group empty below n_r.  Eq. (5): query j sits at n_r + j. */
+int kv_hier_set_hist_len(kv_hier_t *h, const int32_t *hist_len);
+
+/* Hot-cache contents of (g, r): n <= B host rows (-1 = empty slot) with their
+ * last-used stamps (>= 0); rows must be distinct and < hist_cap.  Row bytes
+ * are copied from the host backing.  Synchronous. */
+int kv_hier_set_hot(kv_hier_t *h, int g, int r, const int32_t *rows, const int32_t *last_used, int n);
+
+/* Ready optional history of (g, r) (§3.1): host uint8[hist_cap] bitmap; rows
+ * below the frontier with a non-zero byte become resident, receiving
+ * consecutive pool indices in ascending row order after those already handed
+ * out in this group.  Once per (g, r) until kv_hier_clear_resident(g).
+ * KV_ENOMEM when the pool (resident_cap rows) is full.  Synchronous. */
+int kv_hier_set_resident(kv_hier_t *h, int g, int r, const uint8_t *bitmap);
+int kv_hier_clear_resident(kv_hier_t *h, int g);
+
+/* Loads committed positions first_pos .. n_r-1 (n rows, host bf16
+ * [n][row_elems]) into the ring of (g, r); first_pos + n must equal n_r and
+ * n <= R_d.  Synchronous. */
+int kv_hier_ring_load(kv_hier_t *h, int g, int r, int32_t first_pos, const void *rows, int n);
+
+/* One verification step of layer group g, asynchronous on `stream`
+ * (hipStream_t; NULL = default stream):
+ *   queries    device bf16 [N][q_max][n_heads][d_qk]
+ *   topk_idx   device int32 [N][q_max][topk]; -1 = pad
+ *   causal_pos device int32 [N][q_max]: n_r + j for active queries, -1 for an
+ *              inactive suffix (request inactive when causal_pos[r][0] < 0)
+ *   ring_rows  device bf16 [N][q_max][row_elems]: new KV row of each query's
+ *              position, written to the ring at phi(r, p_j) (eq. 10)
+ *   out        device bf16 [N][q_max][n_heads][d_v]; zero for inactive queries
+ * Resolves the union of each request's selections, probes resident map then
+ * hot cache, fetches every distinct missing row once from pinned host memory
+ * into the group's staging arena (on a side stream, overlapped with attention
+ * of earlier request chunks), runs exact sparse attention of every query over
+ * its own list plus its ring window, and copies promoted rows into their
+ * victim slots.  Caller contract (not checked on the device): causal_pos[r][0]
+ * equals the frontier set by kv_hier_set_hist_len / kv_hier_commit. */
+int kv_hier_verify_step(kv_hier_t *h, int g, const void *queries, const int32_t *topk_idx,
+                        const int32_t *causal_pos, const void *ring_rows, void *out,
+                        void *stream);
+
+/* Acceptance (eq. 7) for every request: accepted[r] = A_r in [0, q_max-1], or
+ * -1 for no commit.  Copies the ring rows of positions n_r .. n_r+A_r of every
+ * group into the pinned host backing and advances n_r by 1 + A_r; rejected
+ * rows are never published.  Asynchronous on `stream`; accepted is host
+ * memory read before return.  Caller contract: A_r < K_r of the last step. */
+int kv_hier_commit(kv_hier_t *h, const int32_t *accepted, void *stream);
+
+/* Waits for all work of the handle, then returns group g's counters:
+ * cumulative over all steps and of the last step.  Either pointer may be NULL. */
+int kv_hier_stats(kv_hier_t *h, int g, kv_hier_counters *cumulative, kv_hier_counters *last);
+int kv_hier_reset_stats(kv_hier_t *h);
+
+/* Waits, then copies request r's lists of the last step of group g. */
+int kv_hier_last_lists(kv_hier_t *h, int g, int r, kv_hier_lists *out);
+
+/* Waits, then copies the slot table of (g, r): host int32[B] rows and stamps. */
+int kv_hier_slot_table(kv_hier_t *h, int g, int r, int32_t *rows, int32_t *last_used);
+
+/* Waits, then copies the rows at n location codes (host int32) of group g
+ * into host bf16 [n][row_elems]; codes of -1 produce zero rows. */
+int kv_hier_read_rows(kv_hier_t *h, int g, const int32_t *locs, int n, void *rows);
+
+/* Committed frontier per request (host int32[n_req]). */
+int kv_hier_hist_len(kv_hier_t *h, int32_t *hist_len);
+
+/* Waits for every stream the handle uses. */
+int kv_hier_sync(kv_hier_t *h);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KV_HIER_H */

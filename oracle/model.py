@@ -174,19 +174,24 @@ class HierOracle:
         if len(set(live)) != len(live) or any(x >= self.cfg.hist_cap for x in live) \
                 or any(x < -1 for x in rows) or any(a < 0 for a in ages):
             raise ValueError("bad hot set")
+        if ages:
+            self.t[g] = max(self.t[g], max(ages))          # R8 (every request counts)
+        if r not in self.st[g]:
+            return                                        # request not modelled here
         st = self.st[g][r]
         st.slot_row = rows + [-1] * (B - len(rows))
         st.slot_lu = ages + [0] * (B - len(ages))
         st.slot_of = {x: s for s, x in enumerate(st.slot_row) if x >= 0}
-        if ages:
-            self.t[g] = max(self.t[g], max(ages))          # R8
 
     def set_resident(self, g: int, r: int, bitmap):
+        bm = np.asarray(bitmap)
+        rows = [s for s in range(min(bm.size, self.n[r])) if bm[s]]
+        if r not in self.st[g]:                           # not modelled: only the cursor moves (R7)
+            self.res_cursor[g] += len(rows)
+            return
         st = self.st[g][r]
         if st.resident_set:
             raise RuntimeError("resident set already given for this request and group")
-        bm = np.asarray(bitmap)
-        rows = [s for s in range(min(bm.size, self.n[r])) if bm[s]]
         for s in rows:                                    # R7
             st.res_idx[s] = self.res_cursor[g]
             self.res_cursor[g] += 1

@@ -1,0 +1,75 @@
+"""The C ABI library loads, exports every declared symbol and rejects bad
+configurations before touching the GPU (no compute calls here)."""
+import os
+import re
+
+import pytest
+
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "kv_hier.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|void|const char \*)\s*(kv_hier_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from hierarchical_sparse_kv_verify_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from hierarchical_sparse_kv_verify_amd import build
+        build.build(force=False)
+    return binding.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from hierarchical_sparse_kv_verify_amd import binding
+    names = _declared()
+    assert len(names) >= 19
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(binding.EXPORTED) == names
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    from hierarchical_sparse_kv_verify_amd import binding
+    with pytest.raises(RuntimeError):
+        binding.load_library(str(tmp_path / "nope.so"))
+
+
+def _cfg(**kw):
+    base = dict(n_req=2, n_groups=1, n_arenas=1, hist_cap=1024, n_prefix=0, prefix_len=0,
+                row_elems=576, d_qk=576, v_off=0, d_v=512, n_heads=64, q_max=4, topk=64,
+                hot_slots=128, ring_window=16, ring_page=16)
+    base.update(kw)
+    return base
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_req=0), -1),
+    (dict(topk=0), -1),
+    (dict(q_max=33), -5),
+    (dict(q_max=32, topk=4096), -5),
+    (dict(row_elems=300, d_qk=256, d_v=256), -5),
+    (dict(d_qk=600), -1),
+    (dict(n_prefix=0, prefix_len=10), -1),
+    (dict(n_prefix=2, prefix_len=0), -1),
+    (dict(hot_slots=20000), -5),
+    (dict(n_req=1 << 20, hot_slots=1024), -5),
+])
+def test_create_rejects_bad_config(lib, kw, code):
+    from hierarchical_sparse_kv_verify_amd import KVHier, KVHierError
+    with pytest.raises(KVHierError) as ei:
+        KVHier(**_cfg(**kw))
+    assert ei.value.code == code
+
+
+def test_null_handle_calls_are_rejected(lib):
+    import ctypes
+    assert lib.kv_hier_sync(None) == -1
+    assert lib.kv_hier_stats(None, 0, None, None) == -1
+    assert lib.kv_hier_verify_step(None, 0, None, None, None, None, None, None) == -1
+    assert b"null" in lib.kv_hier_last_error(None)
+    lib.kv_hier_destroy(None)

@@ -1,0 +1,242 @@
+"""GPU path vs oracle, element by element, through the C ABI.
+
+Integer results (union, classes, missing rows, victims, locations, slot
+tables, counters, committed host rows) must be bit-exact; attention outputs
+within |gpu - ref| <= 2e-2 + 1e-2 |ref| (bf16 inputs, fp32 accumulation).
+"""
+import numpy as np
+import pytest
+
+from tests.pair import assert_close, build_pair, run_lib_step
+from workloads import WORKLOADS, make_accepted, make_step_inputs, shrink
+
+pytestmark = pytest.mark.gpu
+
+TIER_TO_CLS = {2: 0, 0: 1, 1: 2}     # resident, hot, staged(miss) -> oracle class
+
+
+def _cls_of(codes):
+    return [TIER_TO_CLS[int(c) >> 29] for c in codes]
+
+
+def compare_step(pair, g, si, res, out_bits, requests=None, check_out=True):
+    lib = pair.lib
+    w = pair.w
+    reqs = requests if requests is not None else pair.orc.requests
+    for r in reqs:
+        L = lib.last_lists(g, r)
+        rr = res.req[r]
+        if not rr.active:
+            assert L["n_union"] == 0 and (L["loc"] == -1).all(), r
+            continue
+        assert L["union_rows"].tolist() == rr.union, ("union", r)
+        assert _cls_of(L["union_loc"]) == rr.cls, ("classes", r)
+        assert L["miss_rows"].tolist() == rr.miss, ("miss", r)
+        assert L["victims"].tolist() == rr.victims, ("victims", r)
+        np.testing.assert_array_equal(L["loc"], rr.loc, err_msg="loc r=%d" % r)
+        rows, lu = lib.slot_table(g, r)
+        orows, olu = pair.orc.slot_table(g, r)
+        np.testing.assert_array_equal(rows, orows, err_msg="slot rows r=%d" % r)
+        np.testing.assert_array_equal(lu, olu, err_msg="slot stamps r=%d" % r)
+    if check_out:
+        for (r, j), ref in res.out.items():
+            assert_close(out_bits[r, j], ref, "out r=%d j=%d" % (r, j))
+        for r in reqs:
+            for j in range(w.q_max):
+                if int(si.causal_pos[r, j]) < 0:
+                    assert (out_bits[r, j] == 0).all(), ("inactive query output", r, j)
+
+
+def compare_counts(pair, g, res):
+    _, last = pair.lib.stats(g)
+    tot = {}
+    for rr in res.req.values():
+        for k2, v in rr.counts.items():
+            tot[k2] = tot.get(k2, 0) + v
+    for key, lk in (("selections", "selections"), ("pads", "pads"), ("invalid", "invalid"),
+                    ("union", "union_rows"), ("union_resident", "union_resident"),
+                    ("union_hot", "union_hot"), ("union_miss", "union_miss"),
+                    ("promoted", "promoted"), ("overflow", "overflow"),
+                    ("sel_resident", "sel_resident"), ("sel_hot", "sel_hot"), ("sel_miss", "sel_miss"),
+                    ("queries", "active_queries")):
+        assert last[lk] == tot.get(key, 0), (key, last[lk], tot.get(key, 0))
+    assert last["fetched_bytes"] == last["union_miss"] * 2 * pair.w.row_elems
+
+
+def check_exactness(pair, g, r):
+    """Eq. (11)-(12): the row at every returned location is the selected original row."""
+    L = pair.lib.last_lists(g, r)
+    loc = L["loc"].ravel()
+    sel = np.flatnonzero(loc >= 0)
+    if sel.size == 0:
+        return
+    rows = pair.lib.read_rows(g, loc[sel])
+    hist = pair.lib_hists[g]
+    plen = pair.w.prefix_len if pair.w.n_prefix > 0 else 0
+    # the list entries themselves come from the oracle's inputs (topk); rebuild them
+    return rows, sel, hist, plen
+
+
+def _exact_vs_topk(pair, g, r, topk_r):
+    out = check_exactness(pair, g, r)
+    if out is None:
+        return
+    rows, sel, hist, plen = out
+    ent = topk_r.ravel()[sel]
+    for x, e in zip(rows, ent):
+        e = int(e)
+        want = hist.prefix[r % max(pair.w.n_prefix, 1), e] if e < plen else hist.tails[r, e - plen]
+        assert np.array_equal(x, want), ("row at location differs", r, e)
+
+
+def _tiny(**kw):
+    base = shrink(WORKLOADS["tiny"], pad_frac=0.02, invalid_frac=0.01, empty_slot_frac=0.05)
+    return shrink(base, **kw)
+
+
+def test_tiny_parity_and_exactness():
+    w = _tiny()
+    pair = build_pair(w)
+    si = make_step_inputs(w, 0, 0, pair.hist_len)
+    res = pair.orc.verify_step(0, si.topk, si.causal_pos, si.queries, si.block_rows)
+    out = run_lib_step(pair, 0, si)
+    compare_step(pair, 0, si, res, out)
+    compare_counts(pair, 0, res)
+    _exact_vs_topk(pair, 0, 0, si.topk[0])
+    pair.lib.close()
+
+
+def test_tiny_multi_step_with_commits():
+    w = _tiny(var_k=True)
+    pair = build_pair(w)
+    n = pair.hist_len.copy()
+    for step in range(5):
+        si = make_step_inputs(w, 0, step + 1, n)
+        res = pair.orc.verify_step(0, si.topk, si.causal_pos, si.queries, si.block_rows)
+        out = run_lib_step(pair, 0, si)
+        compare_step(pair, 0, si, res, out)
+        compare_counts(pair, 0, res)
+        acc = make_accepted(w, step, si.k_active)
+        pair.orc.commit(acc)
+        pair.lib.commit(acc)
+        pair.lib.sync()
+        n = n + 1 + acc
+        assert pair.lib.hist_len().tolist() == n.tolist()
+        # the committed rows now have their host copy, identical on both sides
+        for r in range(w.n_req):
+            np.testing.assert_array_equal(pair.lib.host_rows(0, 1, r)[: n[r]], pair.orc.hist[0].tails[r, : n[r]])
+    pair.lib.close()
+
+
+def _mla_small(**kw):
+    base = shrink(WORKLOADS["mla32"], n_req=6, n_groups=2, hist_lo=5000, hist_hi=6000, hist_cap=6100,
+                  n_prefix=1, prefix_len=4096, topk=512, hot_slots=1024, ring_window=128,
+                  q_max=8, f_sh=0.75, hit_rate=0.8, pad_frac=0.02, invalid_frac=0.01,
+                  empty_slot_frac=0.03, var_k=True)
+    return shrink(base, **kw)
+
+
+@pytest.mark.parametrize("n_chunks", [1, 2, 3])
+def test_mla_two_groups_two_steps(n_chunks):
+    w = _mla_small()
+    pair = build_pair(w, lib_kw=dict(n_chunks=n_chunks))
+    n = pair.hist_len.copy()
+    for step in range(2):
+        sis = []
+        for g in range(w.n_groups):
+            si = make_step_inputs(w, g, step, n)
+            res = pair.orc.verify_step(g, si.topk, si.causal_pos, si.queries, si.block_rows, n_threads=8)
+            out = run_lib_step(pair, g, si)
+            compare_step(pair, g, si, res, out)
+            compare_counts(pair, g, res)
+            sis.append(si)
+        acc = make_accepted(w, step, sis[0].k_active)
+        pair.orc.commit(acc)
+        pair.lib.commit(acc)
+        n = n + 1 + acc
+    pair.lib.close()
+
+
+def test_mla_128_heads_split_keys():
+    """Two head groups of 64 and key splits merged by the combine pass."""
+    w = _mla_small(n_req=2, n_groups=1, n_heads=128, q_max=4, topk=1024, ring_window=64,
+                   n_prefix=2, hot_slots=2048, var_k=False)
+    pair = build_pair(w)
+    assert pair.lib.info["attn_head_groups"] == 2 and pair.lib.info["attn_splits"] > 1
+    si = make_step_inputs(w, 0, 0, pair.hist_len)
+    res = pair.orc.verify_step(0, si.topk, si.causal_pos, si.queries, si.block_rows, n_threads=8)
+    out = run_lib_step(pair, 0, si)
+    compare_step(pair, 0, si, res, out)
+    pair.lib.close()
+
+
+def test_ring_block_only_reading():
+    w = _tiny()
+    pair = build_pair(w, block_only=True)
+    si = make_step_inputs(w, 0, 0, pair.hist_len)
+    res = pair.orc.verify_step(0, si.topk, si.causal_pos, si.queries, si.block_rows)
+    out = run_lib_step(pair, 0, si)
+    compare_step(pair, 0, si, res, out)
+    pair.lib.close()
+
+
+def test_outputs_bitwise_identical_across_cache_states():
+    w = _mla_small(n_groups=1, var_k=False)
+    outs, misses, unions = [], [], []
+    for warm, rho in ((False, 0.0), (True, 0.0), (True, 0.5)):
+        pair = build_pair(w, warm=warm, rho=rho, with_oracle=False)
+        si = make_step_inputs(w, 0, 0, pair.hist_len)
+        outs.append(run_lib_step(pair, 0, si))
+        _, last = pair.lib.stats(0)
+        misses.append(last["union_miss"])
+        unions.append(last["union_rows"])
+        pair.lib.close()
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+    assert unions[0] == unions[1] == unions[2]
+    assert misses[0] > misses[1] > misses[2]
+
+
+def test_resident_tier_parity():
+    w = _mla_small(n_groups=1)
+    pair = build_pair(w, rho=0.3)
+    si = make_step_inputs(w, 0, 0, pair.hist_len)
+    res = pair.orc.verify_step(0, si.topk, si.causal_pos, si.queries, si.block_rows, n_threads=8)
+    out = run_lib_step(pair, 0, si)
+    compare_step(pair, 0, si, res, out)
+    compare_counts(pair, 0, res)
+    for r in range(w.n_req):
+        _exact_vs_topk(pair, 0, r, si.topk[r])
+    pair.lib.close()
+
+
+def test_inactive_requests_and_queries():
+    w = _mla_small(n_groups=1)
+    pair = build_pair(w)
+    si = make_step_inputs(w, 0, 0, pair.hist_len)
+    si.causal_pos[1, :] = -1                  # whole request inactive
+    si.causal_pos[2, 3:] = -1                 # inactive suffix
+    res = pair.orc.verify_step(0, si.topk, si.causal_pos, si.queries, si.block_rows, n_threads=8)
+    out = run_lib_step(pair, 0, si)
+    compare_step(pair, 0, si, res, out)
+    compare_counts(pair, 0, res)
+    assert (out[1] == 0).all()
+    pair.lib.close()
+
+
+def test_poisoned_arena_after_readers():
+    """With arena poisoning the step's outputs are unchanged: the arena is
+    overwritten only after attention and copy-back have read it."""
+    w = _mla_small(n_groups=1, var_k=False)
+    outs = []
+    for flags in (0, 2):
+        pair = build_pair(w, with_oracle=False, lib_kw=dict(flags=flags, n_chunks=2))
+        si = make_step_inputs(w, 0, 0, pair.hist_len)
+        outs.append(run_lib_step(pair, 0, si))
+        if flags:
+            L = pair.lib.last_lists(0, 0)
+            staged = L["loc"][L["loc"] >= 0]
+            staged = staged[(staged >> 29) == 1][:4]
+            if staged.size:
+                assert (pair.lib.read_rows(0, staged) == 0x7fc0).all()
+        pair.lib.close()
+    assert np.array_equal(outs[0], outs[1])
