@@ -95,6 +95,14 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     if not os.path.exists(p):
         raise RuntimeError("libkvhier.so not found at %s: build it with "
                            "`python -m hierarchical_sparse_kv_verify_amd.build`" % p)
+    # torch ships its own HIP runtime under the same soname (libamdhip64.so.7).
+    # Loading torch first makes the library bind to that runtime, so torch's
+    # allocations and stream handles belong to the runtime the library uses;
+    # loading the library first would put a second runtime in the process.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     L = ctypes.CDLL(p)
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
     sig = {

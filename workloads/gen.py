@@ -246,7 +246,8 @@ def make_step_inputs(w: Workload, group: int, step: int, hist_len: np.ndarray,
     if k_active is None:
         k_active = np.full(N, Q, dtype=np.int32)
         if w.var_k:
-            kr = _seeds(w, group, _P_STEP, step, 99, n=1)[0]
+            # K_r belongs to the request, not to a layer group
+            kr = _seeds(w, 0, _P_STEP, step, 99, n=1)[0]
             k_active = kr.integers(1, Q + 1, size=N).astype(np.int32)
     drawn = [None] * N
     req_iter = range(N) if requests is None else [int(x) for x in requests]
