@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Benchmark of the speculative verification step on one MI355X.
+
+A step is one verification pass of every layer group over one batch of
+synthetic input (ring write, resolution plan, host fetch of missing rows,
+sparse attention, copy-back).  Inputs are resident in HBM / pinned host
+memory before timing starts; the hot-cache state is restored from a device
+snapshot before every step, outside the timed region, so each step resolves
+at the workload's configured hit rate (``--retained`` skips the restore).
+
+Prints one JSON line: verified query-tokens/s (whole job), the roofline of the
+dominant kernel measured with HIP events on the streams the kernels run on,
+every kernel's roofline, and the oracle timed on the host cores over a
+bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_PCIE_GBS = 64.0           # PCIe 5.0 x16, one direction (host link of the MI355X)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mla128")
+    ap.add_argument("--rho", type=float, default=0.0, help="static resident fraction of rows")
+    ap.add_argument("--n-chunks", type=int, default=0)
+    ap.add_argument("--retained", action="store_true", help="keep the cache state between steps")
+    ap.add_argument("--timing-steps", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-requests", type=int, default=16)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the verification step shards by request with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from hierarchical_sparse_kv_verify_amd import KV_FLAG_TIMING
+    from tests.pair import build_pair, to_device
+    from workloads import WORKLOADS, make_history, make_step_inputs, shrink
+    from workloads.gen import make_hist_len
+
+    w = WORKLOADS[args.workload]
+    if args.rho > 0:
+        w = shrink(w, rho=args.rho)
+    torch.cuda.set_device(0)
+    t_setup = time.perf_counter()
+    log("bench: generating %s (%d requests x %d groups)" % (w.name, w.n_req, w.n_groups))
+    hl = make_hist_len(w)
+    hists = [make_history(w, g, hl) for g in range(w.n_groups)]
+    log("bench: host rows ready (%.1fs); creating the library state" % (time.perf_counter() - t_setup))
+    pair = build_pair(w, rho=args.rho, with_oracle=False, histories=hists,
+                      lib_kw=dict(n_chunks=args.n_chunks))
+    lib = pair.lib
+    G = w.n_groups
+    sis = [make_step_inputs(w, g, 0, hl) for g in range(G)]
+    dev = [to_device(si) for si in sis]
+    out = torch.zeros((w.n_req, w.q_max, w.n_heads, w.d_v), dtype=torch.int16, device="cuda")
+    for g in range(G):
+        lib.save_cache(g)
+    torch.cuda.synchronize()
+    log("bench: setup done in %.1fs; info %s" % (time.perf_counter() - t_setup, lib.info))
+
+    def restore():
+        if not args.retained:
+            for g in range(G):
+                lib.restore_cache(g)
+
+    def step():
+        for g in range(G):
+            d = dev[g]
+            lib.verify_step(g, d["queries"], d["topk"], d["causal"], d["ring"], out)
+
+    for _ in range(args.warmup):
+        restore()
+        step()
+    torch.cuda.synchronize()
+    lib.reset_stats()
+    times = []
+    for i in range(args.steps):
+        restore()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        step()
+        torch.cuda.synchronize()
+        times.append(time.perf_counter() - t0)
+    ms = 1000.0 * float(np.mean(times))
+    cum = [lib.stats(g)[0] for g in range(G)]
+    log("bench: %d steps, %.3f ms/step (min %.3f, max %.3f)" %
+        (args.steps, ms, 1000 * min(times), 1000 * max(times)))
+
+    # per-kernel durations: HIP events recorded around every launch on its own stream
+    lib.set_flags(KV_FLAG_TIMING)
+    lib.reset_stats()
+    for _ in range(args.timing_steps):
+        restore()
+        step()
+    torch.cuda.synchronize()
+    tim = [lib.stats(g)[0] for g in range(G)]
+    lib.set_flags(0)
+
+    row_bytes = 2 * w.row_elems
+    queries_per_step = int(sum(int(c["active_queries"]) for c in cum)) // max(1, args.steps) // G
+    sel_per_step = sum(int(c["selections"]) for c in cum) / args.steps
+    union_per_step = sum(int(c["union_rows"]) for c in cum) / args.steps
+    miss_per_step = sum(int(c["union_miss"]) for c in cum) / args.steps
+    selmiss_per_step = sum(int(c["sel_miss"]) for c in cum) / args.steps
+    value = queries_per_step / (ms / 1000.0)
+
+    # algorithmic work of the timing pass
+    T = args.timing_steps
+    tot = lambda key: sum(float(t[key]) for t in tim)
+    fetched = sum(int(t["union_miss"]) for t in tim) * row_bytes
+    n_ring_rows = 0
+    for si in sis:
+        for r in range(w.n_req):
+            n_r = int(si.causal_pos[r, 0])
+            if n_r < 0:
+                continue
+            lo0 = max(0, n_r - w.ring_window + 1)
+            for j in range(w.q_max):
+                p = int(si.causal_pos[r, j])
+                if p >= 0:
+                    n_ring_rows += p - max(lo0, p - w.ring_window + 1, 0) + 1
+    sel_rows = sum(int(t["selections"]) for t in tim) / T
+    rows_attended = (sel_rows + n_ring_rows) * T
+    q_bytes = queries_per_step * G * T * w.n_heads * (w.d_qk + w.d_v) * 2
+    attn_bytes = rows_attended * row_bytes + q_bytes + queries_per_step * G * T * w.topk * 4
+    attn_flops = 2.0 * w.n_heads * rows_attended * (w.d_qk + w.d_v)
+    ms_attn = tot("ms_attn") + tot("ms_combine")
+    ms_gather = tot("ms_gather")
+    ms_plan = tot("ms_plan")
+    ms_promote = tot("ms_promote")
+    n_launch = lambda key: max(1, int(sum(int(t[key]) for t in tim)))
+    promote_bytes = 2 * sum(int(t["promoted"]) for t in tim) * row_bytes
+    plan_bytes = (sum(int(t["active_queries"]) for t in tim) * w.topk * 4 * 3 +
+                  sum(int(t["union_rows"]) for t in tim) * 4 * 4)
+
+    def rl(bound, work, ms_total, launches, peak, unit, traffic=None):
+        achieved = (work / (ms_total / 1000.0)) / (1e9 if unit == "GB/s" else 1e12) if ms_total > 0 else 0.0
+        return {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4) if peak else None, "traffic": traffic,
+                "avg_launch_ms": round(ms_total / launches, 5), "launches": launches,
+                "work_per_launch": work / launches}
+
+    rooflines = {
+        "miss_gather": rl("host_link", fetched, ms_gather, n_launch("n_gather"), PEAK_PCIE_GBS, "GB/s"),
+        "sparse_attn": rl("hbm", attn_bytes, ms_attn, n_launch("n_attn"), PEAK_HBM_GBS, "GB/s"),
+        "sparse_attn_mfma": rl("mfma", attn_flops, ms_attn, n_launch("n_attn"), PEAK_BF16_TFLOPS, "TFLOP/s"),
+        "plan": rl("hbm", plan_bytes, ms_plan, n_launch("n_plan"), PEAK_HBM_GBS, "GB/s"),
+        "promote": rl("hbm", promote_bytes, ms_promote, n_launch("n_promote"), PEAK_HBM_GBS, "GB/s"),
+    }
+    rooflines["miss_gather"]["frac_of_measured_h2d"] = round(
+        rooflines["miss_gather"]["achieved"] / 57.3, 4)
+    kernel_ms = {"miss_gather": ms_gather, "sparse_attn": ms_attn, "plan": ms_plan, "promote": ms_promote}
+    dominant = max(kernel_ms, key=kernel_ms.get)
+    roofline = dict(rooflines[dominant])
+    roofline["kernel"] = dominant
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, hists, hl, sis[0], args.cpu_requests)
+
+    line = {
+        "metric": "verified query-tokens/s per GPU and selected-rows/s; % HBM and host-link peak",
+        "value": round(value, 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "requests": w.n_req, "layer_groups": G, "q_max": w.q_max,
+                   "topk": w.topk, "hot_slots": w.hot_slots, "ring_window": w.ring_window,
+                   "heads": w.n_heads, "row_bytes": row_bytes, "history_rows": [int(hl.min()), int(hl.max())],
+                   "resident_fraction": args.rho, "cache_state": "retained" if args.retained else "restored",
+                   "n_chunks": lib.info["n_chunks"], "attn_splits": lib.info["attn_splits"]},
+        "selected_rows_per_s": round(sel_per_step / (ms / 1000.0), 1),
+        "unique_rows_per_s": round(union_per_step / (ms / 1000.0), 1),
+        "fetched_rows_per_step": miss_per_step,
+        "fetched_bytes_per_step": miss_per_step * row_bytes,
+        "host_fetch_share_distinct": round(miss_per_step / max(1.0, union_per_step), 5),
+        "host_fetch_share_selected": round(selmiss_per_step / max(1.0, sel_per_step), 5),
+        "missing_selections_per_fetched_row": round(selmiss_per_step / max(1.0, miss_per_step), 4),
+        "kernel_ms_per_step": {k: round(v / T, 4) for k, v in kernel_ms.items()},
+        "roofline": roofline,
+        "rooflines": rooflines,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    lib.close()
+
+
+def cpu_baseline(w, hists, hl, si, n_req_sample):
+    """The oracle, as it stands, on the host cores over the first requests of
+    layer group 0 (resolution + attention of all their queries)."""
+    import numpy as np
+
+    import oracle
+    from tests.pair import oracle_config, prefill_rows
+    from workloads import make_hot_warm_set
+
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    reqs = list(range(min(n_req_sample, w.n_req)))
+    # no commit happens here, so the oracle may read the generator's rows in place
+    orc = oracle.HierOracle(oracle_config(w), hists, hl, requests=reqs)
+    for r, hs in enumerate(make_hot_warm_set(w, 0, hl, si)):
+        orc.set_hot(0, r, hs[0], hs[1])
+    for r in reqs:
+        first, rows = prefill_rows(hists[0], w, r, int(hl[r]))
+        orc.ring_load(0, r, first, rows)
+    log("bench: oracle on %d requests x %d queries, %d threads" % (len(reqs), w.q_max, cores))
+    t0 = time.perf_counter()
+    res = orc.verify_step(0, si.topk, si.causal_pos, si.queries, si.block_rows, n_threads=cores)
+    dt = time.perf_counter() - t0
+    nq = len(res.out)
+    # one query token of a step passes through every layer group
+    value = nq / (dt * w.n_groups)
+    log("bench: oracle %.2fs for %d query tokens of one group" % (dt, nq))
+    return {"value": round(value, 3), "unit": "query-tokens/s", "cores": cores, "kind": "oracle",
+            "sample": "%d requests x %d queries of layer group 0 of %s (resolution + attention), "
+                      "scaled by %d layer groups per step; %.2f s" % (len(reqs), w.q_max, w.name,
+                                                                       w.n_groups, dt)}
+
+
+if __name__ == "__main__":
+    main()

@@ -31,6 +31,7 @@ EXPORTED = [
     "kv_hier_set_resident", "kv_hier_clear_resident", "kv_hier_ring_load",
     "kv_hier_verify_step", "kv_hier_commit", "kv_hier_stats", "kv_hier_reset_stats",
     "kv_hier_last_lists", "kv_hier_slot_table", "kv_hier_read_rows", "kv_hier_sync",
+    "kv_hier_set_flags", "kv_hier_cache_snapshot",
 ]
 
 
@@ -125,6 +126,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "kv_hier_slot_table": ([vp, i32, i32, vp, vp], i32),
         "kv_hier_read_rows": ([vp, i32, vp, i32, vp], i32),
         "kv_hier_sync": ([vp], i32),
+        "kv_hier_set_flags": ([vp, ctypes.c_int32], i32),
+        "kv_hier_cache_snapshot": ([vp, i32, i32], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -296,6 +299,16 @@ class KVHier:
 
     def sync(self):
         self._check(self._lib.kv_hier_sync(self._h))
+
+    def set_flags(self, flags: int):
+        self._check(self._lib.kv_hier_set_flags(self._h, int(flags)))
+        self.cfg["flags"] = int(flags)
+
+    def save_cache(self, g: int):
+        self._check(self._lib.kv_hier_cache_snapshot(self._h, g, 0))
+
+    def restore_cache(self, g: int):
+        self._check(self._lib.kv_hier_cache_snapshot(self._h, g, 1))
 
 
 def loc_code(tier: int, index: int) -> int:

@@ -47,6 +47,10 @@ struct Group {
   const uint4* tails_dev = nullptr;       // host-mapped tails
   int t = 0;
   int64_t calls = 0;
+  // cache-state snapshot (kv_hier_cache_snapshot)
+  uint16_t* snap_hot = nullptr;
+  int32_t *snap_row = nullptr, *snap_lu = nullptr, *snap_map = nullptr;
+  int snap_t = -1;
   double ms[K_NUM] = {0};
   int64_t nt[K_NUM] = {0};
 };
@@ -287,6 +291,10 @@ void free_all(kv_hier* h) {
     (void)hipFree(G.req_info);
     (void)hipFree(G.req_counts);
     (void)hipFree(G.cum);
+    (void)hipFree(G.snap_hot);
+    (void)hipFree(G.snap_row);
+    (void)hipFree(G.snap_lu);
+    (void)hipFree(G.snap_map);
     (void)hipFree(const_cast<uint4**>(G.prefix_table));
     for (void* p : G.prefix_host) if (p) (void)hipHostFree(p);
     if (G.tails_host) (void)hipHostFree(G.tails_host);
@@ -949,6 +957,47 @@ int kv_hier_read_rows(kv_hier_t* h, int g, const int32_t* locs, int n, void* row
 int kv_hier_sync(kv_hier_t* h) {
   if (!h) return KV_EINVAL;
   return sync_all(h);
+}
+
+int kv_hier_set_flags(kv_hier_t* h, int32_t flags) {
+  if (!h) return KV_EINVAL;
+  if (flags & ~(KV_FLAG_TIMING | KV_FLAG_POISON)) return fail(h, KV_EINVAL, "unknown flags %d", flags);
+  int rc = sync_all(h);
+  if (rc) return rc;
+  h->cfg.flags = flags;
+  return KV_OK;
+}
+
+int kv_hier_cache_snapshot(kv_hier_t* h, int g, int op) {
+  int rc = check_group(h, g);
+  if (rc) return rc;
+  if (op != 0 && op != 1) return fail(h, KV_EINVAL, "snapshot op %d", op);
+  if ((rc = sync_all(h))) return rc;
+  Group& G = h->grp[g];
+  const size_t NB = size_t(h->cfg.n_req) * h->cfg.hot_slots, NL = size_t(h->cfg.n_req) * h->L;
+  const size_t hot_bytes = NB * h->row_bytes;
+  if (op == 0) {
+    if (!G.snap_hot) {
+      if ((rc = dev_alloc(h, &G.snap_hot, NB * h->cfg.row_elems, nullptr))) return rc;
+      if ((rc = dev_alloc(h, &G.snap_row, NB, nullptr))) return rc;
+      if ((rc = dev_alloc(h, &G.snap_lu, NB, nullptr))) return rc;
+      if ((rc = dev_alloc(h, &G.snap_map, NL, nullptr))) return rc;
+    }
+    HIPCHK(h, hipMemcpy(G.snap_hot, G.hot, hot_bytes, hipMemcpyDeviceToDevice));
+    HIPCHK(h, hipMemcpy(G.snap_row, G.slot_row, NB * 4, hipMemcpyDeviceToDevice));
+    HIPCHK(h, hipMemcpy(G.snap_lu, G.slot_lu, NB * 4, hipMemcpyDeviceToDevice));
+    HIPCHK(h, hipMemcpy(G.snap_map, G.slot_map, NL * 4, hipMemcpyDeviceToDevice));
+    G.snap_t = G.t;
+  } else {
+    if (G.snap_t < 0) return fail(h, KV_ESTATE, "no snapshot of group %d", g);
+    HIPCHK(h, hipMemcpy(G.hot, G.snap_hot, hot_bytes, hipMemcpyDeviceToDevice));
+    HIPCHK(h, hipMemcpy(G.slot_row, G.snap_row, NB * 4, hipMemcpyDeviceToDevice));
+    HIPCHK(h, hipMemcpy(G.slot_lu, G.snap_lu, NB * 4, hipMemcpyDeviceToDevice));
+    HIPCHK(h, hipMemcpy(G.slot_map, G.snap_map, NL * 4, hipMemcpyDeviceToDevice));
+    G.t = G.snap_t;
+  }
+  HIPCHK(h, hipDeviceSynchronize());
+  return KV_OK;
 }
 
 }  // extern "C"

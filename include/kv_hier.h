@@ -225,6 +225,16 @@ int kv_hier_hist_len(kv_hier_t *h, int32_t *hist_len);
 /* Waits for every stream the handle uses. */
 int kv_hier_sync(kv_hier_t *h);
 
+/* Replaces the KV_FLAG_* bits set at create (takes effect for later calls). */
+int kv_hier_set_flags(kv_hier_t *h, int32_t flags);
+
+/* Cache-state snapshot of group g: op 0 saves the hot rows, slot tables,
+ * row->slot map and step counter into library-owned device memory (allocated
+ * on the first save); op 1 restores them, so a following step with the same
+ * inputs resolves exactly as the step after the save did.  Waits for
+ * outstanding work.  KV_ESTATE when restoring without a save. */
+int kv_hier_cache_snapshot(kv_hier_t *h, int g, int op);
+
 #ifdef __cplusplus
 }
 #endif

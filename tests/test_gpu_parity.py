@@ -240,3 +240,29 @@ def test_poisoned_arena_after_readers():
                 assert (pair.lib.read_rows(0, staged) == 0x7fc0).all()
         pair.lib.close()
     assert np.array_equal(outs[0], outs[1])
+
+
+def test_full_size_mla128_sampled():
+    """The benchmarked shape (128 requests x ~100K rows, 4 layer groups, the
+    default chunked launch): sampled requests bit-exact, sampled queries within
+    tolerance; whole-step counters consistent."""
+    w = WORKLOADS["mla128"]
+    reqs = [0, 37, 126, 127]
+    pair = build_pair(w, oracle_requests=reqs)
+    assert pair.lib.info["n_chunks"] > 1
+    attend = {(r, j) for r in reqs for j in (0, 3, 7)}
+    for g in range(w.n_groups):
+        si = make_step_inputs(w, g, 0, pair.hist_len)
+        res = pair.orc.verify_step(g, si.topk, si.causal_pos, si.queries, si.block_rows,
+                                   attend=attend, n_threads=16)
+        out = run_lib_step(pair, g, si)
+        compare_step(pair, g, si, res, out, requests=reqs)
+        _, last = pair.lib.stats(g)
+        assert last["active_queries"] == w.n_req * w.q_max
+        assert last["selections"] == w.n_req * w.q_max * w.topk
+        assert last["fetched_bytes"] == last["union_miss"] * 2 * w.row_elems
+        assert last["union_miss"] == last["promoted"] + last["overflow"]
+        assert 0.12 < last["union_miss"] / last["union_rows"] < 0.16
+        for r in reqs:
+            _exact_vs_topk(pair, g, r, si.topk[r])
+    pair.lib.close()
