@@ -206,8 +206,6 @@ int check_req(kv_hier* h, int r) {
   return KV_OK;
 }
 
-// Ring size of "Adaptive DHiSparse" §3.4 eq. (9): page-rounded window plus block.
-int ring_size(int W, int p, int kmax) { return p * ((W + p - 1 + kmax + p - 1) / p); }
 
 int upload(kv_hier* h, void* dst, const void* src, size_t bytes) {
   if (bytes == 0) return KV_OK;
@@ -314,6 +312,9 @@ void free_all(kv_hier* h) {
   if (h->side) (void)hipStreamDestroy(h->side);
 }
 
+// Ring size of "Adaptive DHiSparse" §3.4 eq. (9): page-rounded window plus block.
+int ring_size(int W, int p, int kmax) { return p * ((W + p - 1 + kmax + p - 1) / p); }
+
 int validate(kv_hier* h, const kv_hier_config& c) {
   if (c.n_req <= 0 || c.n_groups <= 0 || c.n_arenas <= 0 || c.hist_cap <= 0 || c.row_elems <= 0 ||
       c.d_qk <= 0 || c.d_v <= 0 || c.v_off < 0 || c.n_heads <= 0 || c.q_max <= 0 || c.topk <= 0 ||
@@ -331,7 +332,8 @@ int validate(kv_hier* h, const kv_hier_config& c) {
                 c.v_off, c.d_v);
   const int64_t lim = int64_t(1) << kTierShift;
   if (int64_t(c.n_req) * c.hot_slots >= lim || int64_t(c.n_req) * c.q_max * c.topk >= lim ||
-      c.resident_cap >= lim || int64_t(c.hist_cap) >= lim)
+      c.resident_cap >= lim || int64_t(c.hist_cap) >= lim ||
+      int64_t(c.n_req) * ring_size(c.ring_window, c.ring_page, c.q_max) >= lim)
     return fail(h, KV_EUNSUPPORTED, "an index space exceeds 2^29 rows");
   if (c.hot_slots > 16384) return fail(h, KV_EUNSUPPORTED, "hot_slots > 16384");
   return KV_OK;
@@ -381,7 +383,7 @@ static int create_impl(kv_hier* h) {
     if (h->plan_lds > 160 * 1024) return fail(h, KV_EUNSUPPORTED, "plan LDS %zu", h->plan_lds);
   }
   // request chunks for the fetch/attention pipeline
-  h->n_chunks = c.n_chunks > 0 ? std::min(c.n_chunks, N) : (N >= 64 ? 8 : (N >= 16 ? 4 : 1));
+  h->n_chunks = c.n_chunks > 0 ? std::min(c.n_chunks, N) : (N >= 64 ? 4 : (N >= 16 ? 2 : 1));
   for (int i = 0; i <= h->n_chunks; ++i) h->chunk_lo.push_back(int(int64_t(N) * i / h->n_chunks));
   {
     const int hpw = attn_heads_per_wg(c.n_heads);
@@ -390,7 +392,7 @@ static int create_impl(kv_hier* h) {
     const int64_t wgs = int64_t(nc) * c.q_max * h->head_groups;
     const int tiles = (c.topk + c.ring_window + 31) / 32;
     int s = 1;
-    if (wgs < 512) s = int(std::min<int64_t>(8, (512 + wgs - 1) / wgs));
+    if (wgs < 128) s = int(std::min<int64_t>(8, (256 + wgs - 1) / wgs));
     s = std::max(1, std::min(s, tiles / 4));
     h->splits = s;
     if (s > 1) {
