@@ -75,8 +75,10 @@ struct kv_hier {
   std::vector<int> chunk_lo;
   int chunk_words = 0, sort_cap = 1;
   size_t plan_lds = 0;
-  hipStream_t side = nullptr;
+  hipStream_t side = nullptr;       // host fetch
+  hipStream_t work = nullptr;       // the rest of the step when CUs are partitioned (else null)
   hipEvent_t ev_plan = nullptr;
+  hipEvent_t ev_in = nullptr, ev_out = nullptr;
   std::vector<hipEvent_t> ev_fetched;
   std::vector<std::vector<hipEvent_t>> ev_free;
   std::vector<std::vector<char>> free_recorded;
@@ -306,6 +308,9 @@ void free_all(kv_hier* h) {
   for (auto& t : h->pending) { (void)hipEventDestroy(t.a); (void)hipEventDestroy(t.b); }
   for (hipEvent_t e : h->pool) (void)hipEventDestroy(e);
   if (h->ev_plan) (void)hipEventDestroy(h->ev_plan);
+  if (h->ev_in) (void)hipEventDestroy(h->ev_in);
+  if (h->ev_out) (void)hipEventDestroy(h->ev_out);
+  if (h->work) (void)hipStreamDestroy(h->work);
   if (h->ev_commit) (void)hipEventDestroy(h->ev_commit);
   for (hipEvent_t e : h->ev_fetched) (void)hipEventDestroy(e);
   for (auto& v : h->ev_free) for (hipEvent_t e : v) (void)hipEventDestroy(e);
@@ -343,7 +348,10 @@ int validate(kv_hier* h, const kv_hier_config& c) {
 
 extern "C" {
 
-const char* kv_hier_last_error(const kv_hier_t* h) { return h ? h->err.c_str() : "null handle"; }
+// message of the last failed kv_hier_create on this thread (no handle exists then)
+static thread_local std::string g_create_error = "null handle";
+
+const char* kv_hier_last_error(const kv_hier_t* h) { return h ? h->err.c_str() : g_create_error.c_str(); }
 
 void kv_hier_destroy(kv_hier_t* h) {
   if (!h) return;
@@ -479,8 +487,28 @@ static int create_impl(kv_hier* h) {
     }
     h->h_commit = static_cast<int32_t*>(hc);
   }
-  HIPCHK(h, hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking));
+  if (c.fetch_cus > 0) {
+    // partition the CUs: a few for the PCIe-latency-bound fetch, the rest for the step
+    hipDeviceProp_t prop;
+    HIPCHK(h, hipGetDeviceProperties(&prop, h->device));
+    const int ncu = prop.multiProcessorCount;
+    if (c.fetch_cus >= ncu) return fail(h, KV_EINVAL, "fetch_cus %d >= %d CUs", c.fetch_cus, ncu);
+    const int words = (ncu + 31) / 32;
+    std::vector<uint32_t> fm(words, 0), wm(words, 0);
+    // mask bit i belongs to XCD i mod 8 and every stream needs CUs on every XCD:
+    // the first fetch_cus bits give the fetch the same share of each XCD
+    if (c.fetch_cus % 8 != 0) return fail(h, KV_EINVAL, "fetch_cus %d is not a multiple of 8", c.fetch_cus);
+    for (int cu = 0; cu < c.fetch_cus; ++cu) fm[cu / 32] |= 1u << (cu % 32);
+    for (int cu = 0; cu < ncu; ++cu)
+      if (!((fm[cu / 32] >> (cu % 32)) & 1u)) wm[cu / 32] |= 1u << (cu % 32);
+    HIPCHK(h, hipExtStreamCreateWithCUMask(&h->side, uint32_t(words), fm.data()));
+    HIPCHK(h, hipExtStreamCreateWithCUMask(&h->work, uint32_t(words), wm.data()));
+  } else {
+    HIPCHK(h, hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking));
+  }
   HIPCHK(h, hipEventCreateWithFlags(&h->ev_plan, hipEventDisableTiming));
+  HIPCHK(h, hipEventCreateWithFlags(&h->ev_in, hipEventDisableTiming));
+  HIPCHK(h, hipEventCreateWithFlags(&h->ev_out, hipEventDisableTiming));
   HIPCHK(h, hipEventCreateWithFlags(&h->ev_commit, hipEventDisableTiming));
   h->ev_fetched.assign(h->n_chunks, nullptr);
   for (auto& e : h->ev_fetched) HIPCHK(h, hipEventCreateWithFlags(&e, hipEventDisableTiming));
@@ -500,6 +528,7 @@ int kv_hier_create(const kv_hier_config* cfg, kv_hier_t** out) {
   int rc = validate(h, *cfg);
   if (!rc) rc = create_impl(h);
   if (rc) {
+    g_create_error = h->err.empty() ? "kv_hier_create failed" : h->err;
     (void)hipDeviceSynchronize();
     free_all(h);
     delete h;
@@ -681,7 +710,13 @@ int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t*
   if (rc) return rc;
   if (!queries || !topk_idx || !causal_pos || !ring_rows || !out) return fail(h, KV_EINVAL, "null device pointer");
   const kv_hier_config& c = h->cfg;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipStream_t caller = static_cast<hipStream_t>(stream);
+  hipStream_t s = caller;
+  if (h->work) {           // the step runs on the partitioned stream, ordered after the caller's work
+    HIPCHK(h, hipEventRecord(h->ev_in, caller));
+    HIPCHK(h, hipStreamWaitEvent(h->work, h->ev_in, 0));
+    s = h->work;
+  }
   Group& G = h->grp[g];
   const int N = c.n_req;
   const int a = g % c.n_arenas;
@@ -781,6 +816,10 @@ int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t*
     }
     HIPCHK(h, hipEventRecord(h->ev_free[a][ch], s));
     h->free_recorded[a][ch] = 1;
+  }
+  if (h->work) {
+    HIPCHK(h, hipEventRecord(h->ev_out, s));
+    HIPCHK(h, hipStreamWaitEvent(caller, h->ev_out, 0));
   }
   return KV_OK;
 }

@@ -88,6 +88,9 @@ typedef struct {
   int64_t resident_cap;     /* rows of the resident pool per group (0 = no resident tier) */
   float softmax_scale;      /* <= 0 selects 1/sqrt(d_qk)                                 */
   int32_t flags;            /* KV_FLAG_*                                                 */
+  int32_t fetch_cus;        /* >0: CUs reserved for the host fetch (CU-masked streams: the
+                               fetch runs on those CUs, the rest of the step on the others);
+                               0: every stream may use every CU                          */
 } kv_hier_config;
 
 /* Counters of one layer group (kv_hier_stats).  "union_*" count distinct rows
@@ -143,7 +146,8 @@ int kv_hier_create(const kv_hier_config *cfg, kv_hier_t **out);
 /* Frees everything; waits for outstanding work first.  NULL is accepted. */
 void kv_hier_destroy(kv_hier_t *h);
 
-/* Message of the last failing call on h (never NULL). */
+/* Message of the last failing call on h (never NULL); with h == NULL, the
+ * message of the last failed kv_hier_create on the calling thread. */
 const char *kv_hier_last_error(const kv_hier_t *h);
 
 /* Sizes of what create allocated.  Host out-pointer. */

@@ -136,10 +136,10 @@ def _mla_small(**kw):
     return shrink(base, **kw)
 
 
-@pytest.mark.parametrize("n_chunks", [1, 2, 3])
-def test_mla_two_groups_two_steps(n_chunks):
+@pytest.mark.parametrize("n_chunks,fetch_cus", [(1, 0), (2, 0), (3, 0), (2, 16)])
+def test_mla_two_groups_two_steps(n_chunks, fetch_cus):
     w = _mla_small()
-    pair = build_pair(w, lib_kw=dict(n_chunks=n_chunks))
+    pair = build_pair(w, lib_kw=dict(n_chunks=n_chunks, fetch_cus=fetch_cus))
     n = pair.hist_len.copy()
     for step in range(2):
         sis = []
