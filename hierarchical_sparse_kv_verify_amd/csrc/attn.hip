@@ -260,7 +260,9 @@ __global__ __launch_bounds__(C::NT, 1) void attn_kernel(AttnArgs a) {
   const int r = a.r0 + rr;
   const int qi = r * a.Q + j;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hb = w / C::NDP, dq = w % C::NDP;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);      // wave-uniform: held in SGPRs
+  const int hb = w / C::NDP, dq = w % C::NDP;
   const int hl = hb * 32 + (lane & 31);               // head within the workgroup
   const int head = hg * 32 * C::HB + hl;
   const size_t blk = (size_t(qi) * a.head_groups + hg) * a.splits + sp;
@@ -361,9 +363,7 @@ __global__ __launch_bounds__(C::NT, 1) void attn_kernel(AttnArgs a) {
     for (int q = 0; q < C::NDP; ++q) {
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
-        float4 v;
-        if (q == dq) v = make_float4(acc[4 * i4], acc[4 * i4 + 1], acc[4 * i4 + 2], acc[4 * i4 + 3]);
-        else v = sx_blk[(q * 4 + i4) * 64];
+        const float4 v = sx_blk[(q * 4 + i4) * 64];   // own slice too: no divergent select
         if (q == 0) {
           s[4 * i4] = v.x; s[4 * i4 + 1] = v.y; s[4 * i4 + 2] = v.z; s[4 * i4 + 3] = v.w;
         } else {

@@ -26,31 +26,27 @@ __device__ inline const uint4* host_row(const HostRowSrc& s, int r, int row) {
   return s.tails + (size_t(r) * s.tail_rows + (row - s.prefix_len)) * s.row16;
 }
 
+// One 16-byte chunk in flight per lane with 32-bit incremental (row, chunk)
+// indices: the kernel needs few registers, so its waves fit on CUs that also
+// run attention workgroups (a fetch that must wait for free CUs loses most of
+// its host-link rate).
 __global__ __launch_bounds__(256) void miss_gather_kernel(HostRowSrc src, const int32_t* __restrict__ miss_rows,
                                                           const int32_t* __restrict__ req_info,
                                                           uint4* __restrict__ staging, int QK, int r0) {
   const int r = r0 + blockIdx.y;
   const int n = req_info[r * I_NUM + I_NMISS];
   const int row16 = src.row16;
-  const size_t total = size_t(n) * row16;
   const int32_t* mr = miss_rows + size_t(r) * QK;
   uint4* dst = staging + size_t(r) * QK * row16;
-  const size_t stride = size_t(gridDim.x) * blockDim.x;
-  size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  for (; i + 3 * stride < total; i += 4 * stride) {
-    uint4 v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const size_t ii = i + u * stride;
-      const int row = static_cast<int>(ii / row16), c = static_cast<int>(ii % row16);
-      v[u] = host_row(src, r, mr[row])[c];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) dst[i + u * stride] = v[u];
-  }
-  for (; i < total; i += stride) {
-    const int row = static_cast<int>(i / row16), c = static_cast<int>(i % row16);
-    dst[i] = host_row(src, r, mr[row])[c];
+  const int stride = gridDim.x * blockDim.x;
+  const int drow = stride / row16, dc = stride - drow * row16;
+  const int i0 = blockIdx.x * blockDim.x + threadIdx.x;
+  int row = i0 / row16, c = i0 - row * row16;
+  while (row < n) {
+    dst[size_t(row) * row16 + c] = host_row(src, r, mr[row])[c];
+    row += drow;
+    c += dc;
+    if (c >= row16) { c -= row16; ++row; }
   }
 }
 
