@@ -10,19 +10,26 @@
 //
 // Layout and schedule (one workgroup = one query x up to 64 heads x one key split):
 //  - rows are shared by all heads (MQA / absorbed MLA), so heads form the MFMA
-//    N dimension and 32-row tiles of K form M: S^T = K Q^T with
-//    v_mfma_f32_32x32x16_bf16; every lane then holds 16 scores of ONE head,
-//    which makes the online softmax a per-lane update plus one cross-half
-//    exchange, and the probabilities are already the B operand of
-//    O^T = V^T P^T (no register transpose).
-//  - waves come in pairs per 32-head block; the pair splits the key width for
-//    QK^T (partial scores summed through LDS in a fixed order) and the value
-//    width for PV, so Q fragments (registers) and O accumulators are halved.
-//  - a tile is gathered from HBM through location codes into registers one
-//    tile ahead (software prefetch), then written to LDS twice: row-major for
-//    the K operand and transposed (4 rows per 8-byte write) for the V operand.
-//  - softmax in fp32 with exp2 (scale folded with log2 e); P is rounded to bf16
-//    for the PV contraction, the normaliser is accumulated from fp32 P.
+//    N dimension and 32-row tiles form M: S^T = K Q^T with
+//    v_mfma_f32_32x32x16_bf16, then O^T = V^T P^T with the probabilities as
+//    the B operand.
+//  - four waves per 32-head block split the key width for S^T (partial scores
+//    meet in LDS) and the value width for O^T; each of the four then owns a
+//    quarter of the tile's rows for the softmax (reduce-scatter), so every
+//    score is exponentiated once; probabilities go to LDS as bf16 P^T.
+//  - a tile lives in LDS once, row-major with a 1168-byte row stride (36
+//    banks apart), double-buffered; K fragments are plain 16-byte reads and
+//    V^T fragments come from the same rows through ds_read_b64_tr_b16, with
+//    the value dims of an MFMA block interleaved (8 dims from each 32-dim
+//    group) so that both read patterns hit every bank once.
+//  - rows are gathered one tile ahead into registers: the 32 location codes
+//    of a tile are loaded one tile earlier, each wave decodes the codes of
+//    its own rows into wave-uniform addresses, and masked positions read a
+//    zero row, so no load depends on a per-lane branch.
+//  - online softmax in fp32 with exp2 (scale folded with log2 e): the running
+//    max of a head is raised only when a score exceeds it by more than 2^8,
+//    detected per tile with one ballot; the rare raise takes a second pass
+//    over the tile (tile max exchanged in LDS, O and l rescaled).
 //  - the sum order depends only on the list order and the split boundaries,
 //    never on where a row is cached, so outputs are bitwise identical across
 //    cache states.
@@ -36,6 +43,8 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // Global-address-space views: gathered rows and location codes are read with
 // global (not flat) loads, so waiting on LDS never waits on the prefetch.
 #define GLOBAL_AS __attribute__((address_space(1)))
@@ -49,10 +58,9 @@ __device__ __forceinline__ uint4 gload16(uintptr_t addr) {
 }
 
 constexpr int TILE = 32;
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;
-// The running max of a head is raised only when a tile's max exceeds it by
-// more than this (log2 units): numerator and normaliser always share the same
+// A score may exceed its head's running max by up to this much (log2 units)
+// before the max is raised: numerator and normaliser always share the same
 // max, so the result is unchanged, and p stays below 2^8.
 constexpr float kRescaleLog2 = 8.0f;
 
@@ -63,27 +71,27 @@ struct Cfg {
   static constexpr int NW = NDP * HB;
   static constexpr int NT = NW * 64;
   static constexpr int KS = D_QK / NDP / 16; // 16-wide k-steps over this wave's key part
-  static constexpr int DVB = D_V / NDP / 32; // 32-wide value blocks of this wave's value part
-  static constexpr int KCH = D_QK / 8;       // 16-byte chunks of the key
-  static constexpr int V0 = V_OFF / 8, VCH = D_V / 8;
-  static constexpr bool V_IN_K = (V_OFF == 0 && D_V <= D_QK);
-  static constexpr int KO0 = V_IN_K ? VCH : 0;          // first key-only chunk
-  static constexpr int NKO = V_IN_K ? (KCH - VCH) : KCH;
-  static constexpr int KSTR = D_QK + 8;      // key tile row stride (elements): 16 B mod 128 B
-  static constexpr int VSTR = TILE + 4;      // transposed value stride (elements)
-  // (4-row group, value chunk) load tasks; consecutive tasks take consecutive
-  // row groups, so a wave covers 8 row groups x 8 chunks: each load reads 8
-  // whole 128-byte lines and the transposed 8-byte LDS writes hit every bank
-  static constexpr int T1 = (TILE / 4) * VCH;
-  static constexpr int T2 = TILE * NKO;         // (row, key-only chunk) load tasks
-  static constexpr int T1PT = (T1 + NT - 1) / NT;
-  static constexpr int T2PT = (T2 + NT - 1) / NT;
-  static constexpr size_t LDS_K = size_t(TILE) * KSTR * 2;
-  static constexpr size_t LDS_V = size_t(D_V) * VSTR * 2;
-  static constexpr size_t LDS_S = size_t(NW) * 16 * 64 * 4;
-  static constexpr size_t LDS = LDS_K + LDS_V + LDS_S + TILE * 4;
+  static constexpr int DVB = D_V / NDP / 32; // 32-dim value blocks of this wave's value part
+  static constexpr int RCH = ROW / 8;        // 16-byte chunks per row
+  static constexpr int RPW = TILE / NW;      // rows of a tile gathered by one wave
+  // gather instructions per wave and tile: with rows of >= 64 chunks, one
+  // instruction per row for chunks 0..63 plus shared ones for the rest
+  static constexpr bool WIDE = RCH >= 64;
+  static constexpr int REST = WIDE ? RCH - 64 : 0;
+  static constexpr int NU = WIDE ? RPW + (RPW * REST + 63) / 64 : (RPW * RCH) / 64;
+  // row stride: 36 banks (dwords mod 64) apart
+  static constexpr int ROW_DW = ROW / 2;
+  static constexpr int KSTR = ROW + 2 * ((36 - ROW_DW % 64 + 64) % 64);
+  static constexpr int KBUF = TILE * KSTR;   // elements per tile buffer
+  static constexpr int PSTR = TILE + 8;      // P^T row stride (elements): 20 banks
+  static constexpr size_t LDS_K = size_t(2) * KBUF * 2;
+  static constexpr size_t LDS_S = size_t(NW) * 4 * 64 * 16;
+  static constexpr size_t LDS_P = size_t(HB) * 32 * PSTR * 2;
+  static constexpr size_t LDS_M = size_t(NW) * 32 * 4;
+  static constexpr size_t LDS = LDS_K + LDS_S + LDS_P + LDS_M + 16;
   static_assert(D_QK % (NDP * 16) == 0 && D_V % (NDP * 32) == 0 && ROW % 8 == 0, "shape");
-  static_assert(V_IN_K || V_OFF >= D_QK, "value range must lie inside or after the key range");
+  static_assert(V_OFF % 8 == 0 && V_OFF + D_V <= ROW && D_QK <= ROW, "row layout");
+  static_assert(WIDE ? (REST <= 64 && 64 % REST == 0) : (64 % RCH == 0 && (RPW * RCH) % 64 == 0), "gather");
   static_assert(LDS <= 160 * 1024, "LDS");
 };
 
@@ -92,18 +100,16 @@ struct RowCtx {
   int k, n_total, Rd;
   int ring_row0;    // ring row of the window's first position: r*R_d + (lo mod R_d)
   int ring_end;     // (r+1)*R_d: ring rows wrap from here back to r*R_d
-  size_t ring_base;
-  uintptr_t hot, d_staging, d_resident, d_ring;   // d_*: pool base minus hot base
+  uintptr_t hot, d_staging, d_resident, d_ring, zero;   // d_*: pool base minus hot base
 };
 
-// Location codes: a list entry's code is loaded raw (c.loc) one tile before
-// its row is loaded and is only decoded when the row load is issued, so the
-// wave never waits on a code load; positions past the list are the ring
-// window (tier 3, index r*R_d + pos mod R_d) or, past its end, masked (-1).
-__device__ __forceinline__ int raw_code(const RowCtx& c, int idx) {
-  return c.loc[min(idx, c.k - 1)];                  // always inside this query's list
-}
+// Raw code of list position idx, loaded one tile before it is decoded (the
+// load is clamped into this query's list; positions past it are rewritten by
+// final_code).
+__device__ __forceinline__ int raw_code(const RowCtx& c, int idx) { return c.loc[min(idx, c.k - 1)]; }
 
+// Positions past the list are the ring window (tier 3, index r*R_d + pos mod
+// R_d) and, past its end, masked (-1).
 __device__ __forceinline__ int final_code(const RowCtx& c, int idx, int raw) {
   int rrow = c.ring_row0 + (idx - c.k);             // consecutive positions, one wrap at most
   rrow -= rrow >= c.ring_end ? c.Rd : 0;
@@ -111,142 +117,93 @@ __device__ __forceinline__ int final_code(const RowCtx& c, int idx, int raw) {
   return idx < c.k ? raw : (idx < c.n_total ? rc : -1);
 }
 
-// Address of the row a code names; a masked code (-1) yields the hot pool
-// base, a mapped address, so the load can be issued unconditionally and its
-// value cleared when it is written to LDS.
+// Address of the row a code names; masked codes read the zero row.
 template <int ROW>
-__device__ __forceinline__ uintptr_t code_addr(const RowCtx& c, int code) {
-  constexpr size_t RB = size_t(ROW) * 2;
-  const int cc = code < 0 ? 0 : code;
-  const int tier = loc_tier(cc);
-  const size_t ix = size_t(loc_index(cc));
+__device__ __forceinline__ uintptr_t row_addr(const RowCtx& c, int code) {
+  const int tier = loc_tier(code);
   // pool offsets from the hot pool base, selected arithmetically (a select
-  // chain would become an indexed table in scratch memory)
+  // chain becomes an indexed table in scratch memory)
   const uintptr_t off = (tier == kTierStaged ? c.d_staging : uintptr_t(0)) +
                         (tier == kTierResident ? c.d_resident : uintptr_t(0)) +
                         (tier == kTierRing ? c.d_ring : uintptr_t(0));
-  return c.hot + off + ix * RB;
+  return code < 0 ? c.zero : c.hot + off + size_t(loc_index(code)) * (size_t(ROW) * 2);
 }
 
-__device__ __forceinline__ uint32_t lo16(uint32_t w) { return w & 0xffffu; }
-__device__ __forceinline__ uint32_t hi16(uint32_t w) { return w >> 16; }
-__device__ __forceinline__ uint32_t elem(const uint4& v, int e) {
-  const uint32_t w = e < 2 ? v.x : (e < 4 ? v.y : (e < 6 ? v.z : v.w));
-  return (e & 1) ? hi16(w) : lo16(w);
+// (row within the wave's rows, chunk) of gather instruction u for a lane, and
+// whether the lane's chunk is stored (the shared tail instruction may carry
+// duplicates).
+template <class C>
+__device__ __forceinline__ void task_of(int u, int lane, int& rr, int& ch, bool& st) {
+  if (C::WIDE) {
+    if (u < C::RPW) { rr = u; ch = lane; st = true; return; }
+    const int per = 64 / C::REST;                  // rows per tail instruction
+    const int x = (u - C::RPW) * per + lane / C::REST;
+    st = x < C::RPW;
+    rr = st ? x : 0;
+    ch = 64 + lane % C::REST;
+  } else {
+    const int x = u * 64 + lane;
+    rr = x / C::RCH;
+    ch = x % C::RCH;
+    st = true;
+  }
 }
 
 template <class C>
-struct Prefetch {
-  uint4 t1[C::T1PT][4];
-  uint4 t2[C::T2PT];
-  uint32_t live;     // bit per loaded chunk: the row is not masked
-  int flag;
+struct Gather {
+  uint4 v[C::NU];
 };
 
+// Issues the loads of one tile: lanes 0..31 (and their mirrors 32..63) hold
+// the codes of the tile's 32 rows; each lane decodes its row's address, and a
+// wave's instruction takes its row base from the owning lane (readlane for
+// a whole-row instruction, a lane permute otherwise).  Loads are
+// unconditional and their values are consumed one tile later, so the wave
+// never waits for them here.  Returns the tile's live-row mask.
 template <class C>
-struct Codes {
-  int t1[C::T1PT][4];
-  int t2[C::T2PT];
-  int flag;
-};
-
-template <class C>
-__device__ __forceinline__ void tile_codes(Codes<C>& cd, const RowCtx& ctx, int t0, int tid) {
+__device__ __forceinline__ uint32_t gather_issue(Gather<C>& g, const RowCtx& ctx, int code, int w, int lane) {
+  const uint32_t live = static_cast<uint32_t>(__builtin_amdgcn_ballot_w64(code >= 0));
+  const uintptr_t my = row_addr<C::ROW>(ctx, code);
+  const int mlo = static_cast<int>(static_cast<uint32_t>(my));
+  const int mhi = static_cast<int>(static_cast<uint32_t>(my >> 32));
 #pragma unroll
-  for (int a = 0; a < C::T1PT; ++a) {
-    const int task = min(tid + a * C::NT, C::T1 - 1);
-    const int g4 = task % (TILE / 4);
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) cd.t1[a][rr] = raw_code(ctx, t0 + g4 * 4 + rr);
-  }
-#pragma unroll
-  for (int b = 0; b < C::T2PT; ++b) {
-    const int task = min(tid + b * C::NT, C::T2 - 1);
-    cd.t2[b] = raw_code(ctx, t0 + task / C::NKO);
-  }
-  cd.flag = raw_code(ctx, t0 + (tid % TILE));
-}
-
-// Issues the loads of one tile: every load is unconditional and its value is
-// not consumed here, so the wave does not wait for it before the next tile's
-// store (a conditional or masked load would make the compiler wait at once).
-template <class C>
-__device__ __forceinline__ void tile_load(Prefetch<C>& pf, const Codes<C>& cd, const RowCtx& ctx, int t0,
-                                          int tid) {
-  uint32_t live = 0;
-#pragma unroll
-  for (int a = 0; a < C::T1PT; ++a) {
-    const int task = min(tid + a * C::NT, C::T1 - 1);
-    const int g4 = task % (TILE / 4), cv = task / (TILE / 4);
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int code = final_code(ctx, t0 + g4 * 4 + rr, cd.t1[a][rr]);
-      pf.t1[a][rr] = gload16(code_addr<C::ROW>(ctx, code) + size_t(C::V0 + cv) * 16);
-      live |= (code >= 0 ? 1u : 0u) << (a * 4 + rr);
+  for (int u = 0; u < C::NU; ++u) {
+    int rr, ch;
+    bool st;
+    task_of<C>(u, lane, rr, ch, st);
+    uintptr_t base;
+    if (C::WIDE && u < C::RPW) {
+      const int src = w * C::RPW + u;
+      base = (uintptr_t(uint32_t(__builtin_amdgcn_readlane(mhi, src))) << 32) |
+             uint32_t(__builtin_amdgcn_readlane(mlo, src));
+    } else {
+      const int src = w * C::RPW + rr;
+      base = (uintptr_t(uint32_t(__shfl(mhi, src, 64))) << 32) | uint32_t(__shfl(mlo, src, 64));
     }
+    g.v[u] = gload16(base + size_t(ch) * 16);
   }
-#pragma unroll
-  for (int b = 0; b < C::T2PT; ++b) {
-    const int task = min(tid + b * C::NT, C::T2 - 1);
-    const int code = final_code(ctx, t0 + task / C::NKO, cd.t2[b]);
-    pf.t2[b] = gload16(code_addr<C::ROW>(ctx, code) + size_t(C::KO0 + task % C::NKO) * 16);
-    live |= (code >= 0 ? 1u : 0u) << (C::T1PT * 4 + b);
-  }
-  pf.live = live;
-  pf.flag = final_code(ctx, t0 + (tid % TILE), cd.flag) >= 0;
-}
-
-__device__ __forceinline__ uint4 masked(const uint4& v, bool ok) {
-  return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+  return live;
 }
 
 template <class C>
-__device__ __forceinline__ void tile_store(const Prefetch<C>& pf, uint16_t* Ks, uint16_t* Vt, int* rowflag, int tid) {
+__device__ __forceinline__ void gather_store(const Gather<C>& g, uint16_t* kb, int w, int lane) {
 #pragma unroll
-  for (int a = 0; a < C::T1PT; ++a) {
-    const int task = tid + a * C::NT;
-    if (C::T1 % C::NT == 0 || task < C::T1) {
-      const int g4 = task % (TILE / 4), cv = task / (TILE / 4);
-      uint4 v[4];
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) v[rr] = masked(pf.t1[a][rr], (pf.live >> (a * 4 + rr)) & 1u);
-      if (C::V_IN_K) {
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          *reinterpret_cast<uint4*>(Ks + (g4 * 4 + rr) * C::KSTR + (C::V0 + cv) * 8) = v[rr];
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint2 pk;
-        pk.x = elem(v[0], e) | (elem(v[1], e) << 16);
-        pk.y = elem(v[2], e) | (elem(v[3], e) << 16);
-        *reinterpret_cast<uint2*>(Vt + (cv * 8 + e) * C::VSTR + g4 * 4) = pk;
-      }
-    }
-  }
-#pragma unroll
-  for (int b = 0; b < C::T2PT; ++b) {
-    const int task = tid + b * C::NT;
-    if (C::T2 % C::NT == 0 || task < C::T2) {
-      const int rr = task / C::NKO, ck = task % C::NKO;
-      *reinterpret_cast<uint4*>(Ks + rr * C::KSTR + (C::KO0 + ck) * 8) =
-          masked(pf.t2[b], (pf.live >> (C::T1PT * 4 + b)) & 1u);
-    }
-  }
-  // 32-bit mask of the tile's live rows, from the first wave's flags
-  if (tid < 64) {
-    const unsigned long long m = __builtin_amdgcn_ballot_w64(tid < TILE && pf.flag);
-    if (tid == 0) rowflag[0] = static_cast<int>(static_cast<uint32_t>(m));
+  for (int u = 0; u < C::NU; ++u) {
+    int rr, ch;
+    bool st;
+    task_of<C>(u, lane, rr, ch, st);
+    if (st) *reinterpret_cast<uint4*>(kb + (w * C::RPW + rr) * C::KSTR + ch * 8) = g.v[u];
   }
 }
 
 template <class C>
 __global__ __launch_bounds__(C::NT, 1) void attn_kernel(AttnArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
-  uint16_t* Ks = reinterpret_cast<uint16_t*>(lds);
-  uint16_t* Vt = reinterpret_cast<uint16_t*>(lds + C::LDS_K);
-  float* Sx = reinterpret_cast<float*>(lds + C::LDS_K + C::LDS_V);
-  int* rowflag = reinterpret_cast<int*>(lds + C::LDS_K + C::LDS_V + C::LDS_S);
+  uint16_t* Kb = reinterpret_cast<uint16_t*>(lds);
+  float4* Sx = reinterpret_cast<float4*>(lds + C::LDS_K);
+  uint16_t* Pb = reinterpret_cast<uint16_t*>(lds + C::LDS_K + C::LDS_S);
+  float* Mx = reinterpret_cast<float*>(lds + C::LDS_K + C::LDS_S + C::LDS_P);
+  uint8_t* flags = reinterpret_cast<uint8_t*>(lds + C::LDS_K + C::LDS_S + C::LDS_P + C::LDS_M);
 
   const int nreq = a.r1 - a.r0;
   const int per_req = a.Q * a.head_groups * a.splits;
@@ -267,11 +224,12 @@ __global__ __launch_bounds__(C::NT, 1) void attn_kernel(AttnArgs a) {
   const int head = hg * 32 * C::HB + hl;
   const size_t blk = (size_t(qi) * a.head_groups + hg) * a.splits + sp;
   const int hi_half = lane >> 5;
+  const int vq0 = dq * (C::D_V / C::NDP);             // first value dim of this wave
 
   const int p_j = a.causal[qi];
   if (p_j < 0) {  // inactive query: zero output (the combine pass does it when split)
     if (a.splits == 1 && head < a.H) {
-      uint16_t* op = a.out + (size_t(qi) * a.H + head) * C::D_V + dq * (C::D_V / C::NDP);
+      uint16_t* op = a.out + (size_t(qi) * a.H + head) * C::D_V + vq0;
       for (int d = hi_half; d < C::D_V / C::NDP / 4; d += 2)
         *reinterpret_cast<uint2*>(op + d * 4) = make_uint2(0, 0);
     }
@@ -289,13 +247,13 @@ __global__ __launch_bounds__(C::NT, 1) void attn_kernel(AttnArgs a) {
   ctx.k = a.k;
   ctx.n_total = a.k + n_ring;
   ctx.Rd = a.Rd;
-  ctx.ring_base = size_t(r) * a.Rd;
   ctx.ring_row0 = r * a.Rd + lo % a.Rd;
   ctx.ring_end = (r + 1) * a.Rd;
   ctx.hot = reinterpret_cast<uintptr_t>(a.hot);
   ctx.d_staging = reinterpret_cast<uintptr_t>(a.staging) - ctx.hot;
   ctx.d_resident = reinterpret_cast<uintptr_t>(a.resident) - ctx.hot;
   ctx.d_ring = reinterpret_cast<uintptr_t>(a.ring) - ctx.hot;
+  ctx.zero = reinterpret_cast<uintptr_t>(a.zero);
 
   const int n_tiles = (ctx.n_total + TILE - 1) / TILE;
   const int tb = int((long long)n_tiles * sp / a.splits);
@@ -320,27 +278,36 @@ __global__ __launch_bounds__(C::NT, 1) void attn_kernel(AttnArgs a) {
     for (int i = 0; i < 16; ++i) O[d][i] = 0.f;
   float m_run = kNegBig, l_run = 0.f;
   const float sl2 = a.scale_log2;
+  const int crow = lane & 31;                          // tile row whose code this lane holds
 
-  Prefetch<C> pf;
-  Codes<C> cd;
-  tile_codes<C>(cd, ctx, tb * TILE, tid);
-  tile_load<C>(pf, cd, ctx, tb * TILE, tid);
-  tile_codes<C>(cd, ctx, (tb + 1) * TILE, tid);
+  // prologue: tile tb into LDS buffer 0, tile tb+1 in flight, codes of tb+2 in flight
+  Gather<C> g;
+  int code = final_code(ctx, tb * TILE + crow, raw_code(ctx, tb * TILE + crow));
+  uint32_t live_cur = gather_issue<C>(g, ctx, code, w, lane);
+  int raw = raw_code(ctx, (tb + 1) * TILE + crow);
+  gather_store<C>(g, Kb, w, lane);
+  uint32_t live_n1 = gather_issue<C>(g, ctx, final_code(ctx, (tb + 1) * TILE + crow, raw), w, lane);
+  raw = raw_code(ctx, (tb + 2) * TILE + crow);
+  __syncthreads();
 
-  const uint16_t* ks_row = Ks + (lane & 31) * C::KSTR + dq * (C::D_QK / C::NDP) + hi_half * 8;
-  // partial scores as float4: [wave][i/4][lane] (consecutive lanes, 16 B each)
-  float4* sx_own = reinterpret_cast<float4*>(Sx) + size_t(w) * 4 * 64 + lane;
-  const float4* sx_blk = reinterpret_cast<const float4*>(Sx) + size_t(hb * C::NDP) * 4 * 64 + lane;
-  const int vdim0 = dq * (C::D_V / C::NDP) + (lane & 31);
+  // per-lane LDS offsets (elements) inside a tile buffer
+  const int k_off = (lane & 31) * C::KSTR + dq * (C::D_QK / C::NDP) + hi_half * 8;
+  int v_off;
+  {
+    const int gq = (lane >> 4) & 3, s = lane & 15, aq = s & 3;
+    const int row = (gq >> 1) * 8 + (s >> 2);
+    const int dim = C::V_OFF + vq0 + ((gq & 1) * 2 + (aq >> 1)) * (8 * C::DVB) + (aq & 1) * 4;
+    v_off = row * C::KSTR + dim;
+  }
+  float4* sx_own = Sx + size_t(w) * 4 * 64 + lane;
+  const float4* sx_red = Sx + size_t(hb * C::NDP) * 4 * 64 + dq * 64 + lane;   // + q * 256
+  uint16_t* p_own = Pb + (size_t(hb) * 32 + (lane & 31)) * C::PSTR + dq * 8 + hi_half * 4;
+  const uint16_t* p_rd = Pb + (size_t(hb) * 32 + (lane & 31)) * C::PSTR + hi_half * 8;
+  const int sbit0 = dq * 8 + hi_half * 4;              // first tile row of this lane's quarter
 
   for (int t = tb; t < te; ++t) {
-    __syncthreads();
-    tile_store<C>(pf, Ks, Vt, rowflag, tid);
-    __syncthreads();
-    // unconditional (past the range they read masked or unused, always mapped rows):
-    // a conditional prefetch would make the compiler wait for it at once
-    tile_load<C>(pf, cd, ctx, (t + 1) * TILE, tid);                    // rows of tile t+1
-    tile_codes<C>(cd, ctx, (t + 2) * TILE, tid);                       // codes of tile t+2
+    const int buf = (t - tb) & 1;
+    const uint16_t* kb = Kb + buf * C::KBUF;
 
     // partial scores over this wave's part of the key width
     f32x16 acc;
@@ -348,102 +315,146 @@ __global__ __launch_bounds__(C::NT, 1) void attn_kernel(AttnArgs a) {
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-      const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ks_row + ks * 16));
+      const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + k_off + ks * 16));
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[ks], acc, 0, 0, 0);
     }
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4)
       sx_own[i4 * 64] = make_float4(acc[4 * i4], acc[4 * i4 + 1], acc[4 * i4 + 2], acc[4 * i4 + 3]);
     __syncthreads();
-    float s[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] = 0.f;
-    // the block's partial scores summed in key-part order (identical in its waves)
-#pragma unroll
-    for (int q = 0; q < C::NDP; ++q) {
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const float4 v = sx_blk[(q * 4 + i4) * 64];   // own slice too: no divergent select
-        if (q == 0) {
-          s[4 * i4] = v.x; s[4 * i4 + 1] = v.y; s[4 * i4 + 2] = v.z; s[4 * i4 + 3] = v.w;
-        } else {
-          s[4 * i4] += v.x; s[4 * i4 + 1] += v.y; s[4 * i4 + 2] += v.z; s[4 * i4 + 3] += v.w;
-        }
-      }
+
+    // tile t+1 into the other buffer (its last reader, PV of tile t-1, is done);
+    // issue tile t+2 and the codes of tile t+3 (unconditional: positions past
+    // the range read the zero row and are never used)
+    gather_store<C>(g, Kb + (buf ^ 1) * C::KBUF, w, lane);
+    const uint32_t live_n2 = gather_issue<C>(g, ctx, final_code(ctx, (t + 2) * TILE + crow, raw), w, lane);
+    raw = raw_code(ctx, (t + 3) * TILE + crow);
+
+    // this wave's quarter of the rows: scores summed over the key parts in order
+    float s[4];
+    {
+      const float4 v0 = sx_red[0], v1 = sx_red[256], v2 = sx_red[512], v3 = sx_red[768];
+      s[0] = ((v0.x + v1.x) + v2.x) + v3.x;
+      s[1] = ((v0.y + v1.y) + v2.y) + v3.y;
+      s[2] = ((v0.z + v1.z) + v2.z) + v3.z;
+      s[3] = ((v0.w + v1.w) + v2.w) + v3.w;
     }
-    const uint32_t live = static_cast<uint32_t>(rowflag[0]);
+    const uint32_t lb = live_cur >> sbit0;
+    bool over = false;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = (i >> 2) * 8 + hi_half * 4 + (i & 3);
-      s[i] = (live >> row) & 1u ? s[i] * sl2 : -INFINITY;
+    for (int i = 0; i < 4; ++i) {
+      s[i] = (lb >> i) & 1u ? s[i] * sl2 : -INFINITY;
+      over |= s[i] > m_run + kRescaleLog2;
     }
-    // online softmax for head lane%32; the other 16 rows sit in lane ^ 32
-    float mt = s[0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[i]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const bool grow = mt > m_run + kRescaleLog2;
-    if (__builtin_amdgcn_ballot_w64(grow)) {   // wave-uniform: some head's max moved far
-      const float m_new = grow ? mt : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-      m_run = m_new;
-#pragma unroll
-      for (int d = 0; d < C::DVB; ++d)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) O[d][i] *= alpha;
-    }
+    float p[4];
     float ps = 0.f;
-    bf16x8 pb0, pb1;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float p = __builtin_amdgcn_exp2f(s[i] - m_run);
-      ps += p;
-      if (i < 8) pb0[i] = static_cast<__bf16>(p);
-      else pb1[i - 8] = static_cast<__bf16>(p);
+    for (int i = 0; i < 4; ++i) {
+      p[i] = __builtin_amdgcn_exp2f(s[i] - m_run);
+      ps += p[i];
+    }
+    {
+      uint2 pk;
+      pk.x = uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(p[0]))) |
+             (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(p[1]))) << 16);
+      pk.y = uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(p[2]))) |
+             (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(p[3]))) << 16);
+      *reinterpret_cast<uint2*>(p_own) = pk;
+    }
+    const bool any_over = __builtin_amdgcn_ballot_w64(over) != 0;
+    if (lane == 0) flags[w] = any_over ? 1 : 0;
+    __syncthreads();
+
+    const bool slow = C::NW == 8 ? *reinterpret_cast<const uint64_t*>(flags) != 0
+                                 : *reinterpret_cast<const uint32_t*>(flags) != 0;
+    if (slow) {
+      // some score of some head exceeds its running max by more than 2^8:
+      // exchange the tile max, raise the max where needed, redo this tile's p
+      float mq = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+      mq = fmaxf(mq, __shfl_xor(mq, 32, 64));
+      if (lane < 32) Mx[w * 32 + lane] = mq;
+      __syncthreads();
+      float mt = Mx[(hb * C::NDP) * 32 + (lane & 31)];
+#pragma unroll
+      for (int q = 1; q < C::NDP; ++q) mt = fmaxf(mt, Mx[(hb * C::NDP + q) * 32 + (lane & 31)]);
+      if (mt > m_run + kRescaleLog2) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run - mt);
+        l_run *= alpha;
+        m_run = mt;
+#pragma unroll
+        for (int d = 0; d < C::DVB; ++d)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) O[d][i] *= alpha;
+      }
+      ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(s[i] - m_run);
+        ps += p[i];
+      }
+      uint2 pk;
+      pk.x = uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(p[0]))) |
+             (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(p[1]))) << 16);
+      pk.y = uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(p[2]))) |
+             (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(p[3]))) << 16);
+      *reinterpret_cast<uint2*>(p_own) = pk;
+      __syncthreads();
     }
     l_run += ps;
+
     // O^T += V^T P^T over the tile's 32 rows (two 16-row k-steps)
 #pragma unroll
-    for (int d = 0; d < C::DVB; ++d) {
-      const uint16_t* vrow = Vt + (vdim0 + d * 32) * C::VSTR + hi_half * 4;
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p_rd + ks2 * 16));
 #pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) {
-        const uint2 x0 = *reinterpret_cast<const uint2*>(vrow + ks2 * 16);
-        const uint2 x1 = *reinterpret_cast<const uint2*>(vrow + ks2 * 16 + 8);
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(x0.x, x0.y, x1.x, x1.y));
-        O[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, ks2 == 0 ? pb0 : pb1, O[d], 0, 0, 0);
+      for (int d = 0; d < C::DVB; ++d) {
+        const uint16_t* vp = kb + v_off + ks2 * 16 * C::KSTR + d * 8;
+        const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp));
+        const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 4 * C::KSTR));
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+        O[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, O[d], 0, 0, 0);
       }
     }
+    live_cur = live_n1;
+    live_n1 = live_n2;
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  // normaliser: this wave's rows, both lane halves, then the four quarters in order
+  float l2 = l_run + __shfl_xor(l_run, 32, 64);
+  __syncthreads();
+  if (lane < 32) Mx[w * 32 + lane] = l2;
+  __syncthreads();
+  float l_tot = Mx[(hb * C::NDP) * 32 + (lane & 31)];
+#pragma unroll
+  for (int q = 1; q < C::NDP; ++q) l_tot += Mx[(hb * C::NDP + q) * 32 + (lane & 31)];
+
+  // O^T register i of block d holds value dim vq0 + (i/4)*8*DVB + d*8 + hi*4 + i%4
   if (a.splits == 1) {
     if (head < a.H) {
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      uint16_t* op = a.out + (size_t(qi) * a.H + head) * C::D_V + dq * (C::D_V / C::NDP) + hi_half * 4;
+      uint16_t* op = a.out + (size_t(qi) * a.H + head) * C::D_V + vq0 + hi_half * 4;
 #pragma unroll
       for (int d = 0; d < C::DVB; ++d)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
+        for (int g4 = 0; g4 < 4; ++g4) {
           uint16_t h4[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            h4[e] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(O[d][g * 4 + e] * inv));
+            h4[e] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(O[d][g4 * 4 + e] * inv));
           uint2 pk;
           pk.x = uint32_t(h4[0]) | (uint32_t(h4[1]) << 16);
           pk.y = uint32_t(h4[2]) | (uint32_t(h4[3]) << 16);
-          *reinterpret_cast<uint2*>(op + d * 32 + g * 8) = pk;
+          *reinterpret_cast<uint2*>(op + g4 * 8 * C::DVB + d * 8) = pk;
         }
     }
   } else {
-    float* po = a.part_o + (blk * 32 * C::HB + hl) * C::D_V + dq * (C::D_V / C::NDP) + hi_half * 4;
+    float* po = a.part_o + (blk * 32 * C::HB + hl) * C::D_V + vq0 + hi_half * 4;
 #pragma unroll
     for (int d = 0; d < C::DVB; ++d)
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<float4*>(po + d * 32 + g * 8) =
-            make_float4(O[d][g * 4 + 0], O[d][g * 4 + 1], O[d][g * 4 + 2], O[d][g * 4 + 3]);
+      for (int g4 = 0; g4 < 4; ++g4)
+        *reinterpret_cast<float4*>(po + g4 * 8 * C::DVB + d * 8) =
+            make_float4(O[d][g4 * 4 + 0], O[d][g4 * 4 + 1], O[d][g4 * 4 + 2], O[d][g4 * 4 + 3]);
     if (dq == 0 && hi_half == 0) {
       float* pm = a.part_ml + (blk * 32 * C::HB + hl) * 2;
       pm[0] = m_run;

@@ -91,6 +91,7 @@ struct AttnArgs {
   const uint16_t* staging;    // arena of the group
   const uint16_t* resident;   // resident pool (may be null)
   const uint16_t* ring;       // ring of the group
+  const uint16_t* zero;       // one all-zero row (masked positions read it)
   uint16_t* out;              // [N][Q][H][d_v]
   float* part_o;              // [N*Q*HG*S][32*HB][d_v] partial numerators (splits > 1)
   float* part_ml;             // [N*Q*HG*S][32*HB][2]

@@ -70,6 +70,7 @@ struct kv_hier {
   std::vector<Group> grp;
   std::vector<uint16_t*> arena;
   float* part_o = nullptr;
+  uint16_t* zero_row = nullptr;   // one all-zero row: target of masked attention reads
   float* part_ml = nullptr;
   int splits = 1, head_groups = 1, n_chunks = 1;
   std::vector<int> chunk_lo;
@@ -301,6 +302,7 @@ void free_all(kv_hier* h) {
   }
   for (uint16_t* a : h->arena) (void)hipFree(a);
   (void)hipFree(h->part_o);
+  (void)hipFree(h->zero_row);
   (void)hipFree(h->part_ml);
   (void)hipFree(h->d_commit);
   (void)hipFree(h->d_commit_groups);
@@ -472,6 +474,9 @@ static int create_impl(kv_hier* h) {
   h->arena.assign(c.n_arenas, nullptr);
   for (int a = 0; a < c.n_arenas; ++a)
     if ((rc = dev_alloc(h, &h->arena[a], size_t(N) * h->QK * c.row_elems, &h->bytes_staging))) return rc;
+  if ((rc = dev_alloc(h, &h->zero_row, size_t(c.row_elems), &h->bytes_maps))) return rc;
+  if (launch_fill32(reinterpret_cast<uint32_t*>(h->zero_row), 0, size_t(c.row_elems) / 2, nullptr) != hipSuccess)
+    return fail(h, KV_EHIP, "zero row fill failed");
   {
     std::vector<CommitGroup> cg(c.n_groups);
     for (int g = 0; g < c.n_groups; ++g) {
@@ -779,6 +784,7 @@ int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t*
   at.staging = h->arena[a];
   at.resident = G.resident;
   at.ring = G.ring;
+  at.zero = h->zero_row;
   at.out = static_cast<uint16_t*>(out);
   at.part_o = h->part_o;
   at.part_ml = h->part_ml;
