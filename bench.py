@@ -43,6 +43,7 @@ def parse():
     ap.add_argument("--rho", type=float, default=0.0, help="static resident fraction of rows")
     ap.add_argument("--n-chunks", type=int, default=0)
     ap.add_argument("--fetch-cus", type=int, default=0, help="CUs reserved for the host fetch")
+    ap.add_argument("--fetch-wgs", type=int, default=0, help="workgroups per chunk of the host fetch (0 = library default)")
     ap.add_argument("--retained", action="store_true", help="keep the cache state between steps")
     ap.add_argument("--timing-steps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -77,7 +78,7 @@ def main():
     hists = [make_history(w, g, hl) for g in range(w.n_groups)]
     log("bench: host rows ready (%.1fs); creating the library state" % (time.perf_counter() - t_setup))
     pair = build_pair(w, rho=args.rho, with_oracle=False, histories=hists,
-                      lib_kw=dict(n_chunks=args.n_chunks, fetch_cus=args.fetch_cus))
+                      lib_kw=dict(n_chunks=args.n_chunks, fetch_cus=args.fetch_cus, fetch_wgs=args.fetch_wgs))
     lib = pair.lib
     G = w.n_groups
     sis = [make_step_inputs(w, g, 0, hl) for g in range(G)]
@@ -206,7 +207,7 @@ def main():
                    "heads": w.n_heads, "row_bytes": row_bytes, "history_rows": [int(hl.min()), int(hl.max())],
                    "resident_fraction": args.rho, "cache_state": "retained" if args.retained else "restored",
                    "n_chunks": lib.info["n_chunks"], "attn_splits": lib.info["attn_splits"],
-                   "fetch_cus": args.fetch_cus},
+                   "fetch_cus": args.fetch_cus, "fetch_wgs": args.fetch_wgs},
         "selected_rows_per_s": round(sel_per_step / (ms / 1000.0), 1),
         "unique_rows_per_s": round(union_per_step / (ms / 1000.0), 1),
         "fetched_rows_per_step": miss_per_step,

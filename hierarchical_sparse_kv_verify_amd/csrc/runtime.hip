@@ -5,9 +5,14 @@
 // backing, plus chi staging arenas shared by all groups ("Adaptive
 // DHiSparse", §3.4: arenas are reused across layer groups once readers and
 // copy-back finish).  A step enqueues, on the caller's stream: ring write,
-// resolution plan, then per request chunk the attention and the copy-back;
-// the host fetch of each chunk runs on a side stream and is ordered with
-// events, so the fetch of chunk c+1 overlaps the attention of chunk c.
+// resolution plan, then per request chunk the attention; the host fetch of
+// each chunk runs on a side stream and the copy-back (promotion) of the
+// chunk on a third stream right after its fetch (promoted rows go to victim
+// slots, which no list of the step names, so the copy-back need not wait for
+// the attention).  Events order the three, so the fetch of chunk c+1 overlaps
+// the attention of chunk c; an arena is released once both the attention and
+// the copy-back of a chunk are done, and the caller's stream waits for the
+// last copy-back before the step returns control of the group.
 // No host synchronisation happens inside a step.
 #include <algorithm>
 #include <cmath>
@@ -78,6 +83,9 @@ struct kv_hier {
   size_t plan_lds = 0;
   hipStream_t side = nullptr;       // host fetch
   hipStream_t work = nullptr;       // the rest of the step when CUs are partitioned (else null)
+  hipStream_t aux = nullptr;        // copy-back of promoted rows
+  std::vector<hipEvent_t> ev_attn;  // per chunk: attention done
+  hipEvent_t ev_aux = nullptr;      // end of a step's copy-backs
   hipEvent_t ev_plan = nullptr;
   hipEvent_t ev_in = nullptr, ev_out = nullptr;
   std::vector<hipEvent_t> ev_fetched;
@@ -316,7 +324,10 @@ void free_all(kv_hier* h) {
   if (h->ev_commit) (void)hipEventDestroy(h->ev_commit);
   for (hipEvent_t e : h->ev_fetched) (void)hipEventDestroy(e);
   for (auto& v : h->ev_free) for (hipEvent_t e : v) (void)hipEventDestroy(e);
+  for (hipEvent_t e : h->ev_attn) (void)hipEventDestroy(e);
+  if (h->ev_aux) (void)hipEventDestroy(h->ev_aux);
   if (h->side) (void)hipStreamDestroy(h->side);
+  if (h->aux) (void)hipStreamDestroy(h->aux);
 }
 
 // Ring size of "Adaptive DHiSparse" §3.4 eq. (9): page-rounded window plus block.
@@ -326,7 +337,7 @@ int validate(kv_hier* h, const kv_hier_config& c) {
   if (c.n_req <= 0 || c.n_groups <= 0 || c.n_arenas <= 0 || c.hist_cap <= 0 || c.row_elems <= 0 ||
       c.d_qk <= 0 || c.d_v <= 0 || c.v_off < 0 || c.n_heads <= 0 || c.q_max <= 0 || c.topk <= 0 ||
       c.hot_slots <= 0 || c.ring_window <= 0 || c.ring_page <= 0 || c.n_prefix < 0 || c.prefix_len < 0 ||
-      c.n_chunks < 0 || c.resident_cap < 0)
+      c.n_chunks < 0 || c.resident_cap < 0 || c.fetch_cus < 0 || c.fetch_wgs < 0)
     return fail(h, KV_EINVAL, "non-positive size in config");
   if (c.q_max > 32) return fail(h, KV_EUNSUPPORTED, "q_max %d > 32", c.q_max);
   if (int64_t(c.q_max) * c.topk > 65535) return fail(h, KV_EUNSUPPORTED, "q_max*topk > 65535");
@@ -511,6 +522,10 @@ static int create_impl(kv_hier* h) {
   } else {
     HIPCHK(h, hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking));
   }
+  HIPCHK(h, hipStreamCreateWithFlags(&h->aux, hipStreamNonBlocking));
+  HIPCHK(h, hipEventCreateWithFlags(&h->ev_aux, hipEventDisableTiming));
+  h->ev_attn.assign(h->n_chunks, nullptr);
+  for (auto& e : h->ev_attn) HIPCHK(h, hipEventCreateWithFlags(&e, hipEventDisableTiming));
   HIPCHK(h, hipEventCreateWithFlags(&h->ev_plan, hipEventDisableTiming));
   HIPCHK(h, hipEventCreateWithFlags(&h->ev_in, hipEventDisableTiming));
   HIPCHK(h, hipEventCreateWithFlags(&h->ev_out, hipEventDisableTiming));
@@ -767,7 +782,10 @@ int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t*
   for (int ch = 0; ch < h->n_chunks; ++ch) {
     const int r0 = h->chunk_lo[ch], r1 = h->chunk_lo[ch + 1];
     if (h->free_recorded[a][ch]) HIPCHK(h, hipStreamWaitEvent(h->side, h->ev_free[a][ch], 0));
-    const int wpr = std::max(1, 128 / std::max(1, r1 - r0));
+    // few workgroups: enough host reads in flight to fill the link; more only
+    // queue in the memory system and slow the attention running beside them
+    const int wgs = c.fetch_wgs > 0 ? c.fetch_wgs : 32;
+    const int wpr = std::max(1, wgs / std::max(1, r1 - r0));
     ti = time_begin(h, K_GATHER, g, h->side);
     HIPCHK(h, launch_miss_gather(src, G.miss_rows, G.req_info, reinterpret_cast<uint4*>(h->arena[a]), h->QK, r0, r1,
                                  wpr, h->side));
@@ -811,18 +829,25 @@ int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t*
       HIPCHK(h, launch_attn_combine(at, c.d_v, s));
       time_end(h, ti, s);
     }
-    ti = time_begin(h, K_PROMOTE, g, s);
+    // copy-back on the aux stream: after the chunk's fetch, concurrent with its attention
+    HIPCHK(h, hipEventRecord(h->ev_attn[ch], s));
+    HIPCHK(h, hipStreamWaitEvent(h->aux, h->ev_fetched[ch], 0));
+    ti = time_begin(h, K_PROMOTE, g, h->aux);
     HIPCHK(h, launch_promote(reinterpret_cast<const uint4*>(h->arena[a]), G.victims, G.req_info,
-                             reinterpret_cast<uint4*>(G.hot), h->QK, c.hot_slots, h->row16, at.r0, at.r1, s));
-    time_end(h, ti, s);
+                             reinterpret_cast<uint4*>(G.hot), h->QK, c.hot_slots, h->row16, at.r0, at.r1, h->aux));
+    time_end(h, ti, h->aux);
+    HIPCHK(h, hipStreamWaitEvent(h->aux, h->ev_attn[ch], 0));
     if (c.flags & KV_FLAG_POISON) {
       const size_t words = size_t(at.r1 - at.r0) * h->QK * c.row_elems / 2;
       HIPCHK(h, launch_fill32(reinterpret_cast<uint32_t*>(h->arena[a] + size_t(at.r0) * h->QK * c.row_elems),
-                              0x7fc07fc0u, words, s));
+                              0x7fc07fc0u, words, h->aux));
     }
-    HIPCHK(h, hipEventRecord(h->ev_free[a][ch], s));
+    HIPCHK(h, hipEventRecord(h->ev_free[a][ch], h->aux));
     h->free_recorded[a][ch] = 1;
   }
+  // the group's hot cache is complete only after its copy-backs
+  HIPCHK(h, hipEventRecord(h->ev_aux, h->aux));
+  HIPCHK(h, hipStreamWaitEvent(s, h->ev_aux, 0));
   if (h->work) {
     HIPCHK(h, hipEventRecord(h->ev_out, s));
     HIPCHK(h, hipStreamWaitEvent(caller, h->ev_out, 0));
