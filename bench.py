@@ -159,6 +159,7 @@ def main():
     ms_gather = tot("ms_gather")
     ms_plan = tot("ms_plan")
     ms_promote = tot("ms_promote")
+    ms_victims = tot("ms_victims")
     n_launch = lambda key: max(1, int(sum(int(t[key]) for t in tim)))
     promote_bytes = 2 * sum(int(t["promoted"]) for t in tim) * row_bytes
     plan_bytes = (sum(int(t["active_queries"]) for t in tim) * w.topk * 4 * 3 +
@@ -180,7 +181,8 @@ def main():
     }
     rooflines["miss_gather"]["frac_of_measured_h2d"] = round(
         rooflines["miss_gather"]["achieved"] / 57.3, 4)
-    kernel_ms = {"miss_gather": ms_gather, "sparse_attn": ms_attn, "plan": ms_plan, "promote": ms_promote}
+    kernel_ms = {"miss_gather": ms_gather, "sparse_attn": ms_attn, "plan": ms_plan, "plan_victims": ms_victims,
+                 "promote": ms_promote}
     dominant = max(kernel_ms, key=kernel_ms.get)
     roofline = dict(rooflines[dominant])
     roofline["kernel"] = dominant

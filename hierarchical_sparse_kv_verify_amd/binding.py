@@ -53,8 +53,8 @@ class Config(ctypes.Structure):
 COUNTER_FIELDS = ("calls", "active_requests", "active_queries", "selections", "pads", "invalid",
                   "union_rows", "union_resident", "union_hot", "union_miss", "fetched_bytes",
                   "promoted", "overflow", "sel_resident", "sel_hot", "sel_miss")
-TIMING_FIELDS = ("ms_ring", "ms_plan", "ms_gather", "ms_attn", "ms_combine", "ms_promote")
-TIMING_COUNTS = ("n_ring", "n_plan", "n_gather", "n_attn", "n_combine", "n_promote")
+TIMING_FIELDS = ("ms_ring", "ms_plan", "ms_gather", "ms_attn", "ms_combine", "ms_promote", "ms_victims")
+TIMING_COUNTS = ("n_ring", "n_plan", "n_gather", "n_attn", "n_combine", "n_promote", "n_victims")
 
 
 class Counters(ctypes.Structure):

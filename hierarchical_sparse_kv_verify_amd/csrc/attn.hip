@@ -222,7 +222,7 @@ __global__ __launch_bounds__(C::NT, 1) void attn_kernel(AttnArgs a) {
   const int hb = w / C::NDP, dq = w % C::NDP;
   const int hl = hb * 32 + (lane & 31);               // head within the workgroup
   const int head = hg * 32 * C::HB + hl;
-  const size_t blk = (size_t(qi) * a.head_groups + hg) * a.splits + sp;
+  const size_t blk = (size_t(qi - a.r0 * a.Q) * a.head_groups + hg) * a.splits + sp;   // from the chunk's start
   const int hi_half = lane >> 5;
   const int vq0 = dq * (C::D_V / C::NDP);             // first value dim of this wave
 
@@ -479,7 +479,7 @@ __global__ __launch_bounds__(128) void combine_kernel(AttnArgs a) {
     for (int d = threadIdx.x; d < D_V; d += blockDim.x) op[d] = 0;
     return;
   }
-  const size_t blk0 = (size_t(qi) * a.head_groups + hg) * a.splits;
+  const size_t blk0 = (size_t(qi - a.r0 * a.Q) * a.head_groups + hg) * a.splits;
   float m = kNegBig;
   for (int s = 0; s < a.splits; ++s) m = fmaxf(m, a.part_ml[((blk0 + s) * HPW + hl) * 2]);
   float wsum[8];

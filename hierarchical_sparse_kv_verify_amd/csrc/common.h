@@ -38,16 +38,21 @@ struct PlanArgs {
   int32_t* union_loc;        // [N][Q*k]
   int32_t* miss_rows;        // [N][Q*k]
   int32_t* victims;          // [N][Q*k]
+  uint32_t* protect;         // [N][ceil(B/32)] slots holding a selected row (resolve -> victims)
   int32_t* loc;              // [N][Q][k]
   int32_t* req_info;         // [N][I_NUM]
   int64_t* req_counts;       // [N][C_NUM] last step
   unsigned long long* cum;   // [C_NUM] cumulative
   int N, Q, k, B, L, t;
+  int has_resident;          // 0: the resident map holds no row (its lookups are skipped)
   int chunk_words;           // bitmap words per row chunk (rows per chunk = 32 * chunk_words)
   int sort_cap;              // power of two >= B
 };
 size_t plan_lds_bytes(int Q, int k, int B, int chunk_words, int sort_cap);
+// union, probe, staging positions, locations (everything the fetch needs)
 hipError_t launch_plan(const PlanArgs& a, size_t lds, hipStream_t s);
+// LRU victims, promotions and slot-table updates (after launch_plan)
+hipError_t launch_plan_victims(const PlanArgs& a, size_t lds, hipStream_t s);
 
 // ---------------------------------------------------------------- copies
 struct HostRowSrc {
@@ -93,8 +98,8 @@ struct AttnArgs {
   const uint16_t* ring;       // ring of the group
   const uint16_t* zero;       // one all-zero row (masked positions read it)
   uint16_t* out;              // [N][Q][H][d_v]
-  float* part_o;              // [N*Q*HG*S][32*HB][d_v] partial numerators (splits > 1)
-  float* part_ml;             // [N*Q*HG*S][32*HB][2]
+  float* part_o;              // [(chunk requests)*Q*HG*S][32*HB][d_v] partial numerators (splits > 1)
+  float* part_ml;             // [(chunk requests)*Q*HG*S][32*HB][2]
   int N, Q, k, H, W, Rd, block_only;
   int r0, r1;                 // request range of this launch
   int splits, head_groups;

@@ -1,4 +1,5 @@
-// Resolution plan of one verification step, one 1024-thread workgroup per request.
+// Resolution plan of one verification step, one 1024-thread workgroup per
+// request in each of its two kernels.
 //
 // "Adaptive DHiSparse" (arXiv 2610.13708):
 //  - §3.3 eq. (6): the retrieval union U_r of the K_r queries' selections and
@@ -16,8 +17,10 @@
 // prefix sum) yields U_r already in ascending order together with a per-word
 // prefix table, so the rank of any row in U_r is a prefix lookup plus one
 // popcount.  Histories longer than a chunk are processed chunk by chunk.
-// LRU victims: the unselected slots' (last_used, slot) keys are compacted in
-// LDS and bitonic-sorted; keys are unique, so the order is deterministic.
+// LRU victims run in a second kernel, off the path to the host fetch (the
+// fetch needs only the missing rows): the unselected slots' (last_used, slot)
+// keys are compacted in LDS and bitonic-sorted; keys are unique, so the order
+// is deterministic.
 #include "common.h"
 
 namespace kvh {
@@ -26,13 +29,12 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kMissMark = -2;
+constexpr int kBatch = 16;         // independent loads issued together
 
 __host__ __device__ inline size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
 
-__host__ __device__ inline size_t region_a_bytes(int QK, int cw, int sort_cap) {
-  size_t chunk = align16(size_t(cw) * 4) + align16(size_t(cw) * 2) + align16(size_t(QK) * 4);
-  size_t sort = size_t(sort_cap) * 8;
-  return align16(chunk > sort ? chunk : sort);
+__host__ __device__ inline size_t region_a_bytes(int QK, int cw) {
+  return align16(size_t(cw) * 4) + align16(size_t(cw) * 2) + align16(size_t(QK) * 4);
 }
 
 // Exclusive scan over the block of one int per thread; *total gets the sum.
@@ -64,7 +66,13 @@ __device__ int block_exclusive_scan(int v, int* scratch, int* total) {
   return res;
 }
 
-__global__ __launch_bounds__(kThreads) void plan_kernel(PlanArgs a) {
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) v += __shfl_xor(v, d, 64);
+  return v;
+}
+
+__global__ __launch_bounds__(kThreads) void plan_resolve_kernel(PlanArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
@@ -74,13 +82,11 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanArgs a) {
   uint32_t* bitmap = reinterpret_cast<uint32_t*>(lds);
   uint16_t* wpre = reinterpret_cast<uint16_t*>(lds + align16(size_t(CW) * 4));
   int32_t* uloc = reinterpret_cast<int32_t*>(lds + align16(size_t(CW) * 4) + align16(size_t(CW) * 2));
-  unsigned long long* keys = reinterpret_cast<unsigned long long*>(lds);
-  const size_t ra = region_a_bytes(QK, CW, a.sort_cap);
+  const size_t ra = region_a_bytes(QK, CW);
   const int pwords = (B + 31) / 32;
   uint32_t* protect = reinterpret_cast<uint32_t*>(lds + ra);
   int* scratch = reinterpret_cast<int*>(lds + ra + align16(size_t(pwords) * 4));
   int* cnt = scratch + 32;          // C_NUM counters
-  int* misc = cnt + 32;             // misc[0] = number of unprotected slots
 
   const int32_t* cp = a.causal + size_t(r) * Q;
   const int32_t* tk = a.topk + size_t(r) * QK;
@@ -88,7 +94,7 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanArgs a) {
   const int n_raw = cp[0];
   if (n_raw < 0) {  // inactive request: no selections, nothing resolved
     for (int i = tid; i < QK; i += kThreads) loc[i] = -1;
-    if (tid < I_NUM) a.req_info[r * I_NUM + tid] = 0;
+    if (tid < I_NUM && tid != I_NPROMOTE) a.req_info[r * I_NUM + tid] = 0;   // the victim kernel sets I_NPROMOTE
     if (tid < C_NUM) a.req_counts[size_t(r) * C_NUM + tid] = 0;
     return;
   }
@@ -98,7 +104,6 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanArgs a) {
 
   for (int w = tid; w < pwords; w += kThreads) protect[w] = 0;
   if (tid < 32) cnt[tid] = 0;
-  if (tid == 0) misc[0] = 0;
 
   int c_sel = 0, c_pad = 0, c_bad = 0, c_sres = 0, c_shot = 0, c_smiss = 0;
   int c_ures = 0, c_uhot = 0, c_umiss = 0;
@@ -109,18 +114,29 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanArgs a) {
     const int c1 = min(c0 + CB, n_r);
     for (int w = tid; w < CW; w += kThreads) bitmap[w] = 0;
     __syncthreads();
-    // mark the selections of this row chunk
-    for (int i = tid; i < QK; i += kThreads) {
-      if (!((amask >> (i / k)) & 1u)) continue;
-      const int e = tk[i];
-      if (c0 == 0) {
-        if (e == -1) ++c_pad;
-        else if (e >= 0 && e < n_r) ++c_sel;
-        else ++c_bad;
+    // mark the selections of this row chunk (loads issued kBatch at a time)
+    for (int i0 = tid; i0 < QK; i0 += kBatch * kThreads) {
+      int ev[kBatch];
+      bool on[kBatch];
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const int i = i0 + b * kThreads;
+        on[b] = i < QK && ((amask >> (i / k)) & 1u);
+        ev[b] = on[b] ? tk[i] : -1;
       }
-      if (e >= c0 && e < c1) {
-        const int o = e - c0;
-        atomicOr(&bitmap[o >> 5], 1u << (o & 31));
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        if (!on[b]) continue;                    // past the list or an inactive query
+        const int e = ev[b];
+        if (c0 == 0) {
+          if (e == -1) ++c_pad;
+          else if (e >= 0 && e < n_r) ++c_sel;
+          else ++c_bad;
+        }
+        if (e >= c0 && e < c1) {
+          const int o = e - c0;
+          atomicOr(&bitmap[o >> 5], 1u << (o & 31));
+        }
       }
     }
     __syncthreads();
@@ -130,18 +146,38 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanArgs a) {
     for (int w = wb; w < we; ++w) mine += __popc(bitmap[w]);
     int chunk_union;
     const int ubase = block_exclusive_scan(mine, scratch, &chunk_union);
-    // union rows in ascending order; probe resident map, then hot cache
-    int run = ubase, my_miss = 0;
+    // union rows of the chunk in ascending order, with the per-word rank table
+    int run = ubase;
     for (int w = wb; w < we; ++w) {
       wpre[w] = static_cast<uint16_t>(run);
       uint32_t bits = bitmap[w];
       while (bits) {
         const int b = __ffs(bits) - 1;
         bits &= bits - 1;
-        const int u = c0 + w * 32 + b;
-        a.union_rows[size_t(r) * QK + union_base + run] = u;
-        const int rm = a.res_map[size_t(r) * L + u];
-        const int sm = a.slot_map[size_t(r) * L + u];
+        a.union_rows[size_t(r) * QK + union_base + run] = c0 + w * 32 + b;
+        ++run;
+      }
+    }
+    __syncthreads();
+    // probe every union row (strided, so each thread's map loads are
+    // independent): resident map first, then the hot cache (Figure 2)
+    for (int x0 = tid; x0 < chunk_union; x0 += kBatch * kThreads) {
+      int uv[kBatch], rmv[kBatch], smv[kBatch];
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const int x = x0 + b * kThreads;
+        uv[b] = x < chunk_union ? a.union_rows[size_t(r) * QK + union_base + x] : -1;
+      }
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        rmv[b] = a.has_resident && uv[b] >= 0 ? a.res_map[size_t(r) * L + uv[b]] : -1;
+        smv[b] = uv[b] >= 0 ? a.slot_map[size_t(r) * L + uv[b]] : -1;
+      }
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const int x = x0 + b * kThreads;
+        if (x >= chunk_union) continue;
+        const int rm = rmv[b], sm = smv[b];
         if (sm >= 0) atomicOr(&protect[sm >> 5], 1u << (sm & 31));
         int code;
         if (rm >= 0) {
@@ -153,18 +189,21 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanArgs a) {
           ++c_uhot;
         } else {
           code = kMissMark;
-          ++my_miss;
           ++c_umiss;
         }
-        uloc[run] = code;
-        ++run;
+        uloc[x] = code;
       }
     }
+    __syncthreads();
+    // staging positions: misses in ascending row order (contiguous ranges of the union)
+    const int upt = (chunk_union + kThreads - 1) / kThreads;
+    const int xb = min(tid * upt, chunk_union), xe = min(xb + upt, chunk_union);
+    int my_miss = 0;
+    for (int x = xb; x < xe; ++x) my_miss += uloc[x] == kMissMark;
     int chunk_miss;
     const int mbase = block_exclusive_scan(my_miss, scratch, &chunk_miss);
-    // staging positions: misses in ascending row order
     int mi = miss_base + mbase;
-    for (int x = ubase; x < ubase + mine; ++x) {
+    for (int x = xb; x < xe; ++x) {
       int code = uloc[x];
       if (code == kMissMark) {
         a.miss_rows[size_t(r) * QK + mi] = a.union_rows[size_t(r) * QK + union_base + x];
@@ -176,20 +215,28 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanArgs a) {
     }
     __syncthreads();
     // one location per list entry, in selection order (eq. 12)
-    for (int i = tid; i < QK; i += kThreads) {
-      const bool act = (amask >> (i / k)) & 1u;
-      const int e = tk[i];
-      const bool valid = act && e >= 0 && e < n_r;
-      if (c0 == 0 && !valid) loc[i] = -1;
-      if (valid && e >= c0 && e < c1) {
-        const int o = e - c0, w = o >> 5, b = o & 31;
-        const int rank = wpre[w] + __popc(bitmap[w] & ((1u << b) - 1u));
-        const int code = uloc[rank];
-        loc[i] = code;
-        const int tier = loc_tier(code);
-        c_sres += tier == kTierResident;
-        c_shot += tier == kTierHot;
-        c_smiss += tier == kTierStaged;
+    for (int i0 = tid; i0 < QK; i0 += kBatch * kThreads) {
+      int ev[kBatch];
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) ev[q] = i0 + q * kThreads < QK ? tk[i0 + q * kThreads] : -1;
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) {
+        const int i = i0 + q * kThreads;
+        if (i >= QK) continue;
+        const bool act = (amask >> (i / k)) & 1u;
+        const int e = ev[q];
+        const bool valid = act && e >= 0 && e < n_r;
+        if (c0 == 0 && !valid) loc[i] = -1;
+        if (valid && e >= c0 && e < c1) {
+          const int o = e - c0, w = o >> 5, b = o & 31;
+          const int rank = wpre[w] + __popc(bitmap[w] & ((1u << b) - 1u));
+          const int code = uloc[rank];
+          loc[i] = code;
+          const int tier = loc_tier(code);
+          c_sres += tier == kTierResident;
+          c_shot += tier == kTierHot;
+          c_smiss += tier == kTierStaged;
+        }
       }
     }
     union_base += chunk_union;
@@ -206,76 +253,125 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanArgs a) {
     }
   }
 
-  // block totals of the per-thread counters
-  if (c_sel) atomicAdd(&cnt[C_SEL], c_sel);
-  if (c_pad) atomicAdd(&cnt[C_PAD], c_pad);
-  if (c_bad) atomicAdd(&cnt[C_INVALID], c_bad);
-  if (c_sres) atomicAdd(&cnt[C_S_RES], c_sres);
-  if (c_shot) atomicAdd(&cnt[C_S_HOT], c_shot);
-  if (c_smiss) atomicAdd(&cnt[C_S_MISS], c_smiss);
-  if (c_ures) atomicAdd(&cnt[C_U_RES], c_ures);
-  if (c_uhot) atomicAdd(&cnt[C_U_HOT], c_uhot);
-  if (c_umiss) atomicAdd(&cnt[C_U_MISS], c_umiss);
+  // block totals of the per-thread counters: wave sums, one LDS atomic per wave
+  {
+    const int v[9] = {c_sel, c_pad, c_bad, c_sres, c_shot, c_smiss, c_ures, c_uhot, c_umiss};
+    const int slot[9] = {C_SEL, C_PAD, C_INVALID, C_S_RES, C_S_HOT, C_S_MISS, C_U_RES, C_U_HOT, C_U_MISS};
+#pragma unroll
+    for (int q = 0; q < 9; ++q) {
+      const int tot = wave_sum(v[q]);
+      if ((tid & 63) == 0 && tot) atomicAdd(&cnt[slot[q]], tot);
+    }
+  }
 
-  // LRU victims among unselected slots, ordered by (last_used, slot), empty slots first
-  for (int s = tid; s < B; s += kThreads) {
-    if ((protect[s >> 5] >> (s & 31)) & 1u) continue;
-    const int row = a.slot_row[size_t(r) * B + s];
-    const unsigned hi = row < 0 ? 0u : unsigned(a.slot_lu[size_t(r) * B + s]) + 1u;
-    const int pos = atomicAdd(&misc[0], 1);
-    keys[pos] = (static_cast<unsigned long long>(hi) << 32) | unsigned(s);
-  }
-  __syncthreads();
-  const int n_unprot = misc[0];
-  const int n_miss = miss_base;
-  const int n_prom = min(n_miss, n_unprot);
-  int sort_n = 1;
-  while (sort_n < n_unprot) sort_n <<= 1;
-  if (n_prom > 0) {
-    for (int i = n_unprot + tid; i < sort_n; i += kThreads) keys[i] = ~0ull;
-    __syncthreads();
-    for (int size = 2; size <= sort_n; size <<= 1) {
-      for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        for (int i = tid; i < sort_n / 2; i += kThreads) {
-          const int lo = 2 * stride * (i / stride) + (i % stride);
-          const int hi = lo + stride;
-          const bool asc = (lo & size) == 0;
-          const unsigned long long x = keys[lo], y = keys[hi];
-          if ((x > y) == asc) { keys[lo] = y; keys[hi] = x; }
-        }
-        __syncthreads();
-      }
-    }
-    // the i-th missing row (ascending) takes the i-th victim
-    for (int i = tid; i < n_prom; i += kThreads) {
-      const int s = static_cast<int>(keys[i] & 0xffffffffull);
-      const int old = a.slot_row[size_t(r) * B + s];
-      if (old >= 0) a.slot_map[size_t(r) * L + old] = -1;
-      const int nu = a.miss_rows[size_t(r) * QK + i];
-      a.slot_row[size_t(r) * B + s] = nu;
-      a.slot_lu[size_t(r) * B + s] = a.t;
-      a.slot_map[size_t(r) * L + nu] = s;
-      a.victims[size_t(r) * QK + i] = s;
-    }
-  }
+  // hits protect their slots from eviction: handed to the victim kernel
+  for (int w = tid; w < pwords; w += kThreads) a.protect[size_t(r) * pwords + w] = protect[w];
   __syncthreads();
   if (tid == 0) {
     cnt[C_ACTIVE_REQ] = 1;
     cnt[C_ACTIVE_Q] = __popc(amask);
     cnt[C_UNION] = union_base;
-    cnt[C_PROMOTED] = n_prom;
-    cnt[C_OVERFLOW] = n_miss - n_prom;
     int32_t* info = a.req_info + r * I_NUM;
     info[I_NUNION] = union_base;
-    info[I_NMISS] = n_miss;
-    info[I_NPROMOTE] = n_prom;
+    info[I_NMISS] = miss_base;
     info[I_NACTIVE] = __popc(amask);
     info[I_NR] = n_r;
   }
   __syncthreads();
-  if (tid < C_NUM) {
+  // promoted / overflow are counted by the victim kernel
+  if (tid < C_NUM && tid != C_PROMOTED && tid != C_OVERFLOW) {
     a.req_counts[size_t(r) * C_NUM + tid] = cnt[tid];
     if (cnt[tid]) atomicAdd(&a.cum[tid], static_cast<unsigned long long>(cnt[tid]));
+  }
+}
+
+// LRU victims of one request: the i-th missing row (ascending) takes the i-th
+// unprotected slot in (last_used, slot) order, empty slots first; the rest
+// overflow.  Updates the slot tables and the row -> slot map.
+__global__ __launch_bounds__(kThreads) void plan_victims_kernel(PlanArgs a) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int QK = a.Q * a.k, B = a.B, L = a.L;
+  const int pwords = (B + 31) / 32;
+  unsigned long long* keys = reinterpret_cast<unsigned long long*>(lds);
+  uint32_t* protect = reinterpret_cast<uint32_t*>(lds + size_t(a.sort_cap) * 8);
+  int* misc = reinterpret_cast<int*>(lds + size_t(a.sort_cap) * 8 + align16(size_t(pwords) * 4));
+  const int n_miss = a.req_info[r * I_NUM + I_NMISS];
+  int n_prom = 0;
+  if (n_miss > 0) {
+    for (int w = tid; w < pwords; w += kThreads) protect[w] = a.protect[size_t(r) * pwords + w];
+    if (tid == 0) misc[0] = 0;
+    __syncthreads();
+    // unselected slots' keys, compacted with one LDS atomic per wave (the
+    // order is fixed by the sort below)
+    const int lane = tid & 63;
+    for (int s0 = 0, ms = 0; s0 < B; s0 += kThreads, ++ms) {
+      const int s = s0 + tid;
+      bool take = false;
+      unsigned long long key = 0;
+      if (s < B && !((protect[s >> 5] >> (s & 31)) & 1u)) {
+        const int row = a.slot_row[size_t(r) * B + s];
+        const int lu = a.slot_lu[size_t(r) * B + s];
+        const unsigned hi = row < 0 ? 0u : unsigned(lu) + 1u;
+        key = (static_cast<unsigned long long>(hi) << 32) | unsigned(s);
+        take = true;
+      }
+      const unsigned long long m = __builtin_amdgcn_ballot_w64(take);
+      int base = 0;
+      if (lane == 0 && m) base = atomicAdd(&misc[0], static_cast<int>(__popcll(m)));
+      base = __shfl(base, 0, 64);
+      if (take) keys[base + static_cast<int>(__popcll(m & ((1ull << lane) - 1ull)))] = key;
+    }
+    __syncthreads();
+    const int n_unprot = misc[0];
+    n_prom = min(n_miss, n_unprot);
+    int sort_n = 1;
+    while (sort_n < n_unprot) sort_n <<= 1;
+    if (n_prom > 0) {
+      for (int i = n_unprot + tid; i < sort_n; i += kThreads) keys[i] = ~0ull;
+      __syncthreads();
+      // bitonic network; a wave's 64 pairs of a stage with stride <= 64 lie in
+      // its own 128 keys, so between two such stages the wave's own ordering
+      // suffices; a workgroup barrier separates every other pair of stages
+      for (int size = 2; size <= sort_n; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+          for (int i = tid; i < sort_n / 2; i += kThreads) {
+            const int lo = 2 * stride * (i / stride) + (i % stride);
+            const int hi = lo + stride;
+            const bool asc = (lo & size) == 0;
+            const unsigned long long x = keys[lo], y = keys[hi];
+            if ((x > y) == asc) { keys[lo] = y; keys[hi] = x; }
+          }
+          const int next_stride = stride > 1 ? stride >> 1 : size;
+          if (stride > 64 || next_stride > 64 || sort_n / 2 > kThreads || (stride == 1 && size == sort_n)) {
+            __syncthreads();
+          } else {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          }
+        }
+      }
+      // the i-th missing row (ascending) takes the i-th victim
+      for (int i = tid; i < n_prom; i += kThreads) {
+        const int s = static_cast<int>(keys[i] & 0xffffffffull);
+        const int old = a.slot_row[size_t(r) * B + s];
+        if (old >= 0) a.slot_map[size_t(r) * L + old] = -1;
+        const int nu = a.miss_rows[size_t(r) * QK + i];
+        a.slot_row[size_t(r) * B + s] = nu;
+        a.slot_lu[size_t(r) * B + s] = a.t;
+        a.slot_map[size_t(r) * L + nu] = s;
+        a.victims[size_t(r) * QK + i] = s;
+      }
+    }
+  }
+  if (tid == 0) {
+    a.req_info[r * I_NUM + I_NPROMOTE] = n_prom;
+    a.req_counts[size_t(r) * C_NUM + C_PROMOTED] = n_prom;
+    a.req_counts[size_t(r) * C_NUM + C_OVERFLOW] = n_miss - n_prom;
+    if (n_prom) atomicAdd(&a.cum[C_PROMOTED], static_cast<unsigned long long>(n_prom));
+    if (n_miss - n_prom) atomicAdd(&a.cum[C_OVERFLOW], static_cast<unsigned long long>(n_miss - n_prom));
   }
 }
 
@@ -283,18 +379,32 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanArgs a) {
 
 size_t plan_lds_bytes(int Q, int k, int B, int chunk_words, int sort_cap) {
   const int pwords = (B + 31) / 32;
-  return region_a_bytes(Q * k, chunk_words, sort_cap) + align16(size_t(pwords) * 4) + 128 * 4;
+  const size_t resolve = region_a_bytes(Q * k, chunk_words) + align16(size_t(pwords) * 4) + 128 * 4;
+  const size_t victims = size_t(sort_cap) * 8 + align16(size_t(pwords) * 4) + 16;
+  return resolve > victims ? resolve : victims;
 }
 
 hipError_t launch_plan(const PlanArgs& a, size_t lds, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(plan_kernel),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(plan_resolve_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(plan_kernel, dim3(a.N), dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL(plan_resolve_kernel, dim3(a.N), dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_plan_victims(const PlanArgs& a, size_t lds, hipStream_t s) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(plan_victims_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(plan_victims_kernel, dim3(a.N), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 

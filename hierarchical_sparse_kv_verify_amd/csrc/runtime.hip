@@ -4,15 +4,18 @@
 // tables, row->slot and row->resident maps, the draft ring and the pinned host
 // backing, plus chi staging arenas shared by all groups ("Adaptive
 // DHiSparse", §3.4: arenas are reused across layer groups once readers and
-// copy-back finish).  A step enqueues, on the caller's stream: ring write,
-// resolution plan, then per request chunk the attention; the host fetch of
-// each chunk runs on a side stream and the copy-back (promotion) of the
-// chunk on a third stream right after its fetch (promoted rows go to victim
-// slots, which no list of the step names, so the copy-back need not wait for
-// the attention).  Events order the three, so the fetch of chunk c+1 overlaps
-// the attention of chunk c; an arena is released once both the attention and
-// the copy-back of a chunk are done, and the caller's stream waits for the
-// last copy-back before the step returns control of the group.
+// copy-back finish).  A step runs on three streams ordered by events:
+//  - side stream (after the caller's prior work): resolution plan, the host
+//    fetch of each request chunk, then the LRU victim choice (only the
+//    copy-back and the group's next plan, on this same stream, need it);
+//  - caller's stream: ring write (beside the plan), then per chunk the
+//    attention once the chunk's fetch is done;
+//  - copy-back stream: promotion of staged rows into their victim slots
+//    (slots no list of the step names, so it need not wait for the
+//    attention).
+// The fetch of chunk c+1 overlaps the attention of chunk c; an arena chunk is
+// released once both its attention and its copy-back are done; the group's
+// next attention waits for this step's copy-backs.
 // No host synchronisation happens inside a step.
 #include <algorithm>
 #include <cmath>
@@ -29,7 +32,7 @@ using namespace kvh;
 
 namespace {
 
-enum TimedKind { K_RING = 0, K_PLAN, K_GATHER, K_ATTN, K_COMBINE, K_PROMOTE, K_NUM };
+enum TimedKind { K_RING = 0, K_PLAN, K_GATHER, K_ATTN, K_COMBINE, K_PROMOTE, K_VICTIMS, K_NUM };
 
 struct Group {
   uint16_t* hot = nullptr;
@@ -44,6 +47,9 @@ struct Group {
   int32_t* ring_lo = nullptr;
   int32_t *union_rows = nullptr, *union_loc = nullptr, *miss_rows = nullptr, *victims = nullptr;
   int32_t *loc = nullptr, *req_info = nullptr;
+  uint32_t* protect = nullptr;      // [N][ceil(B/32)] slots protected by this step's hits
+  hipEvent_t ev_done = nullptr;     // copy-backs of the group's last step finished
+  bool done_recorded = false;
   int64_t* req_counts = nullptr;
   unsigned long long* cum = nullptr;
   std::vector<void*> prefix_host;
@@ -77,16 +83,15 @@ struct kv_hier {
   float* part_o = nullptr;
   uint16_t* zero_row = nullptr;   // one all-zero row: target of masked attention reads
   float* part_ml = nullptr;
-  int splits = 1, head_groups = 1, n_chunks = 1;
-  std::vector<int> chunk_lo;
+  int splits = 1, head_groups = 1, n_chunks = 1;   // splits: the largest of chunk_splits
+  std::vector<int> chunk_lo, chunk_splits;
   int chunk_words = 0, sort_cap = 1;
   size_t plan_lds = 0;
   hipStream_t side = nullptr;       // host fetch
   hipStream_t work = nullptr;       // the rest of the step when CUs are partitioned (else null)
   hipStream_t aux = nullptr;        // copy-back of promoted rows
   std::vector<hipEvent_t> ev_attn;  // per chunk: attention done
-  hipEvent_t ev_aux = nullptr;      // end of a step's copy-backs
-  hipEvent_t ev_plan = nullptr;
+  hipEvent_t ev_resolved = nullptr; // LRU victims chosen (the copy-backs follow)
   hipEvent_t ev_in = nullptr, ev_out = nullptr;
   std::vector<hipEvent_t> ev_fetched;
   std::vector<std::vector<hipEvent_t>> ev_free;
@@ -296,6 +301,8 @@ void free_all(kv_hier* h) {
     (void)hipFree(G.union_loc);
     (void)hipFree(G.miss_rows);
     (void)hipFree(G.victims);
+    (void)hipFree(G.protect);
+    if (G.ev_done) (void)hipEventDestroy(G.ev_done);
     (void)hipFree(G.loc);
     (void)hipFree(G.req_info);
     (void)hipFree(G.req_counts);
@@ -317,7 +324,6 @@ void free_all(kv_hier* h) {
   if (h->h_commit) (void)hipHostFree(h->h_commit);
   for (auto& t : h->pending) { (void)hipEventDestroy(t.a); (void)hipEventDestroy(t.b); }
   for (hipEvent_t e : h->pool) (void)hipEventDestroy(e);
-  if (h->ev_plan) (void)hipEventDestroy(h->ev_plan);
   if (h->ev_in) (void)hipEventDestroy(h->ev_in);
   if (h->ev_out) (void)hipEventDestroy(h->ev_out);
   if (h->work) (void)hipStreamDestroy(h->work);
@@ -325,7 +331,7 @@ void free_all(kv_hier* h) {
   for (hipEvent_t e : h->ev_fetched) (void)hipEventDestroy(e);
   for (auto& v : h->ev_free) for (hipEvent_t e : v) (void)hipEventDestroy(e);
   for (hipEvent_t e : h->ev_attn) (void)hipEventDestroy(e);
-  if (h->ev_aux) (void)hipEventDestroy(h->ev_aux);
+  if (h->ev_resolved) (void)hipEventDestroy(h->ev_resolved);
   if (h->side) (void)hipStreamDestroy(h->side);
   if (h->aux) (void)hipStreamDestroy(h->aux);
 }
@@ -404,20 +410,32 @@ static int create_impl(kv_hier* h) {
     if (h->plan_lds > 160 * 1024) return fail(h, KV_EUNSUPPORTED, "plan LDS %zu", h->plan_lds);
   }
   // request chunks for the fetch/attention pipeline
-  h->n_chunks = c.n_chunks > 0 ? std::min(c.n_chunks, N) : (N >= 64 ? 4 : (N >= 16 ? 2 : 1));
-  for (int i = 0; i <= h->n_chunks; ++i) h->chunk_lo.push_back(int(int64_t(N) * i / h->n_chunks));
+  // Automatic layout for N >= 64: four quarters with the last one halved, so
+  // the attention left after the last fetch (nothing overlaps it) is short.
+  if (c.n_chunks == 0 && N >= 64) {
+    for (int x : {0, 2, 4, 6, 7, 8}) h->chunk_lo.push_back(int(int64_t(N) * x / 8));
+  } else {
+    const int nch = c.n_chunks > 0 ? std::min(c.n_chunks, N) : (N >= 16 ? 2 : 1);
+    for (int i = 0; i <= nch; ++i) h->chunk_lo.push_back(int(int64_t(N) * i / nch));
+  }
+  h->n_chunks = int(h->chunk_lo.size()) - 1;
   {
+    // key splits per chunk: about 256 workgroups per launch (the combine pass
+    // merges the splits); partials are indexed from the chunk's first request
     const int hpw = attn_heads_per_wg(c.n_heads);
     h->head_groups = (c.n_heads + hpw - 1) / hpw;
-    const int nc = (N + h->n_chunks - 1) / h->n_chunks;
-    const int64_t wgs = int64_t(nc) * c.q_max * h->head_groups;
     const int tiles = (c.topk + c.ring_window + 31) / 32;
-    int s = 1;
-    if (wgs < 128) s = int(std::min<int64_t>(8, (256 + wgs - 1) / wgs));
-    s = std::max(1, std::min(s, tiles / 4));
-    h->splits = s;
-    if (s > 1) {
-      const size_t blocks = size_t(N) * c.q_max * h->head_groups * s;
+    size_t blocks = 0;
+    h->splits = 1;
+    for (int ch = 0; ch < h->n_chunks; ++ch) {
+      const int64_t wgs = int64_t(h->chunk_lo[ch + 1] - h->chunk_lo[ch]) * c.q_max * h->head_groups;
+      int s = wgs < 256 ? int(std::min<int64_t>(8, std::max<int64_t>(1, 256 / std::max<int64_t>(1, wgs)))) : 1;
+      s = std::max(1, std::min(s, tiles / 4));
+      h->chunk_splits.push_back(s);
+      h->splits = std::max(h->splits, s);
+      if (s > 1) blocks = std::max(blocks, size_t(wgs) * s);
+    }
+    if (blocks > 0) {
       rc = dev_alloc(h, &h->part_o, blocks * hpw * c.d_v, &h->bytes_maps);
       if (!rc) rc = dev_alloc(h, &h->part_ml, blocks * hpw * 2, &h->bytes_maps);
       if (rc) return rc;
@@ -441,6 +459,7 @@ static int create_impl(kv_hier* h) {
     if ((rc = dev_alloc(h, &G.union_loc, NQK, &h->bytes_maps))) return rc;
     if ((rc = dev_alloc(h, &G.miss_rows, NQK, &h->bytes_maps))) return rc;
     if ((rc = dev_alloc(h, &G.victims, NQK, &h->bytes_maps))) return rc;
+    if ((rc = dev_alloc(h, &G.protect, size_t(N) * ((c.hot_slots + 31) / 32), &h->bytes_maps))) return rc;
     if ((rc = dev_alloc(h, &G.loc, NQK, &h->bytes_maps))) return rc;
     if ((rc = dev_alloc(h, &G.req_info, size_t(N) * I_NUM, &h->bytes_maps))) return rc;
     if ((rc = dev_alloc(h, &G.req_counts, size_t(N) * C_NUM, &h->bytes_maps))) return rc;
@@ -523,10 +542,10 @@ static int create_impl(kv_hier* h) {
     HIPCHK(h, hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking));
   }
   HIPCHK(h, hipStreamCreateWithFlags(&h->aux, hipStreamNonBlocking));
-  HIPCHK(h, hipEventCreateWithFlags(&h->ev_aux, hipEventDisableTiming));
+  for (Group& G : h->grp) HIPCHK(h, hipEventCreateWithFlags(&G.ev_done, hipEventDisableTiming));
+  HIPCHK(h, hipEventCreateWithFlags(&h->ev_resolved, hipEventDisableTiming));
   h->ev_attn.assign(h->n_chunks, nullptr);
   for (auto& e : h->ev_attn) HIPCHK(h, hipEventCreateWithFlags(&e, hipEventDisableTiming));
-  HIPCHK(h, hipEventCreateWithFlags(&h->ev_plan, hipEventDisableTiming));
   HIPCHK(h, hipEventCreateWithFlags(&h->ev_in, hipEventDisableTiming));
   HIPCHK(h, hipEventCreateWithFlags(&h->ev_out, hipEventDisableTiming));
   HIPCHK(h, hipEventCreateWithFlags(&h->ev_commit, hipEventDisableTiming));
@@ -732,8 +751,8 @@ int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t*
   const kv_hier_config& c = h->cfg;
   hipStream_t caller = static_cast<hipStream_t>(stream);
   hipStream_t s = caller;
+  HIPCHK(h, hipEventRecord(h->ev_in, caller));
   if (h->work) {           // the step runs on the partitioned stream, ordered after the caller's work
-    HIPCHK(h, hipEventRecord(h->ev_in, caller));
     HIPCHK(h, hipStreamWaitEvent(h->work, h->ev_in, 0));
     s = h->work;
   }
@@ -743,6 +762,9 @@ int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t*
   G.t += 1;
   G.calls += 1;
 
+  // resolution plan and host fetch on the side stream (no event hop between
+  // them), after the caller's prior work; the ring write runs beside the plan
+  HIPCHK(h, hipStreamWaitEvent(h->side, h->ev_in, 0));
   int ti = time_begin(h, K_RING, g, s);
   HIPCHK(h, launch_ring_write(static_cast<const uint4*>(ring_rows), causal_pos, reinterpret_cast<uint4*>(G.ring), N,
                               c.q_max, h->Rd, h->row16, s));
@@ -752,6 +774,7 @@ int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t*
   pa.topk = topk_idx;
   pa.causal = causal_pos;
   pa.res_map = G.res_map;
+  pa.has_resident = G.res_cursor > 0 ? 1 : 0;
   pa.slot_map = G.slot_map;
   pa.slot_row = G.slot_row;
   pa.slot_lu = G.slot_lu;
@@ -759,6 +782,7 @@ int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t*
   pa.union_loc = G.union_loc;
   pa.miss_rows = G.miss_rows;
   pa.victims = G.victims;
+  pa.protect = G.protect;
   pa.loc = G.loc;
   pa.req_info = G.req_info;
   pa.req_counts = G.req_counts;
@@ -771,13 +795,11 @@ int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t*
   pa.t = G.t;
   pa.chunk_words = h->chunk_words;
   pa.sort_cap = h->sort_cap;
-  ti = time_begin(h, K_PLAN, g, s);
-  HIPCHK(h, launch_plan(pa, h->plan_lds, s));
-  time_end(h, ti, s);
-  HIPCHK(h, hipEventRecord(h->ev_plan, s));
+  ti = time_begin(h, K_PLAN, g, h->side);
+  HIPCHK(h, launch_plan(pa, h->plan_lds, h->side));
+  time_end(h, ti, h->side);
 
-  // host fetch of every chunk on the side stream
-  HIPCHK(h, hipStreamWaitEvent(h->side, h->ev_plan, 0));
+  // host fetch of every chunk
   const HostRowSrc src = host_src(h, G);
   for (int ch = 0; ch < h->n_chunks; ++ch) {
     const int r0 = h->chunk_lo[ch], r1 = h->chunk_lo[ch + 1];
@@ -792,7 +814,13 @@ int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t*
     time_end(h, ti, h->side);
     HIPCHK(h, hipEventRecord(h->ev_fetched[ch], h->side));
   }
-  // attention and copy-back per chunk on the caller's stream
+  // LRU victims after the last fetch, on the same stream: off the path to the
+  // fetch, and the group's next plan (same stream) sees the updated slot tables
+  ti = time_begin(h, K_VICTIMS, g, h->side);
+  HIPCHK(h, launch_plan_victims(pa, h->plan_lds, h->side));
+  time_end(h, ti, h->side);
+  HIPCHK(h, hipEventRecord(h->ev_resolved, h->side));
+  // attention per chunk on the caller's stream, copy-back on the copy-back stream
   AttnArgs at;
   at.q = static_cast<const uint16_t*>(queries);
   at.loc = G.loc;
@@ -813,25 +841,28 @@ int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t*
   at.W = c.ring_window;
   at.Rd = h->Rd;
   at.block_only = c.ring_block_only ? 1 : 0;
-  at.splits = h->splits;
   at.head_groups = h->head_groups;
   const float scale = c.softmax_scale > 0.f ? c.softmax_scale : 1.0f / std::sqrt(float(c.d_qk));
   at.scale_log2 = scale * 1.4426950408889634f;
+  // hot slots promoted by this group's previous step
+  if (G.done_recorded) HIPCHK(h, hipStreamWaitEvent(s, G.ev_done, 0));
   for (int ch = 0; ch < h->n_chunks; ++ch) {
     at.r0 = h->chunk_lo[ch];
     at.r1 = h->chunk_lo[ch + 1];
+    at.splits = h->chunk_splits[ch];
     HIPCHK(h, hipStreamWaitEvent(s, h->ev_fetched[ch], 0));
     ti = time_begin(h, K_ATTN, g, s);
     HIPCHK(h, launch_attn(at, c.row_elems, c.d_qk, c.v_off, c.d_v, s));
     time_end(h, ti, s);
-    if (h->splits > 1) {
+    if (at.splits > 1) {
       ti = time_begin(h, K_COMBINE, g, s);
       HIPCHK(h, launch_attn_combine(at, c.d_v, s));
       time_end(h, ti, s);
     }
-    // copy-back on the aux stream: after the chunk's fetch, concurrent with its attention
+    // copy-back on the aux stream once the victims are chosen, concurrent
+    // with the attention (victim slots are not read by the step)
     HIPCHK(h, hipEventRecord(h->ev_attn[ch], s));
-    HIPCHK(h, hipStreamWaitEvent(h->aux, h->ev_fetched[ch], 0));
+    if (ch == 0) HIPCHK(h, hipStreamWaitEvent(h->aux, h->ev_resolved, 0));
     ti = time_begin(h, K_PROMOTE, g, h->aux);
     HIPCHK(h, launch_promote(reinterpret_cast<const uint4*>(h->arena[a]), G.victims, G.req_info,
                              reinterpret_cast<uint4*>(G.hot), h->QK, c.hot_slots, h->row16, at.r0, at.r1, h->aux));
@@ -845,9 +876,10 @@ int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t*
     HIPCHK(h, hipEventRecord(h->ev_free[a][ch], h->aux));
     h->free_recorded[a][ch] = 1;
   }
-  // the group's hot cache is complete only after its copy-backs
-  HIPCHK(h, hipEventRecord(h->ev_aux, h->aux));
-  HIPCHK(h, hipStreamWaitEvent(s, h->ev_aux, 0));
+  // the group's hot cache is complete after its copy-backs: the group's next
+  // attention waits for this
+  HIPCHK(h, hipEventRecord(G.ev_done, h->aux));
+  G.done_recorded = true;
   if (h->work) {
     HIPCHK(h, hipEventRecord(h->ev_out, s));
     HIPCHK(h, hipStreamWaitEvent(caller, h->ev_out, 0));
@@ -918,12 +950,14 @@ int kv_hier_stats(kv_hier_t* h, int g, kv_hier_counters* cum, kv_hier_counters* 
       o->ms_attn = G.ms[K_ATTN];
       o->ms_combine = G.ms[K_COMBINE];
       o->ms_promote = G.ms[K_PROMOTE];
+      o->ms_victims = G.ms[K_VICTIMS];
       o->n_ring = G.nt[K_RING];
       o->n_plan = G.nt[K_PLAN];
       o->n_gather = G.nt[K_GATHER];
       o->n_attn = G.nt[K_ATTN];
       o->n_combine = G.nt[K_COMBINE];
       o->n_promote = G.nt[K_PROMOTE];
+      o->n_victims = G.nt[K_VICTIMS];
     }
   };
   if (cum) {

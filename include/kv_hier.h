@@ -116,8 +116,8 @@ typedef struct {
   int64_t sel_hot;
   int64_t sel_miss;         /* missing selections (sum over queries)                     */
   /* kernel time in ms summed over timed calls (KV_FLAG_TIMING), and launch counts */
-  double ms_ring, ms_plan, ms_gather, ms_attn, ms_combine, ms_promote;
-  int64_t n_ring, n_plan, n_gather, n_attn, n_combine, n_promote;
+  double ms_ring, ms_plan, ms_gather, ms_attn, ms_combine, ms_promote, ms_victims;
+  int64_t n_ring, n_plan, n_gather, n_attn, n_combine, n_promote, n_victims;
 } kv_hier_counters;
 
 /* Per-request lists of the last verify_step of a group (kv_hier_last_lists).
