@@ -178,7 +178,9 @@ hipEvent_t take_event(kv_hier* h) {
 
 // Records a start event when timing is on; returns the pending index or -1.
 int time_begin(kv_hier* h, int kind, int g, hipStream_t s) {
-  if (!(h->cfg.flags & KV_FLAG_TIMING)) return -1;
+  const bool on = (h->cfg.flags & KV_FLAG_TIMING) ||
+                  ((h->cfg.flags & KV_FLAG_TIMING_ATTN) && (kind == K_ATTN || kind == K_COMBINE));
+  if (!on) return -1;
   Timed t{kind, g, take_event(h), take_event(h)};
   if (!t.a || !t.b || hipEventRecord(t.a, s) != hipSuccess) return -1;
   h->pending.push_back(t);
@@ -846,6 +848,7 @@ int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t*
   at.scale_log2 = scale * 1.4426950408889634f;
   // hot slots promoted by this group's previous step
   if (G.done_recorded) HIPCHK(h, hipStreamWaitEvent(s, G.ev_done, 0));
+  if (c.flags & KV_FLAG_SERIAL) HIPCHK(h, hipStreamWaitEvent(s, h->ev_fetched[h->n_chunks - 1], 0));
   for (int ch = 0; ch < h->n_chunks; ++ch) {
     at.r0 = h->chunk_lo[ch];
     at.r1 = h->chunk_lo[ch + 1];
@@ -1067,7 +1070,8 @@ int kv_hier_sync(kv_hier_t* h) {
 
 int kv_hier_set_flags(kv_hier_t* h, int32_t flags) {
   if (!h) return KV_EINVAL;
-  if (flags & ~(KV_FLAG_TIMING | KV_FLAG_POISON)) return fail(h, KV_EINVAL, "unknown flags %d", flags);
+  if (flags & ~(KV_FLAG_TIMING | KV_FLAG_POISON | KV_FLAG_TIMING_ATTN | KV_FLAG_SERIAL))
+    return fail(h, KV_EINVAL, "unknown flags %d", flags);
   int rc = sync_all(h);
   if (rc) return rc;
   h->cfg.flags = flags;

@@ -61,7 +61,11 @@ enum { KV_TIER_HOT = 0, KV_TIER_STAGED = 1, KV_TIER_RESIDENT = 2, KV_TIER_RING =
 
 enum {
   KV_FLAG_TIMING = 1,    /* time every kernel with HIP events (kv_hier_stats ms_*) */
-  KV_FLAG_POISON = 2     /* debug: fill a staging arena with NaN after its readers finish */
+  KV_FLAG_POISON = 2,    /* debug: fill a staging arena with NaN after its readers finish */
+  KV_FLAG_TIMING_ATTN = 4, /* time only the attention (and split-combine) launches: the
+                              events then sit on no stream that gates the host fetch   */
+  KV_FLAG_SERIAL = 8      /* measurement: the step's attention starts only after its whole
+                             host fetch, so it runs alone on the GPU (slower steps)     */
 };
 
 typedef struct kv_hier kv_hier_t;  /* opaque, owned by the library */
