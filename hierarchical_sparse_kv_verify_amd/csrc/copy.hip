@@ -29,8 +29,10 @@ __device__ inline const uint4* host_row(const HostRowSrc& s, int r, int row) {
 // One 16-byte chunk in flight per lane with 32-bit incremental (row, chunk)
 // indices: the kernel needs few registers, so its waves fit on CUs that also
 // run attention workgroups (a fetch that must wait for free CUs loses most of
-// its host-link rate).
-__global__ __launch_bounds__(256) void miss_gather_kernel(HostRowSrc src, const int32_t* __restrict__ miss_rows,
+// its host-link rate).  One wave per workgroup spreads the host reads thinly
+// over many CUs: the attention workgroups sharing a CU with them slow down
+// less than under a few CUs each holding four fetch waves.
+__global__ __launch_bounds__(64) void miss_gather_kernel(HostRowSrc src, const int32_t* __restrict__ miss_rows,
                                                           const int32_t* __restrict__ req_info,
                                                           uint4* __restrict__ staging, int QK, int r0) {
   const int r = r0 + blockIdx.y;
@@ -148,7 +150,7 @@ inline unsigned grid_for(size_t work, unsigned cap) {
 hipError_t launch_miss_gather(const HostRowSrc& src, const int32_t* miss_rows, const int32_t* req_info,
                               uint4* staging, int QK, int r0, int r1, int wg_per_req, hipStream_t s) {
   if (r1 <= r0) return hipSuccess;
-  hipLaunchKernelGGL(miss_gather_kernel, dim3(wg_per_req, r1 - r0), dim3(256), 0, s, src, miss_rows,
+  hipLaunchKernelGGL(miss_gather_kernel, dim3(wg_per_req, r1 - r0), dim3(64), 0, s, src, miss_rows,
                      req_info, staging, QK, r0);
   return hipGetLastError();
 }

@@ -806,9 +806,9 @@ int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t*
   for (int ch = 0; ch < h->n_chunks; ++ch) {
     const int r0 = h->chunk_lo[ch], r1 = h->chunk_lo[ch + 1];
     if (h->free_recorded[a][ch]) HIPCHK(h, hipStreamWaitEvent(h->side, h->ev_free[a][ch], 0));
-    // few workgroups: enough host reads in flight to fill the link; more only
-    // queue in the memory system and slow the attention running beside them
-    const int wgs = c.fetch_wgs > 0 ? c.fetch_wgs : 32;
+    // 128 one-wave workgroups: enough host reads in flight to fill the link;
+    // more only queue in the memory system and slow the attention beside them
+    const int wgs = c.fetch_wgs > 0 ? c.fetch_wgs : 128;
     const int wpr = std::max(1, wgs / std::max(1, r1 - r0));
     ti = time_begin(h, K_GATHER, g, h->side);
     HIPCHK(h, launch_miss_gather(src, G.miss_rows, G.req_info, reinterpret_cast<uint4*>(h->arena[a]), h->QK, r0, r1,

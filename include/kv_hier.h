@@ -95,9 +95,10 @@ typedef struct {
   int32_t fetch_cus;        /* >0: CUs reserved for the host fetch (CU-masked streams: the
                                fetch runs on those CUs, the rest of the step on the others);
                                0: every stream may use every CU                          */
-  int32_t fetch_wgs;        /* workgroups of one chunk's host fetch, at least one per request
-                               (0 = 32): enough PCIe reads in flight to fill the link; more
-                               only queue in the memory system and slow the attention    */
+  int32_t fetch_wgs;        /* one-wave workgroups of a chunk's host fetch, at least one per
+                               request (0 = 128): enough PCIe reads in flight to fill the
+                               link; more only queue in the memory system and slow the
+                               attention running beside them                             */
 } kv_hier_config;
 
 /* Counters of one layer group (kv_hier_stats).  "union_*" count distinct rows

@@ -225,21 +225,23 @@ def test_inactive_requests_and_queries():
 
 def test_poisoned_arena_after_readers():
     """With arena poisoning the step's outputs are unchanged: the arena is
-    overwritten only after attention and copy-back have read it."""
+    overwritten only after attention and copy-back have read it.  Timing
+    events and the serialised attention leave the outputs unchanged too."""
     w = _mla_small(n_groups=1, var_k=False)
     outs = []
-    for flags in (0, 2):
+    for flags in (0, 2, 1, 4 | 8):
         pair = build_pair(w, with_oracle=False, lib_kw=dict(flags=flags, n_chunks=2))
         si = make_step_inputs(w, 0, 0, pair.hist_len)
         outs.append(run_lib_step(pair, 0, si))
-        if flags:
+        if flags == 2:
             L = pair.lib.last_lists(0, 0)
             staged = L["loc"][L["loc"] >= 0]
             staged = staged[(staged >> 29) == 1][:4]
             if staged.size:
                 assert (pair.lib.read_rows(0, staged) == 0x7fc0).all()
         pair.lib.close()
-    assert np.array_equal(outs[0], outs[1])
+    for o in outs[1:]:
+        assert np.array_equal(outs[0], o)
 
 
 def test_full_size_mla128_sampled():
