@@ -47,7 +47,7 @@ class Config(ctypes.Structure):
         "d_qk", "v_off", "d_v", "n_heads", "q_max", "topk", "hot_slots", "ring_window",
         "ring_page", "ring_block_only", "n_chunks")] + [
         ("resident_cap", ctypes.c_int64), ("softmax_scale", ctypes.c_float), ("flags", ctypes.c_int32),
-        ("fetch_cus", ctypes.c_int32), ("fetch_wgs", ctypes.c_int32)]
+        ("fetch_cus", ctypes.c_int32), ("fetch_wgs", ctypes.c_int32), ("plan_share", ctypes.c_int32)]
 
 
 COUNTER_FIELDS = ("calls", "active_requests", "active_queries", "selections", "pads", "invalid",
@@ -170,7 +170,7 @@ class KVHier:
         self._lib = load_library()
         c = Config()
         defaults = dict(n_arenas=1, n_prefix=0, prefix_len=0, ring_block_only=0, n_chunks=0,
-                        resident_cap=0, softmax_scale=0.0, flags=0, fetch_cus=0, fetch_wgs=0)
+                        resident_cap=0, softmax_scale=0.0, flags=0, fetch_cus=0, fetch_wgs=0, plan_share=0)
         defaults.update(cfg)
         for name, _ in Config._fields_:
             if name not in defaults:

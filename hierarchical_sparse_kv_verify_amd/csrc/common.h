@@ -83,6 +83,8 @@ hipError_t launch_commit(const CommitGroup* groups, int G, const int32_t* nbefor
 struct PoolView { const uint4* hot; const uint4* staging; const uint4* resident; const uint4* ring; };
 hipError_t launch_read_rows(const PoolView& pv, const int32_t* locs, int n, uint4* dst, int row16,
                             hipStream_t s);
+// a follower layer's counters: dst[r][c] = src[r][c]; cum[c] += sum_r src[r][c]
+hipError_t launch_counts_follow(const int64_t* src, int64_t* dst, unsigned long long* cum, int N, hipStream_t s);
 // fill 32-bit words with a value (used instead of memset inside the step)
 hipError_t launch_fill32(uint32_t* p, uint32_t v, size_t n, hipStream_t s);
 

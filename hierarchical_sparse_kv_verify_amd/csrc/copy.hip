@@ -134,6 +134,21 @@ __global__ __launch_bounds__(256) void read_rows_kernel(PoolView pv, const int32
   }
 }
 
+// A follower layer's counters: the leader's last-step per-request counts,
+// copied and added to the follower's cumulative counters.
+__global__ __launch_bounds__(256) void counts_follow_kernel(const int64_t* __restrict__ src, int64_t* __restrict__ dst,
+                                                            unsigned long long* __restrict__ cum, int N) {
+  for (int c = 0; c < C_NUM; ++c) {
+    int64_t part = 0;
+    for (int r = threadIdx.x; r < N; r += blockDim.x) {
+      const int64_t v = src[size_t(r) * C_NUM + c];
+      dst[size_t(r) * C_NUM + c] = v;
+      part += v;
+    }
+    if (part) atomicAdd(&cum[c], static_cast<unsigned long long>(part));
+  }
+}
+
 __global__ __launch_bounds__(256) void fill32_kernel(uint32_t* p, uint32_t v, size_t n) {
   const size_t stride = size_t(gridDim.x) * blockDim.x;
   for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = v;
@@ -192,6 +207,11 @@ hipError_t launch_read_rows(const PoolView& pv, const int32_t* locs, int n, uint
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(read_rows_kernel, dim3(grid_for(size_t(n) * row16, 1024)), dim3(256), 0, s, pv, locs, n,
                      dst, row16);
+  return hipGetLastError();
+}
+
+hipError_t launch_counts_follow(const int64_t* src, int64_t* dst, unsigned long long* cum, int N, hipStream_t s) {
+  hipLaunchKernelGGL(counts_follow_kernel, dim3(1), dim3(256), 0, s, src, dst, cum, N);
   return hipGetLastError();
 }
 

@@ -35,6 +35,8 @@ namespace {
 enum TimedKind { K_RING = 0, K_PLAN, K_GATHER, K_ATTN, K_COMBINE, K_PROMOTE, K_VICTIMS, K_NUM };
 
 struct Group {
+  int leader = 0;                   // group whose plan this group uses (itself unless a follower)
+  int member = 0;                   // index within its plan-sharing set (0 = the leader)
   uint16_t* hot = nullptr;
   int32_t* slot_row = nullptr;
   int32_t* slot_lu = nullptr;
@@ -93,7 +95,8 @@ struct kv_hier {
   std::vector<hipEvent_t> ev_attn;  // per chunk: attention done
   hipEvent_t ev_resolved = nullptr; // LRU victims chosen (the copy-backs follow)
   hipEvent_t ev_in = nullptr, ev_out = nullptr;
-  std::vector<hipEvent_t> ev_fetched;
+  int share = 1;                    // groups per plan-sharing set (leader + followers)
+  std::vector<std::vector<hipEvent_t>> ev_fetched;   // [set member][chunk]
   std::vector<std::vector<hipEvent_t>> ev_free;
   std::vector<std::vector<char>> free_recorded;
   std::vector<int32_t> hist_len;
@@ -330,7 +333,7 @@ void free_all(kv_hier* h) {
   if (h->ev_out) (void)hipEventDestroy(h->ev_out);
   if (h->work) (void)hipStreamDestroy(h->work);
   if (h->ev_commit) (void)hipEventDestroy(h->ev_commit);
-  for (hipEvent_t e : h->ev_fetched) (void)hipEventDestroy(e);
+  for (auto& v : h->ev_fetched) for (hipEvent_t e : v) (void)hipEventDestroy(e);
   for (auto& v : h->ev_free) for (hipEvent_t e : v) (void)hipEventDestroy(e);
   for (hipEvent_t e : h->ev_attn) (void)hipEventDestroy(e);
   if (h->ev_resolved) (void)hipEventDestroy(h->ev_resolved);
@@ -345,7 +348,7 @@ int validate(kv_hier* h, const kv_hier_config& c) {
   if (c.n_req <= 0 || c.n_groups <= 0 || c.n_arenas <= 0 || c.hist_cap <= 0 || c.row_elems <= 0 ||
       c.d_qk <= 0 || c.d_v <= 0 || c.v_off < 0 || c.n_heads <= 0 || c.q_max <= 0 || c.topk <= 0 ||
       c.hot_slots <= 0 || c.ring_window <= 0 || c.ring_page <= 0 || c.n_prefix < 0 || c.prefix_len < 0 ||
-      c.n_chunks < 0 || c.resident_cap < 0 || c.fetch_cus < 0 || c.fetch_wgs < 0)
+      c.n_chunks < 0 || c.resident_cap < 0 || c.fetch_cus < 0 || c.fetch_wgs < 0 || c.plan_share < 0)
     return fail(h, KV_EINVAL, "non-positive size in config");
   if (c.q_max > 32) return fail(h, KV_EUNSUPPORTED, "q_max %d > 32", c.q_max);
   if (int64_t(c.q_max) * c.topk > 65535) return fail(h, KV_EUNSUPPORTED, "q_max*topk > 65535");
@@ -362,6 +365,10 @@ int validate(kv_hier* h, const kv_hier_config& c) {
       int64_t(c.n_req) * ring_size(c.ring_window, c.ring_page, c.q_max) >= lim)
     return fail(h, KV_EUNSUPPORTED, "an index space exceeds 2^29 rows");
   if (c.hot_slots > 16384) return fail(h, KV_EUNSUPPORTED, "hot_slots > 16384");
+  if (c.plan_share > 1 && c.n_groups % c.plan_share != 0)
+    return fail(h, KV_EINVAL, "n_groups %d is not a multiple of plan_share %d", c.n_groups, c.plan_share);
+  if (c.plan_share > 1 && c.n_arenas < c.plan_share)
+    return fail(h, KV_EINVAL, "plan_share %d needs as many arenas (n_arenas %d)", c.plan_share, c.n_arenas);
   return KV_OK;
 }
 
@@ -443,9 +450,12 @@ static int create_impl(kv_hier* h) {
       if (rc) return rc;
     }
   }
+  h->share = c.plan_share > 1 ? c.plan_share : 1;
   h->grp.resize(c.n_groups);
   for (int g = 0; g < c.n_groups; ++g) {
     Group& G = h->grp[g];
+    G.member = g % h->share;
+    G.leader = g - G.member;
     G.res_set.assign(N, 0);
     const size_t NB = size_t(N) * B, NL = size_t(N) * L, NQK = size_t(N) * h->QK;
     if ((rc = dev_alloc(h, &G.hot, NB * c.row_elems, &h->bytes_hot))) return rc;
@@ -551,8 +561,9 @@ static int create_impl(kv_hier* h) {
   HIPCHK(h, hipEventCreateWithFlags(&h->ev_in, hipEventDisableTiming));
   HIPCHK(h, hipEventCreateWithFlags(&h->ev_out, hipEventDisableTiming));
   HIPCHK(h, hipEventCreateWithFlags(&h->ev_commit, hipEventDisableTiming));
-  h->ev_fetched.assign(h->n_chunks, nullptr);
-  for (auto& e : h->ev_fetched) HIPCHK(h, hipEventCreateWithFlags(&e, hipEventDisableTiming));
+  h->ev_fetched.assign(h->share, std::vector<hipEvent_t>(h->n_chunks, nullptr));
+  for (auto& v : h->ev_fetched)
+    for (auto& e : v) HIPCHK(h, hipEventCreateWithFlags(&e, hipEventDisableTiming));
   h->ev_free.assign(c.n_arenas, std::vector<hipEvent_t>(h->n_chunks, nullptr));
   h->free_recorded.assign(c.n_arenas, std::vector<char>(h->n_chunks, 0));
   for (auto& v : h->ev_free)
@@ -749,7 +760,14 @@ int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t*
                         const int32_t* causal_pos, const void* ring_rows, void* out, void* stream) {
   int rc = check_group(h, g);
   if (rc) return rc;
-  if (!queries || !topk_idx || !causal_pos || !ring_rows || !out) return fail(h, KV_EINVAL, "null device pointer");
+  if (!queries || !causal_pos || !ring_rows || !out) return fail(h, KV_EINVAL, "null device pointer");
+  {
+    const Group& G0 = h->grp[g];
+    if (G0.member == 0 && !topk_idx) return fail(h, KV_EINVAL, "null device pointer");
+    if (G0.member != 0 && h->grp[G0.leader].t != G0.t + 1)
+      return fail(h, KV_ESTATE, "group %d uses the plan of group %d: call that group's step first, once per step",
+                  g, G0.leader);
+  }
   const kv_hier_config& c = h->cfg;
   hipStream_t caller = static_cast<hipStream_t>(stream);
   hipStream_t s = caller;
@@ -759,73 +777,89 @@ int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t*
     s = h->work;
   }
   Group& G = h->grp[g];
+  Group& P = h->grp[G.leader];      // owner of the plan state (G itself unless a follower)
+  const bool lead = G.member == 0;
   const int N = c.n_req;
   const int a = g % c.n_arenas;
-  G.t += 1;
+  if (lead) {
+    G.t += 1;
+  } else {
+    G.t = P.t;
+  }
   G.calls += 1;
 
-  // resolution plan and host fetch on the side stream (no event hop between
-  // them), after the caller's prior work; the ring write runs beside the plan
-  HIPCHK(h, hipStreamWaitEvent(h->side, h->ev_in, 0));
   int ti = time_begin(h, K_RING, g, s);
   HIPCHK(h, launch_ring_write(static_cast<const uint4*>(ring_rows), causal_pos, reinterpret_cast<uint4*>(G.ring), N,
                               c.q_max, h->Rd, h->row16, s));
   time_end(h, ti, s);
+  if (lead) {
+    // resolution plan and host fetch on the side stream (no event hop between
+    // them), after the caller's prior work; the ring write runs beside the plan
+    HIPCHK(h, hipStreamWaitEvent(h->side, h->ev_in, 0));
 
-  PlanArgs pa;
-  pa.topk = topk_idx;
-  pa.causal = causal_pos;
-  pa.res_map = G.res_map;
-  pa.has_resident = G.res_cursor > 0 ? 1 : 0;
-  pa.slot_map = G.slot_map;
-  pa.slot_row = G.slot_row;
-  pa.slot_lu = G.slot_lu;
-  pa.union_rows = G.union_rows;
-  pa.union_loc = G.union_loc;
-  pa.miss_rows = G.miss_rows;
-  pa.victims = G.victims;
-  pa.protect = G.protect;
-  pa.loc = G.loc;
-  pa.req_info = G.req_info;
-  pa.req_counts = G.req_counts;
-  pa.cum = G.cum;
-  pa.N = N;
-  pa.Q = c.q_max;
-  pa.k = c.topk;
-  pa.B = c.hot_slots;
-  pa.L = h->L;
-  pa.t = G.t;
-  pa.chunk_words = h->chunk_words;
-  pa.sort_cap = h->sort_cap;
-  ti = time_begin(h, K_PLAN, g, h->side);
-  HIPCHK(h, launch_plan(pa, h->plan_lds, h->side));
-  time_end(h, ti, h->side);
-
-  // host fetch of every chunk
-  const HostRowSrc src = host_src(h, G);
-  for (int ch = 0; ch < h->n_chunks; ++ch) {
-    const int r0 = h->chunk_lo[ch], r1 = h->chunk_lo[ch + 1];
-    if (h->free_recorded[a][ch]) HIPCHK(h, hipStreamWaitEvent(h->side, h->ev_free[a][ch], 0));
-    // 128 one-wave workgroups: enough host reads in flight to fill the link;
-    // more only queue in the memory system and slow the attention beside them
-    const int wgs = c.fetch_wgs > 0 ? c.fetch_wgs : 128;
-    const int wpr = std::max(1, wgs / std::max(1, r1 - r0));
-    ti = time_begin(h, K_GATHER, g, h->side);
-    HIPCHK(h, launch_miss_gather(src, G.miss_rows, G.req_info, reinterpret_cast<uint4*>(h->arena[a]), h->QK, r0, r1,
-                                 wpr, h->side));
+    PlanArgs pa;
+    pa.topk = topk_idx;
+    pa.causal = causal_pos;
+    pa.res_map = G.res_map;
+    pa.has_resident = G.res_cursor > 0 ? 1 : 0;
+    pa.slot_map = G.slot_map;
+    pa.slot_row = G.slot_row;
+    pa.slot_lu = G.slot_lu;
+    pa.union_rows = G.union_rows;
+    pa.union_loc = G.union_loc;
+    pa.miss_rows = G.miss_rows;
+    pa.victims = G.victims;
+    pa.protect = G.protect;
+    pa.loc = G.loc;
+    pa.req_info = G.req_info;
+    pa.req_counts = G.req_counts;
+    pa.cum = G.cum;
+    pa.N = N;
+    pa.Q = c.q_max;
+    pa.k = c.topk;
+    pa.B = c.hot_slots;
+    pa.L = h->L;
+    pa.t = G.t;
+    pa.chunk_words = h->chunk_words;
+    pa.sort_cap = h->sort_cap;
+    ti = time_begin(h, K_PLAN, g, h->side);
+    HIPCHK(h, launch_plan(pa, h->plan_lds, h->side));
     time_end(h, ti, h->side);
-    HIPCHK(h, hipEventRecord(h->ev_fetched[ch], h->side));
+
+    // host fetch of every chunk, for this group and then for every follower
+    // layer of its plan (one selection starts the transfers of all of them;
+    // each layer fetches its own bytes into its own arena).  The LRU victims
+    // follow this group's own fetch, on the same stream: off the path to its
+    // fetch, before the followers' fetches (their copy-backs need them), and
+    // the group's next plan (same stream) sees the updated slot tables.
+    for (int m = 0; m < h->share; ++m) {
+      const int gm = g + m, am = gm % c.n_arenas;
+      const HostRowSrc src = host_src(h, h->grp[gm]);
+      for (int ch = 0; ch < h->n_chunks; ++ch) {
+        const int r0 = h->chunk_lo[ch], r1 = h->chunk_lo[ch + 1];
+        if (h->free_recorded[am][ch]) HIPCHK(h, hipStreamWaitEvent(h->side, h->ev_free[am][ch], 0));
+        // 128 one-wave workgroups: enough host reads in flight to fill the link;
+        // more only queue in the memory system and slow the attention beside them
+        const int wgs = c.fetch_wgs > 0 ? c.fetch_wgs : 128;
+        const int wpr = std::max(1, wgs / std::max(1, r1 - r0));
+        ti = time_begin(h, K_GATHER, gm, h->side);
+        HIPCHK(h, launch_miss_gather(src, G.miss_rows, G.req_info, reinterpret_cast<uint4*>(h->arena[am]), h->QK,
+                                     r0, r1, wpr, h->side));
+        time_end(h, ti, h->side);
+        HIPCHK(h, hipEventRecord(h->ev_fetched[m][ch], h->side));
+      }
+      if (m == 0) {
+        ti = time_begin(h, K_VICTIMS, g, h->side);
+        HIPCHK(h, launch_plan_victims(pa, h->plan_lds, h->side));
+        time_end(h, ti, h->side);
+        HIPCHK(h, hipEventRecord(h->ev_resolved, h->side));
+      }
+    }
   }
-  // LRU victims after the last fetch, on the same stream: off the path to the
-  // fetch, and the group's next plan (same stream) sees the updated slot tables
-  ti = time_begin(h, K_VICTIMS, g, h->side);
-  HIPCHK(h, launch_plan_victims(pa, h->plan_lds, h->side));
-  time_end(h, ti, h->side);
-  HIPCHK(h, hipEventRecord(h->ev_resolved, h->side));
   // attention per chunk on the caller's stream, copy-back on the copy-back stream
   AttnArgs at;
   at.q = static_cast<const uint16_t*>(queries);
-  at.loc = G.loc;
+  at.loc = P.loc;
   at.causal = causal_pos;
   at.ring_lo = G.ring_lo;
   at.hot = G.hot;
@@ -848,12 +882,12 @@ int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t*
   at.scale_log2 = scale * 1.4426950408889634f;
   // hot slots promoted by this group's previous step
   if (G.done_recorded) HIPCHK(h, hipStreamWaitEvent(s, G.ev_done, 0));
-  if (c.flags & KV_FLAG_SERIAL) HIPCHK(h, hipStreamWaitEvent(s, h->ev_fetched[h->n_chunks - 1], 0));
+  if (c.flags & KV_FLAG_SERIAL) HIPCHK(h, hipStreamWaitEvent(s, h->ev_fetched[G.member][h->n_chunks - 1], 0));
   for (int ch = 0; ch < h->n_chunks; ++ch) {
     at.r0 = h->chunk_lo[ch];
     at.r1 = h->chunk_lo[ch + 1];
     at.splits = h->chunk_splits[ch];
-    HIPCHK(h, hipStreamWaitEvent(s, h->ev_fetched[ch], 0));
+    HIPCHK(h, hipStreamWaitEvent(s, h->ev_fetched[G.member][ch], 0));
     ti = time_begin(h, K_ATTN, g, s);
     HIPCHK(h, launch_attn(at, c.row_elems, c.d_qk, c.v_off, c.d_v, s));
     time_end(h, ti, s);
@@ -865,9 +899,15 @@ int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t*
     // copy-back on the aux stream once the victims are chosen, concurrent
     // with the attention (victim slots are not read by the step)
     HIPCHK(h, hipEventRecord(h->ev_attn[ch], s));
-    if (ch == 0) HIPCHK(h, hipStreamWaitEvent(h->aux, h->ev_resolved, 0));
+    if (ch == 0) {
+      HIPCHK(h, hipStreamWaitEvent(h->aux, h->ev_resolved, 0));
+      // a follower's counters are its plan's: copy the leader's last-step counts
+      if (!lead) HIPCHK(h, launch_counts_follow(P.req_counts, G.req_counts, G.cum, N, h->aux));
+    }
+    // a follower's chunk is fetched after its leader's victims are chosen
+    if (!lead) HIPCHK(h, hipStreamWaitEvent(h->aux, h->ev_fetched[G.member][ch], 0));
     ti = time_begin(h, K_PROMOTE, g, h->aux);
-    HIPCHK(h, launch_promote(reinterpret_cast<const uint4*>(h->arena[a]), G.victims, G.req_info,
+    HIPCHK(h, launch_promote(reinterpret_cast<const uint4*>(h->arena[a]), P.victims, P.req_info,
                              reinterpret_cast<uint4*>(G.hot), h->QK, c.hot_slots, h->row16, at.r0, at.r1, h->aux));
     time_end(h, ti, h->aux);
     HIPCHK(h, hipStreamWaitEvent(h->aux, h->ev_attn[ch], 0));
@@ -997,7 +1037,7 @@ int kv_hier_last_lists(kv_hier_t* h, int g, int r, kv_hier_lists* o) {
   if (!o || !o->union_rows || !o->union_loc || !o->miss_rows || !o->victims || !o->loc)
     return fail(h, KV_EINVAL, "null list buffer");
   if ((rc = sync_all(h))) return rc;
-  Group& G = h->grp[g];
+  Group& G = h->grp[h->grp[g].leader];   // lists belong to the plan (the leader's for a follower)
   int32_t info[I_NUM];
   if ((rc = download(h, info, G.req_info + size_t(r) * I_NUM, sizeof info))) return rc;
   const size_t base = size_t(r) * h->QK;
@@ -1019,8 +1059,9 @@ int kv_hier_slot_table(kv_hier_t* h, int g, int r, int32_t* rows, int32_t* last_
   if (!rows || !last_used) return fail(h, KV_EINVAL, "null output");
   if ((rc = sync_all(h))) return rc;
   const int B = h->cfg.hot_slots;
-  if ((rc = download(h, rows, h->grp[g].slot_row + size_t(r) * B, size_t(B) * 4))) return rc;
-  return download(h, last_used, h->grp[g].slot_lu + size_t(r) * B, size_t(B) * 4);
+  const Group& G = h->grp[h->grp[g].leader];   // the plan's slot table (shared by its followers)
+  if ((rc = download(h, rows, G.slot_row + size_t(r) * B, size_t(B) * 4))) return rc;
+  return download(h, last_used, G.slot_lu + size_t(r) * B, size_t(B) * 4);
 }
 
 int kv_hier_read_rows(kv_hier_t* h, int g, const int32_t* locs, int n, void* rows) {

@@ -99,6 +99,15 @@ typedef struct {
                                request (0 = 128): enough PCIe reads in flight to fill the
                                link; more only queue in the memory system and slow the
                                attention running beside them                             */
+  int32_t plan_share;       /* > 1: groups come in consecutive sets of plan_share payload
+                               layers fed by one index producer (one selection).  The first
+                               group of a set resolves the selection once and starts the
+                               host fetch of every layer of the set (each into its own
+                               arena: n_arenas >= plan_share); the others reuse its plan
+                               and their verify_step only attends and copies back.  Groups
+                               of a set must be given identical set_hot / set_resident
+                               contents (their own payload rows).  0 or 1: one plan per
+                               group.                                                    */
 } kv_hier_config;
 
 /* Counters of one layer group (kv_hier_stats).  "union_*" count distinct rows
@@ -204,7 +213,13 @@ int kv_hier_ring_load(kv_hier_t *h, int g, int r, int32_t first_pos, const void 
  * of earlier request chunks), runs exact sparse attention of every query over
  * its own list plus its ring window, and copies promoted rows into their
  * victim slots.  Caller contract (not checked on the device): causal_pos[r][0]
- * equals the frontier set by kv_hier_set_hist_len / kv_hier_commit. */
+ * equals the frontier set by kv_hier_set_hist_len / kv_hier_commit.
+ * With plan_share > 1 ("Adaptive DHiSparse" §3.2: one index producer announcing
+ * positions for several payload layers): the first group of a set resolves
+ * topk_idx and starts the host fetch of every layer of the set; a follower
+ * group's step (after its leader's, once per step, else KV_ESTATE) ignores
+ * topk_idx (may be NULL), attends over its own payload through the leader's
+ * locations and copies back into its own hot cache. */
 int kv_hier_verify_step(kv_hier_t *h, int g, const void *queries, const int32_t *topk_idx,
                         const int32_t *causal_pos, const void *ring_rows, void *out,
                         void *stream);
@@ -221,10 +236,12 @@ int kv_hier_commit(kv_hier_t *h, const int32_t *accepted, void *stream);
 int kv_hier_stats(kv_hier_t *h, int g, kv_hier_counters *cumulative, kv_hier_counters *last);
 int kv_hier_reset_stats(kv_hier_t *h);
 
-/* Waits, then copies request r's lists of the last step of group g. */
+/* Waits, then copies request r's lists of the last step of group g (a
+ * follower's are its leader's). */
 int kv_hier_last_lists(kv_hier_t *h, int g, int r, kv_hier_lists *out);
 
-/* Waits, then copies the slot table of (g, r): host int32[B] rows and stamps. */
+/* Waits, then copies the slot table of (g, r): host int32[B] rows and stamps
+ * (a follower's is its leader's: the plan's table). */
 int kv_hier_slot_table(kv_hier_t *h, int g, int r, int32_t *rows, int32_t *last_used);
 
 /* Waits, then copies the rows at n location codes (host int32) of group g

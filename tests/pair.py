@@ -26,7 +26,7 @@ def lib_config(w: Workload, **kw) -> dict:
                row_elems=w.row_elems, d_qk=w.d_qk, v_off=w.v_off, d_v=w.d_v, n_heads=w.n_heads,
                q_max=w.q_max, topk=w.topk, hot_slots=w.hot_slots, ring_window=w.ring_window,
                ring_page=w.ring_page, ring_block_only=0, n_chunks=0, resident_cap=0,
-               softmax_scale=0.0, flags=0, fetch_cus=0, fetch_wgs=0)
+               softmax_scale=0.0, flags=0, fetch_cus=0, fetch_wgs=0, plan_share=w.plan_share)
     cfg.update(kw)
     return cfg
 

@@ -58,6 +58,9 @@ def _cfg(**kw):
     (dict(n_prefix=2, prefix_len=0), -1),
     (dict(hot_slots=20000), -5),
     (dict(n_req=1 << 20, hot_slots=1024), -5),
+    (dict(n_groups=3, plan_share=2, n_arenas=2), -1),
+    (dict(n_groups=4, plan_share=4, n_arenas=2), -1),
+    (dict(plan_share=-1), -1),
 ])
 def test_create_rejects_bad_config(lib, kw, code):
     from hierarchical_sparse_kv_verify_amd import KVHier, KVHierError

@@ -157,6 +157,37 @@ def test_mla_two_groups_two_steps(n_chunks, fetch_cus):
     pair.lib.close()
 
 
+def test_plan_shared_by_follower_layers():
+    """Follower-layer reuse of one plan: groups 0-1 and 2-3 each form a set fed
+    by one selection.  The leader resolves once and fetches for both layers;
+    the follower attends over its own payload through the leader's locations.
+    Every layer matches the oracle, which resolves each group on its own from
+    identical selections and warm sets, over two steps with a commit."""
+    from hierarchical_sparse_kv_verify_amd import KVHierError
+    w = _mla_small(n_groups=4, plan_share=2, n_arenas=2)
+    pair = build_pair(w)
+    n = pair.hist_len.copy()
+    for step in range(2):
+        sis = []
+        for g in range(w.n_groups):
+            si = make_step_inputs(w, g, step, n)
+            res = pair.orc.verify_step(g, si.topk, si.causal_pos, si.queries, si.block_rows, n_threads=8)
+            out = run_lib_step(pair, g, si)
+            compare_step(pair, g, si, res, out)
+            compare_counts(pair, g, res)
+            sis.append(si)
+        if step == 0:
+            # a follower whose leader has not stepped again is refused
+            with pytest.raises(KVHierError) as ei:
+                run_lib_step(pair, 1, sis[1])
+            assert ei.value.code == -4
+        acc = make_accepted(w, step, sis[0].k_active)
+        pair.orc.commit(acc)
+        pair.lib.commit(acc)
+        n = n + 1 + acc
+    pair.lib.close()
+
+
 def test_mla_128_heads_split_keys():
     """Two head groups of 64 and key splits merged by the combine pass."""
     w = _mla_small(n_req=2, n_groups=1, n_heads=128, q_max=4, topk=1024, ring_window=64,

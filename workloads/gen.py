@@ -61,6 +61,8 @@ class Workload:
     empty_slot_frac: float = 0.0
     var_k: bool = False       # draw K_r in [1, q_max] per request
     ring_prefill: bool = True  # load the W-1 committed positions below n_r into the ring
+    plan_share: int = 1       # payload layers per index producer: consecutive groups of this
+                              # size share one selection (and warm set / resident map)
     note: str = ""
 
     @property
@@ -118,7 +120,18 @@ def _mla512() -> Workload:
              "128 heads, Q=4, k=2048, B=2048, W=64")
 
 
-WORKLOADS = {w.name: w for w in (_tiny(), _mla32(), _mla128(), _mla128_res(), _mla512())}
+def _mla128_shared() -> Workload:
+    return dataclasses.replace(
+        _mla128(), name="mla128_shared", n_arenas=4, plan_share=4,
+        note="mla128 with its 4 layer groups fed by one index producer: one selection, "
+             "four payload layers (follower-layer reuse of one plan)")
+
+
+WORKLOADS = {w.name: w for w in (_tiny(), _mla32(), _mla128(), _mla128_res(), _mla512(), _mla128_shared())}
+
+
+def _leader(w: Workload, group: int) -> int:
+    return group - group % max(1, w.plan_share)
 
 
 def shrink(w: Workload, **kw) -> Workload:
@@ -238,6 +251,22 @@ def make_step_inputs(w: Workload, group: int, step: int, hist_len: np.ndarray,
     ``requests`` restricts generation to a subset (other rows of the outputs are
     left as pads / inactive), which the full-size parity tests use to sample."""
     N, Q, k = w.n_req, w.q_max, w.topk
+    if w.plan_share > 1:
+        # one selection per index producer; each payload layer has its own
+        # queries and new rows
+        lead = make_step_inputs(dataclasses.replace(w, plan_share=1), _leader(w, group), step, hist_len,
+                                k_active, requests)
+        if group == _leader(w, group):
+            return lead
+        rngs = _seeds(w, group, _P_STEP, step, 1, n=N)
+        queries = np.zeros_like(lead.queries)
+        block = np.zeros_like(lead.block_rows)
+        for r in (range(N) if requests is None else [int(x) for x in requests]):
+            for j in range(Q):
+                queries[r, j] = _normal_bf16(rngs[r], (w.n_heads, w.d_qk))
+                block[r, j] = _normal_bf16(rngs[r], (w.row_elems,))
+        return StepInputs(topk=lead.topk, causal_pos=lead.causal_pos, queries=queries, block_rows=block,
+                          k_active=lead.k_active, drawn=lead.drawn)
     rngs = _seeds(w, group, _P_STEP, step, n=N)
     topk = np.full((N, Q, k), -1, dtype=np.int32)
     causal = np.full((N, Q), -1, dtype=np.int32)
@@ -301,7 +330,7 @@ def make_hot_warm_set(w: Workload, group: int, hist_len: np.ndarray, step_in: St
     empty slots (-1).  Without a target: core rows plus undrawn filler.  Ages are
     uniform in {0..7}."""
     B = w.hot_slots
-    rngs = _seeds(w, group, _P_WARM, n=w.n_req)
+    rngs = _seeds(w, _leader(w, group), _P_WARM, n=w.n_req)
     out = [None] * w.n_req
     req_iter = range(w.n_req) if requests is None else [int(x) for x in requests]
     for r in req_iter:
@@ -337,7 +366,7 @@ def make_resident_bitmaps(w: Workload, group: int, hist_len: np.ndarray, rho: fl
     bm = np.zeros((w.n_req, w.hist_cap), dtype=np.uint8)
     if rho <= 0:
         return bm
-    rngs = _seeds(w, group, _P_RESIDENT, int(round(rho * 1000)), n=w.n_req)
+    rngs = _seeds(w, _leader(w, group), _P_RESIDENT, int(round(rho * 1000)), n=w.n_req)
     req_iter = range(w.n_req) if requests is None else [int(x) for x in requests]
     for r in req_iter:
         n_r = int(hist_len[r])
