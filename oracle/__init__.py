@@ -9,4 +9,5 @@ from .model import (  # noqa: F401
     HierOracle, OracleConfig, StepResult, loc_code, ring_addr, ring_rows, staging_bytes,
     to_bf16_bits,
 )
+from .residency import OptResidency  # noqa: F401
 from . import native  # noqa: F401

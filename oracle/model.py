@@ -46,6 +46,10 @@ Readings where the pages leave a step open (each marked READING below):
   R7 resident pool indices are handed out per layer group in call order of
      set_resident, ascending row order within a call.
   R8 the step counter of a group starts above every age given to set_hot.
+
+Dynamic optional residency (§3.1, eqs. 3-4) is modelled in ``residency.py``;
+once attached, its ready map (shared by every group) is what step (1) of the
+resolution order consults, in place of the static resident sets.
 """
 from __future__ import annotations
 
@@ -159,6 +163,7 @@ class HierOracle:
         self.res_cursor = [0] * cfg.n_groups
         self.r_d = ring_rows(cfg.ring_window, cfg.ring_page, cfg.q_max)
         self.last_k = {r: 0 for r in self.requests}
+        self.opt = None                                   # dynamic optional residency (residency.py)
         self.st = [{r: _Req(slot_row=[-1] * cfg.hot_slots, slot_lu=[0] * cfg.hot_slots,
                             slot_of={}, res_idx={}, ring={}, ring_lo=self.n[r])
                     for r in self.requests} for _ in range(cfg.n_groups)]
@@ -186,6 +191,8 @@ class HierOracle:
     def set_resident(self, g: int, r: int, bitmap):
         bm = np.asarray(bitmap)
         rows = [s for s in range(min(bm.size, self.n[r])) if bm[s]]
+        if self.opt is not None:
+            raise RuntimeError("static resident sets and dynamic residency do not mix")
         if r not in self.st[g]:                           # not modelled: only the cursor moves (R7)
             self.res_cursor[g] += len(rows)
             return
@@ -196,6 +203,19 @@ class HierOracle:
             st.res_idx[s] = self.res_cursor[g]
             self.res_cursor[g] += 1
         st.resident_set = True
+
+    def attach_residency(self, opt):
+        """Dynamic optional residency: the ready map of `opt` (shared by every
+        group) replaces the static resident sets."""
+        if any(st.resident_set for grp in self.st for st in grp.values()):
+            raise RuntimeError("static resident sets and dynamic residency do not mix")
+        self.opt = opt
+
+    def _resident(self, g: int, r: int, u: int):
+        """Resident pool row of history row u, or None (Figure 2 callout 1)."""
+        if self.opt is not None:
+            return self.opt.lookup(r, u)
+        return self.st[g][r].res_idx.get(u)
 
     def clear_resident(self, g: int):
         self.res_cursor[g] = 0
@@ -267,8 +287,11 @@ class HierOracle:
 
             # Figure 2 / §3.2: (1) direct map, (2) hot cache, (3) host; R3
             cls = {}
+            res_at = {}
             for u in U:
-                if u in st.res_idx:
+                ri = self._resident(g, r, u)
+                if ri is not None:
+                    res_at[u] = ri
                     cls[u] = CLS_RESIDENT
                 elif u in st.slot_of:
                     cls[u] = CLS_HOT
@@ -289,7 +312,7 @@ class HierOracle:
                     c = cls[e]
                     sel_cls[c] += 1
                     if c == CLS_RESIDENT:
-                        loc[j, i] = loc_code(RESIDENT, st.res_idx[e])
+                        loc[j, i] = loc_code(RESIDENT, res_at[e])
                     elif c == CLS_HOT:
                         loc[j, i] = loc_code(HOT, r * B + st.slot_of[e])
                     else:
