@@ -17,13 +17,13 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvhier.so")
 
-KV_OK, KV_EINVAL, KV_ENOMEM, KV_EHIP, KV_ESTATE, KV_EUNSUPPORTED = 0, -1, -2, -3, -4, -5
+KV_OK, KV_EINVAL, KV_ENOMEM, KV_EHIP, KV_ESTATE, KV_EUNSUPPORTED, KV_EWAIT = 0, -1, -2, -3, -4, -5, -6
 KV_TIER_HOT, KV_TIER_STAGED, KV_TIER_RESIDENT, KV_TIER_RING = 0, 1, 2, 3
 KV_FLAG_TIMING, KV_FLAG_POISON, KV_FLAG_TIMING_ATTN, KV_FLAG_SERIAL = 1, 2, 4, 8
 TIER_SHIFT = 29
 
 _ERRNAMES = {KV_EINVAL: "KV_EINVAL", KV_ENOMEM: "KV_ENOMEM", KV_EHIP: "KV_EHIP",
-             KV_ESTATE: "KV_ESTATE", KV_EUNSUPPORTED: "KV_EUNSUPPORTED"}
+             KV_ESTATE: "KV_ESTATE", KV_EUNSUPPORTED: "KV_EUNSUPPORTED", KV_EWAIT: "KV_EWAIT"}
 
 EXPORTED = [
     "kv_hier_create", "kv_hier_destroy", "kv_hier_last_error", "kv_hier_info_get",
@@ -31,7 +31,8 @@ EXPORTED = [
     "kv_hier_set_resident", "kv_hier_clear_resident", "kv_hier_ring_load",
     "kv_hier_verify_step", "kv_hier_commit", "kv_hier_stats", "kv_hier_reset_stats",
     "kv_hier_last_lists", "kv_hier_slot_table", "kv_hier_read_rows", "kv_hier_sync",
-    "kv_hier_set_flags", "kv_hier_cache_snapshot",
+    "kv_hier_set_flags", "kv_hier_cache_snapshot", "kv_hier_opt_admit", "kv_hier_opt_complete",
+    "kv_hier_opt_populate", "kv_hier_opt_publish", "kv_hier_opt_query",
 ]
 
 
@@ -47,7 +48,8 @@ class Config(ctypes.Structure):
         "d_qk", "v_off", "d_v", "n_heads", "q_max", "topk", "hot_slots", "ring_window",
         "ring_page", "ring_block_only", "n_chunks")] + [
         ("resident_cap", ctypes.c_int64), ("softmax_scale", ctypes.c_float), ("flags", ctypes.c_int32),
-        ("fetch_cus", ctypes.c_int32), ("fetch_wgs", ctypes.c_int32), ("plan_share", ctypes.c_int32)]
+        ("fetch_cus", ctypes.c_int32), ("fetch_wgs", ctypes.c_int32), ("plan_share", ctypes.c_int32),
+        ("opt_page_rows", ctypes.c_int32), ("opt_reserve", ctypes.c_int32)]
 
 
 COUNTER_FIELDS = ("calls", "active_requests", "active_queries", "selections", "pads", "invalid",
@@ -80,6 +82,19 @@ class Info(ctypes.Structure):
                [(n, ctypes.c_int64) for n in ("bytes_hot", "bytes_staging", "bytes_ring", "bytes_maps",
                                               "bytes_resident", "bytes_host")] + \
                [("attn_splits", ctypes.c_int32), ("attn_head_groups", ctypes.c_int32)]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+OPT_INFO_FIELDS = ("admitted", "required_pages", "held_pages", "ready_pages", "pending_pages", "free_pages",
+                   "eligible_pages", "pages_populated", "pages_published", "pages_reclaimed",
+                   "requests_reclaimed", "admissions_waited", "bytes_populated")
+
+
+class OptInfo(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("pool_pages", "page_rows", "reserve", "cursor")] + \
+               [(n, ctypes.c_int64) for n in OPT_INFO_FIELDS]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -129,6 +144,11 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "kv_hier_sync": ([vp], i32),
         "kv_hier_set_flags": ([vp, ctypes.c_int32], i32),
         "kv_hier_cache_snapshot": ([vp, i32, i32], i32),
+        "kv_hier_opt_admit": ([vp, i32, ctypes.c_int32, vp, i32, vp], i32),
+        "kv_hier_opt_complete": ([vp, i32], i32),
+        "kv_hier_opt_populate": ([vp, ctypes.c_int32, vp], i32),
+        "kv_hier_opt_publish": ([vp, i32], i32),
+        "kv_hier_opt_query": ([vp, i32, ctypes.c_int32, vp, vp, ctypes.POINTER(OptInfo)], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -170,7 +190,8 @@ class KVHier:
         self._lib = load_library()
         c = Config()
         defaults = dict(n_arenas=1, n_prefix=0, prefix_len=0, ring_block_only=0, n_chunks=0,
-                        resident_cap=0, softmax_scale=0.0, flags=0, fetch_cus=0, fetch_wgs=0, plan_share=0)
+                        resident_cap=0, softmax_scale=0.0, flags=0, fetch_cus=0, fetch_wgs=0, plan_share=0,
+                        opt_page_rows=0, opt_reserve=0)
         defaults.update(cfg)
         for name, _ in Config._fields_:
             if name not in defaults:
@@ -311,6 +332,42 @@ class KVHier:
 
     def restore_cache(self, g: int):
         self._check(self._lib.kv_hier_cache_snapshot(self._h, g, 1))
+
+    # -------------------------------------------------------------- dynamic optional residency
+    def opt_admit(self, r: int, required_pages: int, order=()):
+        """Returns the number of reclaimed requests, or None when the
+        admission has to wait (KV_EWAIT)."""
+        o = _i32(list(order))
+        q = ctypes.c_int32(0)
+        rc = self._lib.kv_hier_opt_admit(self._h, r, int(required_pages), o.ctypes.data if o.size else None,
+                                         o.size, ctypes.byref(q))
+        if rc == KV_EWAIT:
+            return None
+        self._check(rc)
+        return q.value
+
+    def opt_complete(self, r: int):
+        self._check(self._lib.kv_hier_opt_complete(self._h, r))
+
+    def opt_populate(self, max_pages: int) -> int:
+        n = ctypes.c_int32(0)
+        self._check(self._lib.kv_hier_opt_populate(self._h, int(max_pages), ctypes.byref(n)))
+        return n.value
+
+    def opt_publish(self, wait: bool = False):
+        self._check(self._lib.kv_hier_opt_publish(self._h, 1 if wait else 0))
+
+    def opt_info(self) -> dict:
+        inf = OptInfo()
+        self._check(self._lib.kv_hier_opt_query(self._h, -1, 0, None, None, ctypes.byref(inf)))
+        return inf.as_dict()
+
+    def opt_pages(self, r: int, n_pages: int):
+        """Pool page held for each page index of request r (-1 none) and its ready flag."""
+        held = np.zeros(n_pages, np.int32)
+        ready = np.zeros(n_pages, np.uint8)
+        self._check(self._lib.kv_hier_opt_query(self._h, r, n_pages, held.ctypes.data, ready.ctypes.data, None))
+        return held, ready
 
 
 def loc_code(tier: int, index: int) -> int:

@@ -85,6 +85,15 @@ hipError_t launch_read_rows(const PoolView& pv, const int32_t* locs, int n, uint
                             hipStream_t s);
 // a follower layer's counters: dst[r][c] = src[r][c]; cum[c] += sum_r src[r][c]
 hipError_t launch_counts_follow(const int64_t* src, int64_t* dst, unsigned long long* cum, int N, hipStream_t s);
+// dynamic optional residency: one descriptor per group; a page list holds
+// (request, page index, pool page) triples
+struct OptGroup { HostRowSrc src; uint4* pool; int32_t* res_map; };
+// pool rows of every listed page in every group <- host rows idx*P .. idx*P+P-1 of the request
+hipError_t launch_opt_copy(const OptGroup* groups, int G, const int32_t* list, int n, int P, int row16, int wgs,
+                           hipStream_t s);
+// res_map of every group: rows of every listed page -> pool*P + i (publish) or -1 (withdraw)
+hipError_t launch_opt_map(const OptGroup* groups, int G, const int32_t* list, int n, int P, int L, int publish,
+                          hipStream_t s);
 // fill 32-bit words with a value (used instead of memset inside the step)
 hipError_t launch_fill32(uint32_t* p, uint32_t v, size_t n, hipStream_t s);
 

@@ -13,6 +13,8 @@
 //    phi(r, p) = r*R_d + (p mod R_d) (eq. 10; Figure 3 callout 4).
 //  - commit: committed ring rows get their host copy (eq. 7 and the text
 //    after eq. 8: host backup of committed rows follows verification).
+//  - optional-history population and its publication in the resident map
+//    (§3.1: reserve pages, copy their rows, publish after the copy).
 // Loop bounds come from device-side counts, so no host round trip is needed
 // between resolution and movement.
 #include "common.h"
@@ -149,6 +151,43 @@ __global__ __launch_bounds__(256) void counts_follow_kernel(const int64_t* __res
   }
 }
 
+// Population of optional history ("Adaptive DHiSparse" §3.1): the rows of
+// each listed page, for every group, from pinned host memory into the group's
+// pool page.  Flattened over (page, group, row, 16-byte chunk) so consecutive
+// lanes read consecutive chunks of one host row; one-wave workgroups, as for
+// the miss fetch, keep the reads spread thinly beside concurrent steps.
+__global__ __launch_bounds__(64) void opt_copy_kernel(const OptGroup* __restrict__ groups,
+                                                      const int32_t* __restrict__ list, int n, int G, int P,
+                                                      int row16) {
+  const size_t per_page = size_t(P) * row16;
+  const size_t total = size_t(n) * G * per_page;
+  const size_t stride = size_t(gridDim.x) * blockDim.x;
+  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const size_t eg = i / per_page;
+    const int w = static_cast<int>(i - eg * per_page);
+    const int e = static_cast<int>(eg / G), g = static_cast<int>(eg - size_t(e) * G);
+    const int row = w / row16, c = w - row * row16;
+    const int r = list[3 * e], idx = list[3 * e + 1], page = list[3 * e + 2];
+    const OptGroup& og = groups[g];
+    og.pool[(size_t(page) * P + row) * row16 + c] = host_row(og.src, r, idx * P + row)[c];
+  }
+}
+
+// Publication (or withdrawal) of listed pages in every group's resident map.
+__global__ __launch_bounds__(256) void opt_map_kernel(const OptGroup* __restrict__ groups,
+                                                     const int32_t* __restrict__ list, int n, int G, int P, int L,
+                                                     int publish) {
+  const size_t total = size_t(n) * G * P;
+  const size_t stride = size_t(gridDim.x) * blockDim.x;
+  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const size_t eg = i / P;
+    const int row = static_cast<int>(i - eg * P);
+    const int e = static_cast<int>(eg / G), g = static_cast<int>(eg - size_t(e) * G);
+    const int r = list[3 * e], idx = list[3 * e + 1], page = list[3 * e + 2];
+    groups[g].res_map[size_t(r) * L + size_t(idx) * P + row] = publish ? page * P + row : -1;
+  }
+}
+
 __global__ __launch_bounds__(256) void fill32_kernel(uint32_t* p, uint32_t v, size_t n) {
   const size_t stride = size_t(gridDim.x) * blockDim.x;
   for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = v;
@@ -212,6 +251,25 @@ hipError_t launch_read_rows(const PoolView& pv, const int32_t* locs, int n, uint
 
 hipError_t launch_counts_follow(const int64_t* src, int64_t* dst, unsigned long long* cum, int N, hipStream_t s) {
   hipLaunchKernelGGL(counts_follow_kernel, dim3(1), dim3(256), 0, s, src, dst, cum, N);
+  return hipGetLastError();
+}
+
+hipError_t launch_opt_copy(const OptGroup* groups, int G, const int32_t* list, int n, int P, int row16, int wgs,
+                           hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const size_t work = size_t(n) * G * P * row16;
+  size_t grid = (work + 63) / 64;
+  if (grid > size_t(wgs)) grid = size_t(wgs);
+  hipLaunchKernelGGL(opt_copy_kernel, dim3(static_cast<unsigned>(grid)), dim3(64), 0, s, groups, list, n, G, P,
+                     row16);
+  return hipGetLastError();
+}
+
+hipError_t launch_opt_map(const OptGroup* groups, int G, const int32_t* list, int n, int P, int L, int publish,
+                          hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(opt_map_kernel, dim3(grid_for(size_t(n) * G * P, 1024)), dim3(256), 0, s, groups, list, n, G,
+                     P, L, publish);
   return hipGetLastError();
 }
 

@@ -17,11 +17,22 @@
 // released once both its attention and its copy-back are done; the group's
 // next attention waits for this step's copy-backs.
 // No host synchronisation happens inside a step.
+//
+// Dynamic optional residency (§3.1, eqs. 3-4) keeps its bookkeeping on the
+// host: admission, reclaim and round-robin population are host decisions; the
+// page copies run on a fourth stream beside the steps, and the resident maps
+// change only through small map kernels on the side stream, so every plan
+// sees the maps as of its own place in that stream.  A page is published
+// once its copy's event has completed (checked without waiting at the first
+// group's step); a reclaimed page is withdrawn at once and rewritten only
+// after the attention of every earlier step.
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <deque>
+#include <set>
 #include <string>
 #include <vector>
 
@@ -73,6 +84,45 @@ struct Timed {
   hipEvent_t a, b;
 };
 
+// pinned host page list handed to a stream (reusable once its event completes)
+struct ListBuf {
+  int32_t* host = nullptr;
+  size_t cap = 0;
+  hipEvent_t ev = nullptr;
+  bool busy = false;
+};
+
+enum PageState : char { PG_FREE = 0, PG_PENDING = 1, PG_READY = 2 };
+
+// Host bookkeeping of dynamic optional residency (one per handle: a page index
+// addresses the same page in every group's pool).
+struct Opt {
+  bool on = false;
+  int P = 0, M = 0, reserve = 0, cursor = 0;
+  int64_t sum_req = 0, sum_held = 0, n_published = 0;
+  std::vector<char> admitted;
+  std::vector<int32_t> required, eligible, n_held, n_ready;
+  std::vector<std::vector<int32_t>> held;     // [r][page index] -> pool page (pages fill ascending)
+  std::vector<char> state, needs_wait;        // per pool page
+  std::vector<uint32_t> gen;                  // per pool page: bumped at every reservation
+  std::set<int32_t> free;                     // lowest first
+  struct Batch {
+    hipEvent_t ev;
+    std::vector<int32_t> ent;                 // (request, page index, pool page, gen) per page
+  };
+  std::deque<Batch> pending;
+  hipStream_t stream = nullptr;               // population copies
+  hipEvent_t ev_unpub = nullptr;              // last withdrawal from the maps (side stream)
+  bool unpub_recorded = false;
+  int32_t* d_list_side = nullptr;             // page lists on the device, one per stream
+  int32_t* d_list_copy = nullptr;
+  OptGroup* d_groups = nullptr;
+  std::vector<ListBuf> bufs;
+  std::vector<hipEvent_t> ev_pool;
+  int64_t pages_populated = 0, pages_published = 0, pages_reclaimed = 0, requests_reclaimed = 0,
+          admissions_waited = 0, bytes_populated = 0;
+};
+
 }  // namespace
 
 struct kv_hier {
@@ -107,6 +157,7 @@ struct kv_hier {
   CommitGroup* d_commit_groups = nullptr;
   std::vector<Timed> pending;
   std::vector<hipEvent_t> pool;
+  Opt opt;
   std::string err;
   int64_t bytes_hot = 0, bytes_staging = 0, bytes_ring = 0, bytes_maps = 0, bytes_res = 0, bytes_host = 0;
 };
@@ -339,6 +390,18 @@ void free_all(kv_hier* h) {
   if (h->ev_resolved) (void)hipEventDestroy(h->ev_resolved);
   if (h->side) (void)hipStreamDestroy(h->side);
   if (h->aux) (void)hipStreamDestroy(h->aux);
+  Opt& o = h->opt;
+  for (auto& b : o.pending) (void)hipEventDestroy(b.ev);
+  for (hipEvent_t e : o.ev_pool) (void)hipEventDestroy(e);
+  for (ListBuf& b : o.bufs) {
+    if (b.host) (void)hipHostFree(b.host);
+    if (b.ev) (void)hipEventDestroy(b.ev);
+  }
+  (void)hipFree(o.d_list_side);
+  (void)hipFree(o.d_list_copy);
+  (void)hipFree(o.d_groups);
+  if (o.ev_unpub) (void)hipEventDestroy(o.ev_unpub);
+  if (o.stream) (void)hipStreamDestroy(o.stream);
 }
 
 // Ring size of "Adaptive DHiSparse" §3.4 eq. (9): page-rounded window plus block.
@@ -348,7 +411,8 @@ int validate(kv_hier* h, const kv_hier_config& c) {
   if (c.n_req <= 0 || c.n_groups <= 0 || c.n_arenas <= 0 || c.hist_cap <= 0 || c.row_elems <= 0 ||
       c.d_qk <= 0 || c.d_v <= 0 || c.v_off < 0 || c.n_heads <= 0 || c.q_max <= 0 || c.topk <= 0 ||
       c.hot_slots <= 0 || c.ring_window <= 0 || c.ring_page <= 0 || c.n_prefix < 0 || c.prefix_len < 0 ||
-      c.n_chunks < 0 || c.resident_cap < 0 || c.fetch_cus < 0 || c.fetch_wgs < 0 || c.plan_share < 0)
+      c.n_chunks < 0 || c.resident_cap < 0 || c.fetch_cus < 0 || c.fetch_wgs < 0 || c.plan_share < 0 ||
+      c.opt_page_rows < 0 || c.opt_reserve < 0)
     return fail(h, KV_EINVAL, "non-positive size in config");
   if (c.q_max > 32) return fail(h, KV_EUNSUPPORTED, "q_max %d > 32", c.q_max);
   if (int64_t(c.q_max) * c.topk > 65535) return fail(h, KV_EUNSUPPORTED, "q_max*topk > 65535");
@@ -369,7 +433,134 @@ int validate(kv_hier* h, const kv_hier_config& c) {
     return fail(h, KV_EINVAL, "n_groups %d is not a multiple of plan_share %d", c.n_groups, c.plan_share);
   if (c.plan_share > 1 && c.n_arenas < c.plan_share)
     return fail(h, KV_EINVAL, "plan_share %d needs as many arenas (n_arenas %d)", c.plan_share, c.n_arenas);
+  if (c.opt_page_rows > 0 &&
+      (c.resident_cap <= 0 || c.resident_cap % c.opt_page_rows != 0 || c.opt_page_rows > c.hist_cap))
+    return fail(h, KV_EINVAL, "dynamic residency needs resident_cap a positive multiple of opt_page_rows <= hist_cap");
   return KV_OK;
+}
+
+// ---------------------------------------------------------------- optional residency helpers
+
+// A pinned page list of n int32 for one stream use; *out receives its index.
+int take_list(kv_hier* h, size_t n, int* out) {
+  Opt& o = h->opt;
+  for (size_t i = 0; i < o.bufs.size(); ++i) {
+    ListBuf& b = o.bufs[i];
+    if (b.busy) {
+      const hipError_t q = hipEventQuery(b.ev);
+      if (q == hipErrorNotReady) continue;
+      if (q != hipSuccess) return fail(h, KV_EHIP, "list event: %s", hipGetErrorString(q));
+      b.busy = false;
+    }
+    if (b.cap >= n) {
+      *out = int(i);
+      return KV_OK;
+    }
+  }
+  ListBuf b;
+  b.cap = std::max<size_t>(n, 4096);
+  void* p = nullptr;
+  if (hipHostMalloc(&p, b.cap * 4, hipHostMallocDefault) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(h, KV_ENOMEM, "pinned page list of %zu entries", b.cap);
+  }
+  b.host = static_cast<int32_t*>(p);
+  if (hipEventCreateWithFlags(&b.ev, hipEventDisableTiming) != hipSuccess) {
+    (void)hipHostFree(p);
+    return fail(h, KV_EHIP, "event create failed");
+  }
+  o.bufs.push_back(b);
+  *out = int(o.bufs.size()) - 1;
+  return KV_OK;
+}
+
+// Moves a (request, page, pool page) list to the stream's device list buffer.
+int stage_list(kv_hier* h, const std::vector<int32_t>& ent, int32_t* dev, hipStream_t s) {
+  int bi = -1;
+  int rc = take_list(h, ent.size(), &bi);
+  if (rc) return rc;
+  ListBuf& b = h->opt.bufs[bi];
+  std::memcpy(b.host, ent.data(), ent.size() * 4);
+  HIPCHK(h, hipMemcpyAsync(dev, b.host, ent.size() * 4, hipMemcpyHostToDevice, s));
+  HIPCHK(h, hipEventRecord(b.ev, s));
+  b.busy = true;
+  return KV_OK;
+}
+
+// Publication (publish = 1) or withdrawal of pages in every group's resident
+// map, on the side stream: ordered before every later plan.
+int opt_map(kv_hier* h, const std::vector<int32_t>& ent, int publish) {
+  if (ent.empty()) return KV_OK;
+  Opt& o = h->opt;
+  int rc = stage_list(h, ent, o.d_list_side, h->side);
+  if (rc) return rc;
+  HIPCHK(h, launch_opt_map(o.d_groups, h->cfg.n_groups, o.d_list_side, int(ent.size() / 3), o.P, h->L, publish,
+                           h->side));
+  if (!publish) {
+    HIPCHK(h, hipEventRecord(o.ev_unpub, h->side));
+    o.unpub_recorded = true;
+  }
+  return KV_OK;
+}
+
+// Publishes every pending page whose copy has completed (all of them, waiting,
+// when wait is set).  Batches complete in order: they share one stream.
+int opt_publish_impl(kv_hier* h, bool wait) {
+  Opt& o = h->opt;
+  std::vector<int32_t> pub;
+  while (!o.pending.empty()) {
+    Opt::Batch& b = o.pending.front();
+    if (wait) {
+      HIPCHK(h, hipEventSynchronize(b.ev));
+    } else {
+      const hipError_t q = hipEventQuery(b.ev);
+      if (q == hipErrorNotReady) break;
+      if (q != hipSuccess) return fail(h, KV_EHIP, "population event: %s", hipGetErrorString(q));
+    }
+    for (size_t i = 0; i + 4 <= b.ent.size(); i += 4) {
+      const int32_t r = b.ent[i], idx = b.ent[i + 1], pg = b.ent[i + 2];
+      const uint32_t gen = uint32_t(b.ent[i + 3]);
+      // a page reclaimed while its copy ran is not published (its owner changed)
+      if (o.gen[pg] != gen || o.state[pg] != PG_PENDING) continue;
+      o.state[pg] = PG_READY;
+      o.n_ready[r] += 1;
+      pub.push_back(r);
+      pub.push_back(idx);
+      pub.push_back(pg);
+    }
+    o.ev_pool.push_back(b.ev);
+    o.pending.pop_front();
+  }
+  if (pub.empty()) return KV_OK;
+  o.n_published += int64_t(pub.size() / 3);
+  o.pages_published += int64_t(pub.size() / 3);
+  return opt_map(h, pub, 1);
+}
+
+// Drops every optional page of request r (reclaim or completion): ready pages
+// are withdrawn from the maps now and marked to be rewritten only after the
+// readers of earlier steps; pending pages are simply never published.
+int opt_drop(kv_hier* h, int r) {
+  Opt& o = h->opt;
+  std::vector<int32_t> wd;
+  for (int idx = 0; idx < o.n_held[r]; ++idx) {
+    const int32_t pg = o.held[r][idx];
+    if (o.state[pg] == PG_READY) {
+      wd.push_back(r);
+      wd.push_back(idx);
+      wd.push_back(pg);
+      o.needs_wait[pg] = 1;
+      o.n_published -= 1;
+    }
+    o.state[pg] = PG_FREE;
+    o.free.insert(pg);
+    o.held[r][idx] = -1;
+  }
+  o.pages_reclaimed += o.n_held[r];
+  o.sum_held -= o.n_held[r];
+  o.n_held[r] = 0;
+  o.n_ready[r] = 0;
+  return opt_map(h, wd, 0);
 }
 
 }  // namespace
@@ -519,6 +710,40 @@ static int create_impl(kv_hier* h) {
   if ((rc = dev_alloc(h, &h->zero_row, size_t(c.row_elems), &h->bytes_maps))) return rc;
   if (launch_fill32(reinterpret_cast<uint32_t*>(h->zero_row), 0, size_t(c.row_elems) / 2, nullptr) != hipSuccess)
     return fail(h, KV_EHIP, "zero row fill failed");
+  if (c.opt_page_rows > 0) {
+    Opt& o = h->opt;
+    o.on = true;
+    o.P = c.opt_page_rows;
+    o.M = int(c.resident_cap / c.opt_page_rows);
+    o.reserve = c.opt_reserve;
+    o.admitted.assign(N, 0);
+    o.required.assign(N, 0);
+    o.eligible.assign(N, 0);
+    o.n_held.assign(N, 0);
+    o.n_ready.assign(N, 0);
+    o.held.assign(N, {});
+    o.state.assign(o.M, PG_FREE);
+    o.needs_wait.assign(o.M, 0);
+    o.gen.assign(o.M, 0);
+    for (int i = 0; i < o.M; ++i) o.free.insert(o.free.end(), i);
+    std::vector<OptGroup> og(c.n_groups);
+    for (int g = 0; g < c.n_groups; ++g) {
+      og[g].src = host_src(h, h->grp[g]);
+      og[g].pool = reinterpret_cast<uint4*>(h->grp[g].resident);
+      og[g].res_map = h->grp[g].res_map;
+      // debug: a page read before its copy completes shows up as NaN
+      if ((c.flags & KV_FLAG_POISON) &&
+          launch_fill32(reinterpret_cast<uint32_t*>(h->grp[g].resident), 0x7fc07fc0u,
+                        size_t(c.resident_cap) * c.row_elems / 2, nullptr) != hipSuccess)
+        return fail(h, KV_EHIP, "pool poison fill failed");
+    }
+    if ((rc = dev_alloc(h, &o.d_groups, og.size(), nullptr))) return rc;
+    if ((rc = upload(h, o.d_groups, og.data(), og.size() * sizeof(OptGroup)))) return rc;
+    if ((rc = dev_alloc(h, &o.d_list_side, size_t(o.M) * 3, &h->bytes_maps))) return rc;
+    if ((rc = dev_alloc(h, &o.d_list_copy, size_t(o.M) * 3, &h->bytes_maps))) return rc;
+    HIPCHK(h, hipStreamCreateWithFlags(&o.stream, hipStreamNonBlocking));
+    HIPCHK(h, hipEventCreateWithFlags(&o.ev_unpub, hipEventDisableTiming));
+  }
   {
     std::vector<CommitGroup> cg(c.n_groups);
     for (int g = 0; g < c.n_groups; ++g) {
@@ -630,6 +855,10 @@ int kv_hier_set_hist_len(kv_hier_t* h, const int32_t* hist_len) {
   for (int r = 0; r < h->cfg.n_req; ++r)
     if (hist_len[r] < 0 || hist_len[r] > h->cfg.hist_cap)
       return fail(h, KV_EINVAL, "hist_len[%d] = %d outside [0, %d]", r, hist_len[r], h->cfg.hist_cap);
+  if (h->opt.on)
+    for (int r = 0; r < h->cfg.n_req; ++r)
+      if (h->opt.admitted[r])
+        return fail(h, KV_ESTATE, "request %d is admitted: its imported history is fixed until completion", r);
   int rc = sync_all(h);
   if (rc) return rc;
   h->hist_len.assign(hist_len, hist_len + h->cfg.n_req);
@@ -698,6 +927,7 @@ int kv_hier_set_resident(kv_hier_t* h, int g, int r, const uint8_t* bitmap) {
   if (rc) return rc;
   if ((rc = check_req(h, r))) return rc;
   if (!bitmap) return fail(h, KV_EINVAL, "null bitmap");
+  if (h->opt.on) return fail(h, KV_ESTATE, "static resident sets are not used with dynamic residency");
   Group& G = h->grp[g];
   if (G.res_set[r]) return fail(h, KV_ESTATE, "resident set of request %d already given", r);
   const int lim = std::min(h->hist_len[r], h->L);
@@ -725,6 +955,7 @@ int kv_hier_set_resident(kv_hier_t* h, int g, int r, const uint8_t* bitmap) {
 int kv_hier_clear_resident(kv_hier_t* h, int g) {
   int rc = check_group(h, g);
   if (rc) return rc;
+  if (h->opt.on) return fail(h, KV_ESTATE, "static resident sets are not used with dynamic residency");
   if ((rc = sync_all(h))) return rc;
   Group& G = h->grp[g];
   HIPCHK(h, launch_fill32(reinterpret_cast<uint32_t*>(G.res_map), 0xffffffffu, size_t(h->cfg.n_req) * h->L, nullptr));
@@ -796,12 +1027,15 @@ int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t*
     // resolution plan and host fetch on the side stream (no event hop between
     // them), after the caller's prior work; the ring write runs beside the plan
     HIPCHK(h, hipStreamWaitEvent(h->side, h->ev_in, 0));
+    // optional-history pages whose copies have completed become ready for
+    // this step's resolution (the first group's step is the step boundary)
+    if (g == 0 && h->opt.on && (rc = opt_publish_impl(h, false))) return rc;
 
     PlanArgs pa;
     pa.topk = topk_idx;
     pa.causal = causal_pos;
     pa.res_map = G.res_map;
-    pa.has_resident = G.res_cursor > 0 ? 1 : 0;
+    pa.has_resident = (h->opt.on ? h->opt.n_published > 0 : G.res_cursor > 0) ? 1 : 0;
     pa.slot_map = G.slot_map;
     pa.slot_row = G.slot_row;
     pa.slot_lu = G.slot_lu;
@@ -1148,6 +1382,175 @@ int kv_hier_cache_snapshot(kv_hier_t* h, int g, int op) {
     G.t = G.snap_t;
   }
   HIPCHK(h, hipDeviceSynchronize());
+  return KV_OK;
+}
+
+// ---------------------------------------------------------------- dynamic optional residency
+
+int kv_hier_opt_admit(kv_hier_t* h, int r, int32_t required_pages, const int32_t* order, int n_order,
+                      int32_t* n_reclaimed) {
+  if (!h) return KV_EINVAL;
+  Opt& o = h->opt;
+  if (!o.on) return fail(h, KV_ESTATE, "dynamic residency is off (opt_page_rows = 0)");
+  int rc = check_req(h, r);
+  if (rc) return rc;
+  if (o.admitted[r]) return fail(h, KV_ESTATE, "request %d is already admitted", r);
+  if (required_pages < 0 || n_order < 0 || (n_order > 0 && !order))
+    return fail(h, KV_EINVAL, "bad admission arguments");
+  std::vector<char> seen(h->cfg.n_req, 0);
+  for (int i = 0; i < n_order; ++i) {
+    const int x = order[i];
+    if (x < 0 || x >= h->cfg.n_req || !o.admitted[x] || seen[x])
+      return fail(h, KV_EINVAL, "reclaim order entry %d (%d) is not a distinct admitted request", i, x);
+    seen[x] = 1;
+  }
+  // eq. (3): required + optional + reserve <= M; eq. (4): the first q of the
+  // reclaim order whose optional pages cover the deficit
+  const int64_t deficit = o.sum_req + required_pages + o.sum_held + o.reserve - int64_t(o.M);
+  int q = 0;
+  if (deficit > 0) {
+    int64_t covered = 0;
+    while (q < n_order && covered < deficit) covered += o.n_held[order[q++]];
+    if (covered < deficit) {
+      o.admissions_waited += 1;
+      return fail(h, KV_EWAIT, "admission of request %d waits: deficit %lld pages, reclaimable %lld", r,
+                  (long long)deficit, (long long)covered);
+    }
+  }
+  for (int i = 0; i < q; ++i)
+    if ((rc = opt_drop(h, order[i]))) return rc;
+  o.requests_reclaimed += q;
+  o.admitted[r] = 1;
+  o.required[r] = required_pages;
+  o.sum_req += required_pages;
+  o.eligible[r] = std::min(h->hist_len[r], h->L) / o.P;   // complete imported pages
+  o.held[r].assign(o.eligible[r], -1);
+  o.n_held[r] = 0;
+  o.n_ready[r] = 0;
+  if (n_reclaimed) *n_reclaimed = q;
+  return KV_OK;
+}
+
+int kv_hier_opt_complete(kv_hier_t* h, int r) {
+  if (!h) return KV_EINVAL;
+  Opt& o = h->opt;
+  if (!o.on) return fail(h, KV_ESTATE, "dynamic residency is off (opt_page_rows = 0)");
+  int rc = check_req(h, r);
+  if (rc) return rc;
+  if (!o.admitted[r]) return fail(h, KV_ESTATE, "request %d is not admitted", r);
+  if ((rc = opt_drop(h, r))) return rc;
+  o.admitted[r] = 0;
+  o.sum_req -= o.required[r];
+  o.required[r] = 0;
+  o.eligible[r] = 0;
+  o.held[r].clear();
+  return KV_OK;
+}
+
+int kv_hier_opt_populate(kv_hier_t* h, int32_t max_pages, int32_t* n_assigned) {
+  if (!h) return KV_EINVAL;
+  Opt& o = h->opt;
+  if (!o.on) return fail(h, KV_ESTATE, "dynamic residency is off (opt_page_rows = 0)");
+  if (max_pages < 0) return fail(h, KV_EINVAL, "negative page bound");
+  const int N = h->cfg.n_req;
+  const int64_t budget = int64_t(o.M) - o.sum_req - o.reserve - o.sum_held;
+  const int64_t limit = std::min<int64_t>(max_pages, std::max<int64_t>(0, budget));
+  std::vector<int32_t> ent, copy;
+  bool wait = false;
+  int r = o.cursor, idle = 0;
+  int64_t n = 0;
+  while (n < limit && idle < N) {
+    if (o.admitted[r] && o.n_held[r] < o.eligible[r]) {
+      const int idx = o.n_held[r];          // held pages always form a prefix 0 .. n_held-1
+      const int32_t pg = *o.free.begin();
+      o.free.erase(o.free.begin());
+      o.held[r][idx] = pg;
+      o.n_held[r] += 1;
+      o.state[pg] = PG_PENDING;
+      o.gen[pg] += 1;
+      if (o.needs_wait[pg]) { wait = true; o.needs_wait[pg] = 0; }
+      ent.insert(ent.end(), {r, idx, pg, int32_t(o.gen[pg])});
+      copy.insert(copy.end(), {r, idx, pg});
+      ++n;
+      idle = 0;
+    } else {
+      ++idle;
+    }
+    r = (r + 1) % N;
+  }
+  o.cursor = r;
+  o.sum_held += n;
+  if (n_assigned) *n_assigned = int32_t(n);
+  if (n == 0) return KV_OK;
+  if (wait) {
+    // pages withdrawn from the maps: rewrite them only after the withdrawal and
+    // after the attention of every step issued so far (their last readers)
+    if (o.unpub_recorded) HIPCHK(h, hipStreamWaitEvent(o.stream, o.ev_unpub, 0));
+    for (Group& G : h->grp)
+      if (G.done_recorded) HIPCHK(h, hipStreamWaitEvent(o.stream, G.ev_done, 0));
+  }
+  int rc = stage_list(h, copy, o.d_list_copy, o.stream);
+  if (rc) return rc;
+  HIPCHK(h, launch_opt_copy(o.d_groups, h->cfg.n_groups, o.d_list_copy, int(n), o.P, h->row16, 128, o.stream));
+  Opt::Batch b;
+  if (!o.ev_pool.empty()) {
+    b.ev = o.ev_pool.back();
+    o.ev_pool.pop_back();
+  } else {
+    HIPCHK(h, hipEventCreateWithFlags(&b.ev, hipEventDisableTiming));
+  }
+  HIPCHK(h, hipEventRecord(b.ev, o.stream));
+  b.ent = std::move(ent);
+  o.pending.push_back(std::move(b));
+  o.pages_populated += n;
+  o.bytes_populated += n * o.P * int64_t(h->row_bytes) * h->cfg.n_groups;
+  return KV_OK;
+}
+
+int kv_hier_opt_publish(kv_hier_t* h, int wait) {
+  if (!h) return KV_EINVAL;
+  if (!h->opt.on) return fail(h, KV_ESTATE, "dynamic residency is off (opt_page_rows = 0)");
+  if (wait != 0 && wait != 1) return fail(h, KV_EINVAL, "wait must be 0 or 1");
+  return opt_publish_impl(h, wait == 1);
+}
+
+int kv_hier_opt_query(kv_hier_t* h, int r, int32_t n_pages, int32_t* held, uint8_t* ready,
+                      kv_hier_opt_info* info) {
+  if (!h) return KV_EINVAL;
+  const Opt& o = h->opt;
+  if (!o.on) return fail(h, KV_ESTATE, "dynamic residency is off (opt_page_rows = 0)");
+  if (info) {
+    std::memset(info, 0, sizeof *info);
+    info->pool_pages = o.M;
+    info->page_rows = o.P;
+    info->reserve = o.reserve;
+    info->cursor = o.cursor;
+    for (int x = 0; x < h->cfg.n_req; ++x) {
+      info->admitted += o.admitted[x] ? 1 : 0;
+      info->ready_pages += o.n_ready[x];
+      info->eligible_pages += o.admitted[x] ? o.eligible[x] : 0;
+    }
+    info->required_pages = o.sum_req;
+    info->held_pages = o.sum_held;
+    info->pending_pages = o.sum_held - info->ready_pages;
+    info->free_pages = int64_t(o.free.size());
+    info->pages_populated = o.pages_populated;
+    info->pages_published = o.pages_published;
+    info->pages_reclaimed = o.pages_reclaimed;
+    info->requests_reclaimed = o.requests_reclaimed;
+    info->admissions_waited = o.admissions_waited;
+    info->bytes_populated = o.bytes_populated;
+  }
+  if (r >= 0) {
+    int rc = check_req(h, r);
+    if (rc) return rc;
+    if (n_pages < 0) return fail(h, KV_EINVAL, "negative page count");
+    for (int i = 0; i < n_pages; ++i) {
+      const int32_t pg = (i < int(o.held[r].size())) ? o.held[r][i] : -1;
+      if (held) held[i] = pg;
+      if (ready) ready[i] = (pg >= 0 && o.state[pg] == PG_READY) ? 1 : 0;
+    }
+  }
   return KV_OK;
 }
 

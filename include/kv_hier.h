@@ -24,6 +24,11 @@
  *     are copied back to their hot-cache slots.
  *   - §3.5 eqs. (11)-(12): every list entry gets a location l with
  *     KV[l] = c_{r,s}; a row held in two tiers resolves to one of them.
+ *   - §3.1 eqs. (3)-(4) ("Load-Adaptive Residency"): optional history in
+ *     reclaimable pages of the device pool; admission reclaims whole requests
+ *     in the runtime's reclaim order until their pages cover the deficit;
+ *     bounded round-robin repopulation; locations are published as ready
+ *     only after their copies complete (kv_hier_opt_*).
  *
  * Conventions
  *   - Every call returns KV_OK (0) or a negative KV_E* code; no exception
@@ -54,7 +59,8 @@ enum {
   KV_ENOMEM = -2,        /* device or pinned host allocation failed      */
   KV_EHIP = -3,          /* a HIP runtime call failed                    */
   KV_ESTATE = -4,        /* call not valid in the current state          */
-  KV_EUNSUPPORTED = -5   /* shape outside what the kernels are built for */
+  KV_EUNSUPPORTED = -5,  /* shape outside what the kernels are built for */
+  KV_EWAIT = -6          /* admission must wait (eq. 4): nothing changed  */
 };
 
 enum { KV_TIER_HOT = 0, KV_TIER_STAGED = 1, KV_TIER_RESIDENT = 2, KV_TIER_RING = 3 };
@@ -108,6 +114,13 @@ typedef struct {
                                of a set must be given identical set_hot / set_resident
                                contents (their own payload rows).  0 or 1: one plan per
                                group.                                                    */
+  int32_t opt_page_rows;    /* > 0: dynamic optional residency (kv_hier_opt_*): the resident
+                               pool of every group is resident_cap / opt_page_rows pages of
+                               this many rows (resident_cap a multiple of it); one page index
+                               addresses the same page in every group's pool.  Static
+                               resident sets (kv_hier_set_resident) are then refused.
+                               0: static resident sets only.                             */
+  int32_t opt_reserve;      /* M_res of eq. (3), in pages (dynamic residency)            */
 } kv_hier_config;
 
 /* Counters of one layer group (kv_hier_stats).  "union_*" count distinct rows
@@ -185,7 +198,7 @@ int kv_hier_set_hist_len(kv_hier_t *h, const int32_t *hist_len);
  * are copied from the host backing.  Synchronous. */
 int kv_hier_set_hot(kv_hier_t *h, int g, int r, const int32_t *rows, const int32_t *last_used, int n);
 
-/* Ready optional history of (g, r) (§3.1): host uint8[hist_cap] bitmap; rows
+/* Static ready optional history of (g, r) (§3.1): host uint8[hist_cap] bitmap; rows
  * below the frontier with a non-zero byte become resident, receiving
  * consecutive pool indices in ascending row order after those already handed
  * out in this group.  Once per (g, r) until kv_hier_clear_resident(g).
@@ -256,6 +269,88 @@ int kv_hier_sync(kv_hier_t *h);
 
 /* Replaces the KV_FLAG_* bits set at create (takes effect for later calls). */
 int kv_hier_set_flags(kv_hier_t *h, int32_t flags);
+
+/* ---------------------------------------------------------------------------
+ * Dynamic optional residency ("Adaptive DHiSparse" §3.1, eqs. 3-4; Figure 2).
+ * Needs opt_page_rows > 0.  The pool holds M = resident_cap / opt_page_rows
+ * pages of P = opt_page_rows rows in every group.  An admitted request's
+ * required allocations are charged against M in pages (they live in the
+ * request's own hot cache, ring and staging, not in the pool); its optional
+ * history is the complete pages of its imported history, floor(n_r / P)
+ * pages for the frontier n_r at admission.  Eq. (3) holds at all times:
+ * sum(required) + sum(held) + opt_reserve <= M.  A page is "held" once
+ * population reserves it and "ready" once its copy has completed and it has
+ * been published to the map that resolution probes first; rows of a pending
+ * page resolve through the hot cache or the host.  Every row keeps its host
+ * copy, so reclaiming never needs a backup copy here.  All of these calls
+ * are host-side decisions plus asynchronous device work: they never wait for
+ * the GPU (except kv_hier_opt_publish with wait = 1).
+ * ------------------------------------------------------------------------- */
+
+typedef struct {
+  int32_t pool_pages;          /* M                                                     */
+  int32_t page_rows;           /* P                                                     */
+  int32_t reserve;             /* M_res                                                 */
+  int32_t cursor;              /* next request slot the round-robin population visits   */
+  int64_t admitted;            /* admitted requests                                     */
+  int64_t required_pages;      /* sum of required pages of admitted requests            */
+  int64_t held_pages;          /* optional pages held (pending + ready)                 */
+  int64_t ready_pages;         /* optional pages published as ready                     */
+  int64_t pending_pages;       /* held, copy not yet published                          */
+  int64_t free_pages;          /* pool pages held by nobody                             */
+  int64_t eligible_pages;      /* complete imported pages of admitted requests          */
+  int64_t pages_populated;     /* cumulative: pages reserved and copied                 */
+  int64_t pages_published;     /* cumulative                                            */
+  int64_t pages_reclaimed;     /* cumulative: pages dropped by reclaim or completion    */
+  int64_t requests_reclaimed;  /* cumulative: requests taken by eq. (4)                 */
+  int64_t admissions_waited;   /* cumulative: admissions refused with KV_EWAIT          */
+  int64_t bytes_populated;     /* cumulative host bytes copied into the pool (all groups) */
+} kv_hier_opt_info;
+
+/* Admission of request r with `required_pages` pages of required allocations
+ * (eq. 3).  When the admission leaves a deficit
+ *   Delta = sum(required) + required_pages + sum(held) + reserve - M > 0,
+ * the requests of `order` (host int32[n_order], distinct admitted requests:
+ * the runtime's reclaim order r_1, r_2, ...) are walked and the first q with
+ * a_{r_1} + ... + a_{r_q} >= Delta lose all of their optional pages (eq. 4;
+ * a_r counts held pages, pending or ready); the other requests keep theirs.
+ * Reclaimed pages are unpublished before any later step resolves, and reused
+ * only after the attention of earlier steps has read them.  A reclaimed request
+ * stays admitted and resolves through its hot cache and the host.  If the
+ * whole order cannot cover Delta, returns KV_EWAIT and changes nothing.
+ * *n_reclaimed (may be NULL) receives q.  KV_ESTATE: no dynamic residency, or
+ * r already admitted. */
+int kv_hier_opt_admit(kv_hier_t *h, int r, int32_t required_pages, const int32_t *order, int n_order,
+                      int32_t *n_reclaimed);
+
+/* Completion of request r: its required and optional pages are released
+ * (optional pages unpublished and reused as after a reclaim).  KV_ESTATE if r
+ * is not admitted. */
+int kv_hier_opt_complete(kv_hier_t *h, int r);
+
+/* One bounded round-robin population attempt: request slots are visited
+ * cyclically from the cursor; each visit to an admitted request holding fewer
+ * than its eligible pages reserves its next page (ascending page index) in
+ * the lowest free pool page.  Stops after max_pages pages, when the eq. (3)
+ * budget is used up, or after a whole cycle without a reservation; the cursor
+ * then points past the last visited slot.  The rows of the reserved pages are
+ * copied from pinned host memory into every group's pool on the library's
+ * population stream, concurrently with steps; the pages become ready when
+ * published after the copy.  *n_assigned (may be NULL) receives the count. */
+int kv_hier_opt_populate(kv_hier_t *h, int32_t max_pages, int32_t *n_assigned);
+
+/* Publishes the pages whose copies have completed (wait = 0: those already
+ * complete; wait = 1: waits for every pending copy first).  Publication is
+ * ordered before the next step's resolution.  The first group's verify_step
+ * (g = 0) publishes completed copies by itself, without waiting. */
+int kv_hier_opt_publish(kv_hier_t *h, int wait);
+
+/* Host view of the residency state: totals (info, may be NULL) and, for
+ * request r when r >= 0, the pool page held for each of its first n_pages
+ * page indexes (held, host int32[n_pages], -1 = none) and whether it is
+ * published (ready, host uint8[n_pages]); either array may be NULL. */
+int kv_hier_opt_query(kv_hier_t *h, int r, int32_t n_pages, int32_t *held, uint8_t *ready,
+                      kv_hier_opt_info *info);
 
 /* Cache-state snapshot of group g: op 0 saves the hot rows, slot tables,
  * row->slot map and step counter into library-owned device memory (allocated

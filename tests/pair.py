@@ -124,7 +124,7 @@ def assert_close(gpu_bits: np.ndarray, ref: np.ndarray, what: str = ""):
     got = f32_from_bf16_bits(gpu_bits).astype(np.float64)
     err = np.abs(got - ref)
     lim = TOL_ABS + TOL_REL * np.abs(ref)
-    bad = err > lim
+    bad = ~(err <= lim)          # NaN fails too
     if bad.any():
         i = np.argwhere(bad)[0]
         raise AssertionError("%s: %d of %d outputs outside 2e-2 + 1e-2*|ref|; first at %s: got %r ref %r"

@@ -61,6 +61,10 @@ def _cfg(**kw):
     (dict(n_groups=3, plan_share=2, n_arenas=2), -1),
     (dict(n_groups=4, plan_share=4, n_arenas=2), -1),
     (dict(plan_share=-1), -1),
+    (dict(opt_page_rows=64), -1),                          # dynamic residency without a pool
+    (dict(opt_page_rows=64, resident_cap=1000), -1),       # pool not a whole number of pages
+    (dict(opt_page_rows=2048, resident_cap=4096), -1),     # page longer than the history
+    (dict(opt_reserve=-1), -1),
 ])
 def test_create_rejects_bad_config(lib, kw, code):
     from hierarchical_sparse_kv_verify_amd import KVHier, KVHierError
@@ -76,4 +80,7 @@ def test_null_handle_calls_are_rejected(lib):
     assert lib.kv_hier_stats(None, 0, None, None) == -1
     assert lib.kv_hier_verify_step(None, 0, None, None, None, None, None, None) == -1
     assert lib.kv_hier_last_error(None)
+    assert lib.kv_hier_opt_admit(None, 0, 0, None, 0, None) == -1
+    assert lib.kv_hier_opt_populate(None, 1, None) == -1
+    assert lib.kv_hier_opt_query(None, -1, 0, None, None, None) == -1
     lib.kv_hier_destroy(None)
