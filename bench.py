@@ -50,6 +50,13 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=128,
                     help="requests of layer group 0 the oracle resolves and attends in the CPU baseline")
+    ap.add_argument("--load-step", action="store_true",
+                    help="residency under a load step (low -> full -> low load), optional residency on and off")
+    ap.add_argument("--load-lo", type=int, default=16, help="active requests at low load")
+    ap.add_argument("--load-steps", default="20,20,40", help="steps of the low, full and recovery phases")
+    ap.add_argument("--page-rows", type=int, default=64, help="rows per optional-history page")
+    ap.add_argument("--populate-pages", type=int, default=512, help="population bound per step (pages)")
+    ap.add_argument("--reserve-pages", type=int, default=64, help="admission reserve (pages)")
     return ap.parse_args()
 
 
@@ -61,6 +68,10 @@ def main():
               "(the verification step shards by request with no exchange; see DESIGN.md)",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.load_step:
+        load_step(args)
+        return
 
     import numpy as np
     import torch
@@ -257,6 +268,142 @@ def main():
     }
     print(json.dumps(line), flush=True)
     lib.close()
+
+
+def load_step(args):
+    """Optional residency under a load step, at the level of the verification
+    step ("Adaptive DHiSparse" §4.3.1, Figure 6, Table A1): the same selections
+    and hot-cache state every step, while the load goes from a few requests
+    (their whole imported history resident on admission) to every request slot
+    (admissions reclaim whole requests, eq. 4) and back (completions free pages
+    that a bounded round-robin population refills).  Reports, per phase and
+    step, the share of selections fetched from host, the coverage (ready over
+    eligible pages) and the step time, with residency on and off."""
+    import math
+
+    import numpy as np
+    import torch
+
+    from tests.pair import build_pair, to_device
+    from workloads import WORKLOADS, make_history, make_step_inputs
+    from workloads.gen import make_hist_len
+
+    w = WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    P, lo, N, G = args.page_rows, args.load_lo, w.n_req, w.n_groups
+    s_lo, s_hi, s_rec = (int(x) for x in args.load_steps.split(","))
+    hl = make_hist_len(w)
+    hists = [make_history(w, g, hl) for g in range(G)]
+    sis = [make_step_inputs(w, g, 0, hl) for g in range(G)]
+    # required allocations of an admitted request, in pages: its hot cache and
+    # its ring of R_d = p*ceil((W+p-1+K_max)/p) rows
+    ring_rows = w.ring_page * math.ceil((w.ring_window + w.ring_page - 1 + w.q_max) / w.ring_page)
+    required = math.ceil((w.hot_slots + ring_rows) / P)
+    elig_max = int(hl.max()) // P
+    M = lo * (elig_max + required) + args.reserve_pages     # low load: every history fits
+    lo_set = np.arange(N) < lo
+    everyone = np.ones(N, dtype=bool)
+    report = {}
+    for arm in ("on", "off"):
+        kw = dict(resident_cap=M * P, opt_page_rows=P, opt_reserve=args.reserve_pages) if arm == "on" else {}
+        log("load step: arm %s, pool %d pages of %d rows (%.2f GB per group)" %
+            (arm, M if arm == "on" else 0, P, M * P * 2 * w.row_elems / 1e9 if arm == "on" else 0.0))
+        pair = build_pair(w, with_oracle=False, histories=hists, lib_kw=kw)
+        lib = pair.lib
+        assert lib.info["ring_rows"] == ring_rows
+        dev = [to_device(si) for si in sis]
+        causal = {}
+        for name, mask in (("lo", lo_set), ("all", everyone)):
+            cs = []
+            for si in sis:
+                c = si.causal_pos.copy()
+                c[~mask] = -1
+                cs.append(torch.from_numpy(c).cuda())
+            causal[name] = cs
+        out = torch.zeros((N, w.q_max, w.n_heads, w.d_v), dtype=torch.int16, device="cuda")
+        for g in range(G):
+            lib.save_cache(g)
+        admitted = []
+        waits = 0
+        if arm == "on":
+            # resident-first admission: the imported history is placed on the device
+            for r in range(lo):
+                assert lib.opt_admit(r, required, admitted) is not None
+                admitted.append(r)
+            while lib.opt_populate(4096):
+                pass
+            lib.opt_publish(wait=True)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        series, phases = [], []
+        for phase, n_steps, act in (("low", s_lo, "lo"), ("full", s_hi, "all"), ("recovery", s_rec, "lo")):
+            reclaimed = 0
+            if arm == "on" and phase == "full":
+                for r in range(lo, N):
+                    q = lib.opt_admit(r, required, admitted)
+                    if q is None:
+                        waits += 1
+                        continue
+                    reclaimed += q
+                    admitted.append(r)
+            if arm == "on" and phase == "recovery":
+                for r in range(lo, N):
+                    if r in admitted:
+                        lib.opt_complete(r)
+                        admitted.remove(r)
+            rows = []
+            for i in range(n_steps):
+                for g in range(G):
+                    lib.restore_cache(g)
+                torch.cuda.synchronize()
+                if arm == "on" and phase != "low":
+                    lib.opt_populate(args.populate_pages)    # runs beside the step
+                ev0.record()
+                for g in range(G):
+                    d = dev[g]
+                    lib.verify_step(g, d["queries"], d["topk"], causal[act][g], d["ring"], out)
+                ev1.record()
+                torch.cuda.synchronize()
+                ms = ev0.elapsed_time(ev1)
+                last = [lib.stats(g)[1] for g in range(G)]
+                tot = {k: sum(int(x[k]) for x in last) for k in ("selections", "sel_miss", "union_rows",
+                                                                 "union_miss", "active_queries")}
+                cov = None
+                if arm == "on":
+                    inf = lib.opt_info()
+                    cov = inf["ready_pages"] / max(1, inf["eligible_pages"])
+                rows.append(dict(ms=ms, cov=cov, share_sel=tot["sel_miss"] / max(1, tot["selections"]),
+                                 share_dist=tot["union_miss"] / max(1, tot["union_rows"]),
+                                 tokens=tot["active_queries"] / G))
+                series.append([phase, round(ms, 3), None if cov is None else round(cov, 4),
+                               round(rows[-1]["share_sel"], 5)])
+            mean = lambda k: float(np.mean([x[k] for x in rows])) if rows else None
+            ph = dict(phase=phase, steps=n_steps, active_requests=int(lo if act == "lo" else N),
+                      ms_per_step=round(mean("ms"), 4),
+                      tokens_per_s=round(mean("tokens") / (mean("ms") / 1000.0), 1),
+                      host_share_selected=round(mean("share_sel"), 5),
+                      host_share_distinct=round(mean("share_dist"), 5))
+            if arm == "on":
+                ph.update(coverage_first=round(rows[0]["cov"], 4), coverage_last=round(rows[-1]["cov"], 4),
+                          coverage_mean=round(mean("cov"), 4), requests_reclaimed=reclaimed)
+            phases.append(ph)
+            log("load step: arm %s phase %s: %s" % (arm, phase, ph))
+        res = dict(phases=phases, series=series)
+        if arm == "on":
+            inf = lib.opt_info()
+            res.update(admissions_waited=waits, pages_populated=inf["pages_populated"],
+                       pages_reclaimed=inf["pages_reclaimed"], bytes_populated=inf["bytes_populated"])
+        report[arm] = res
+        lib.close()
+        del pair, lib, dev, causal, out
+        torch.cuda.empty_cache()
+    line = {"metric": "host-fetched share of selections under a load step, optional residency on/off",
+            "unit": "fraction", "n_gpus": 1, "data": "synthetic",
+            "config": {"workload": w.name, "requests": N, "low_load_requests": lo, "layer_groups": G,
+                       "page_rows": P, "pool_pages": M, "required_pages_per_request": required,
+                       "reserve_pages": args.reserve_pages, "populate_pages_per_step": args.populate_pages,
+                       "steps": [s_lo, s_hi, s_rec], "reclaim_order": "admission order (oldest first)"},
+            "arms": report}
+    print(json.dumps(line), flush=True)
 
 
 def measure_h2d(torch, mib=512, reps=3):
