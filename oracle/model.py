@@ -164,6 +164,7 @@ class HierOracle:
         self.r_d = ring_rows(cfg.ring_window, cfg.ring_page, cfg.q_max)
         self.last_k = {r: 0 for r in self.requests}
         self.opt = None                                   # dynamic optional residency (residency.py)
+        self.last_sel = [None] * cfg.n_groups             # (topk, causal_pos, per-request activity)
         self.st = [{r: _Req(slot_row=[-1] * cfg.hot_slots, slot_lu=[0] * cfg.hot_slots,
                             slot_of={}, res_idx={}, ring={}, ring_lo=self.n[r])
                     for r in self.requests} for _ in range(cfg.n_groups)]
@@ -266,9 +267,12 @@ class HierOracle:
                 continue
             J = [j for j in range(Q) if cp[j] >= 0]
             self.last_k[r] = len(J)
-            # Figure 3 callout 4: the rows of all K queries are written; eq. (10) places them
-            for j in J:
-                st.ring[cp[j]] = np.array(block_rows[r][j], dtype=np.uint16)
+            # Figure 3 callout 4: the rows of all K queries are written; eq. (10) places them.
+            # A Reindex consumer of a shared source passes no rows: the source's
+            # producer already wrote this step's block (§2, physical-source sharing).
+            if block_rows is not None:
+                for j in J:
+                    st.ring[cp[j]] = np.array(block_rows[r][j], dtype=np.uint16)
 
             # eq. (6): U_r is the union of the K_r selections (R1 for validity)
             n_sel = n_pad = n_bad = 0
@@ -347,7 +351,21 @@ class HierOracle:
                                overflow=len(D) - n_prom, loc=loc, counts=counts)
 
         out = self._attend(g, topk, causal_pos, queries, res, attend, n_threads)
+        self.last_sel[g] = (np.array(topk, dtype=np.int32, copy=True), np.array(causal_pos, dtype=np.int32, copy=True),
+                            {r: res[r].active for r in self.requests})
         return StepResult(step=t, req=res, out=out)
+
+    def verify_reuse(self, g: int, queries, attend="all", n_threads: int = 1) -> Dict[tuple, np.ndarray]:
+        """A Reuse consumer (§2 "physical-source sharing"; §3.2): new queries
+        attend over the latest selection of source g through its location
+        vector and payload.  Placement never changes the result (eqs. 11-12),
+        so this is eq. (1) over that selection's lists plus the ring window;
+        no resolution, fetch or cache update happens."""
+        if self.last_sel[g] is None:
+            raise RuntimeError("no selection of this source to reuse")
+        topk, causal_pos, active = self.last_sel[g]
+        res = {r: ReqResult(active=active[r]) for r in self.requests}
+        return self._attend(g, topk, causal_pos, queries, res, attend, n_threads)
 
     def _attend(self, g, topk, causal_pos, queries, res, attend, n_threads):
         """Eq. (1) over each query's own list (read from the original rows,
@@ -393,7 +411,9 @@ class HierOracle:
     def commit(self, accepted):
         """Eq. (7): the anchor and A_r accepted drafts join history,
         n' = n + 1 + A; committed rows get their host copy and rejected rows
-        are never published (§3.3, after eq. 8)."""
+        are never published (§3.3, after eq. 8).  The step's selections end
+        with it: nothing is left to reuse."""
+        self.last_sel = [None] * self.cfg.n_groups
         for r in self.requests:
             a = int(accepted[r])
             if a < 0:
