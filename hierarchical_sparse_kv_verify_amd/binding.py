@@ -32,7 +32,7 @@ EXPORTED = [
     "kv_hier_verify_step", "kv_hier_commit", "kv_hier_stats", "kv_hier_reset_stats",
     "kv_hier_last_lists", "kv_hier_slot_table", "kv_hier_read_rows", "kv_hier_sync",
     "kv_hier_set_flags", "kv_hier_cache_snapshot", "kv_hier_opt_admit", "kv_hier_opt_complete",
-    "kv_hier_opt_populate", "kv_hier_opt_publish", "kv_hier_opt_query",
+    "kv_hier_opt_populate", "kv_hier_opt_publish", "kv_hier_opt_query", "kv_hier_verify_reuse",
 ]
 
 
@@ -135,6 +135,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "kv_hier_clear_resident": ([vp, i32], i32),
         "kv_hier_ring_load": ([vp, i32, i32, ctypes.c_int32, vp, i32], i32),
         "kv_hier_verify_step": ([vp, i32, vp, vp, vp, vp, vp, vp], i32),
+        "kv_hier_verify_reuse": ([vp, i32, vp, vp, vp, vp], i32),
         "kv_hier_commit": ([vp, vp, vp], i32),
         "kv_hier_stats": ([vp, i32, ctypes.POINTER(Counters), ctypes.POINTER(Counters)], i32),
         "kv_hier_reset_stats": ([vp], i32),
@@ -276,9 +277,17 @@ class KVHier:
 
     # -------------------------------------------------------------- the step
     def verify_step(self, g: int, queries, topk_idx, causal_pos, ring_rows, out, stream=None):
+        """ring_rows None: a Reindex consumer of a shared source (the ring already
+        holds this step's rows); topk_idx None only for a follower layer."""
         self._check(self._lib.kv_hier_verify_step(
-            self._h, g, _dev_ptr(queries), _dev_ptr(topk_idx), _dev_ptr(causal_pos),
-            _dev_ptr(ring_rows), _dev_ptr(out), _stream_handle(stream)))
+            self._h, g, _dev_ptr(queries), None if topk_idx is None else _dev_ptr(topk_idx),
+            _dev_ptr(causal_pos), None if ring_rows is None else _dev_ptr(ring_rows), _dev_ptr(out),
+            _stream_handle(stream)))
+
+    def verify_reuse(self, g: int, queries, causal_pos, out, stream=None):
+        """A Reuse consumer: new queries over the latest selection of source g."""
+        self._check(self._lib.kv_hier_verify_reuse(self._h, g, _dev_ptr(queries), _dev_ptr(causal_pos),
+                                                   _dev_ptr(out), _stream_handle(stream)))
 
     def commit(self, accepted, stream=None):
         a = _i32(accepted)

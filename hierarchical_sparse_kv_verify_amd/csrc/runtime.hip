@@ -63,6 +63,7 @@ struct Group {
   uint32_t* protect = nullptr;      // [N][ceil(B/32)] slots protected by this step's hits
   hipEvent_t ev_done = nullptr;     // copy-backs of the group's last step finished
   bool done_recorded = false;
+  bool sel_valid = false;           // this step's selection may be reused (until commit)
   int64_t* req_counts = nullptr;
   unsigned long long* cum = nullptr;
   std::vector<void*> prefix_host;
@@ -149,6 +150,8 @@ struct kv_hier {
   std::vector<std::vector<hipEvent_t>> ev_fetched;   // [set member][chunk]
   std::vector<std::vector<hipEvent_t>> ev_free;
   std::vector<std::vector<char>> free_recorded;
+  std::vector<int> arena_owner;     // group whose payload the arena holds (-1 none)
+  std::vector<int> arena_step;      // that group's step counter when it was fetched
   std::vector<int32_t> hist_len;
   int32_t* d_commit = nullptr;
   int32_t* h_commit = nullptr;
@@ -791,6 +794,8 @@ static int create_impl(kv_hier* h) {
     for (auto& e : v) HIPCHK(h, hipEventCreateWithFlags(&e, hipEventDisableTiming));
   h->ev_free.assign(c.n_arenas, std::vector<hipEvent_t>(h->n_chunks, nullptr));
   h->free_recorded.assign(c.n_arenas, std::vector<char>(h->n_chunks, 0));
+  h->arena_owner.assign(c.n_arenas, -1);
+  h->arena_step.assign(c.n_arenas, 0);
   for (auto& v : h->ev_free)
     for (auto& e : v) HIPCHK(h, hipEventCreateWithFlags(&e, hipEventDisableTiming));
   HIPCHK(h, hipDeviceSynchronize());
@@ -991,7 +996,7 @@ int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t*
                         const int32_t* causal_pos, const void* ring_rows, void* out, void* stream) {
   int rc = check_group(h, g);
   if (rc) return rc;
-  if (!queries || !causal_pos || !ring_rows || !out) return fail(h, KV_EINVAL, "null device pointer");
+  if (!queries || !causal_pos || !out) return fail(h, KV_EINVAL, "null device pointer");
   {
     const Group& G0 = h->grp[g];
     if (G0.member == 0 && !topk_idx) return fail(h, KV_EINVAL, "null device pointer");
@@ -1019,10 +1024,13 @@ int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t*
   }
   G.calls += 1;
 
-  int ti = time_begin(h, K_RING, g, s);
-  HIPCHK(h, launch_ring_write(static_cast<const uint4*>(ring_rows), causal_pos, reinterpret_cast<uint4*>(G.ring), N,
-                              c.q_max, h->Rd, h->row16, s));
-  time_end(h, ti, s);
+  int ti = -1;
+  if (ring_rows) {       // null: the source's producer already wrote this step's rows (a Reindex consumer)
+    ti = time_begin(h, K_RING, g, s);
+    HIPCHK(h, launch_ring_write(static_cast<const uint4*>(ring_rows), causal_pos, reinterpret_cast<uint4*>(G.ring),
+                                N, c.q_max, h->Rd, h->row16, s));
+    time_end(h, ti, s);
+  }
   if (lead) {
     // resolution plan and host fetch on the side stream (no event hop between
     // them), after the caller's prior work; the ring write runs beside the plan
@@ -1072,6 +1080,13 @@ int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t*
       for (int ch = 0; ch < h->n_chunks; ++ch) {
         const int r0 = h->chunk_lo[ch], r1 = h->chunk_lo[ch + 1];
         if (h->free_recorded[am][ch]) HIPCHK(h, hipStreamWaitEvent(h->side, h->ev_free[am][ch], 0));
+        if (c.flags & KV_FLAG_POISON) {
+          // debug: between the chunk's last readers and its next fetch the arena
+          // holds NaN, so a read outside that order shows in the outputs
+          const size_t words = size_t(r1 - r0) * h->QK * c.row_elems / 2;
+          HIPCHK(h, launch_fill32(reinterpret_cast<uint32_t*>(h->arena[am] + size_t(r0) * h->QK * c.row_elems),
+                                  0x7fc07fc0u, words, h->side));
+        }
         // 128 one-wave workgroups: enough host reads in flight to fill the link;
         // more only queue in the memory system and slow the attention beside them
         const int wgs = c.fetch_wgs > 0 ? c.fetch_wgs : 128;
@@ -1082,6 +1097,8 @@ int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t*
         time_end(h, ti, h->side);
         HIPCHK(h, hipEventRecord(h->ev_fetched[m][ch], h->side));
       }
+      h->arena_owner[am] = gm;
+      h->arena_step[am] = G.t;
       if (m == 0) {
         ti = time_begin(h, K_VICTIMS, g, h->side);
         HIPCHK(h, launch_plan_victims(pa, h->plan_lds, h->side));
@@ -1145,11 +1162,6 @@ int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t*
                              reinterpret_cast<uint4*>(G.hot), h->QK, c.hot_slots, h->row16, at.r0, at.r1, h->aux));
     time_end(h, ti, h->aux);
     HIPCHK(h, hipStreamWaitEvent(h->aux, h->ev_attn[ch], 0));
-    if (c.flags & KV_FLAG_POISON) {
-      const size_t words = size_t(at.r1 - at.r0) * h->QK * c.row_elems / 2;
-      HIPCHK(h, launch_fill32(reinterpret_cast<uint32_t*>(h->arena[a] + size_t(at.r0) * h->QK * c.row_elems),
-                              0x7fc07fc0u, words, h->aux));
-    }
     HIPCHK(h, hipEventRecord(h->ev_free[a][ch], h->aux));
     h->free_recorded[a][ch] = 1;
   }
@@ -1157,6 +1169,77 @@ int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t*
   // attention waits for this
   HIPCHK(h, hipEventRecord(G.ev_done, h->aux));
   G.done_recorded = true;
+  G.sel_valid = true;
+  if (h->work) {
+    HIPCHK(h, hipEventRecord(h->ev_out, s));
+    HIPCHK(h, hipStreamWaitEvent(caller, h->ev_out, 0));
+  }
+  return KV_OK;
+}
+
+int kv_hier_verify_reuse(kv_hier_t* h, int g, const void* queries, const int32_t* causal_pos, void* out,
+                         void* stream) {
+  int rc = check_group(h, g);
+  if (rc) return rc;
+  if (!queries || !causal_pos || !out) return fail(h, KV_EINVAL, "null device pointer");
+  const kv_hier_config& c = h->cfg;
+  Group& G = h->grp[g];
+  const Group& P = h->grp[G.leader];
+  const int a = g % c.n_arenas;
+  if (!G.sel_valid) return fail(h, KV_ESTATE, "group %d has no selection of this step to reuse", g);
+  if (h->arena_owner[a] != g || h->arena_step[a] != G.t)
+    return fail(h, KV_ESTATE, "the staged payload of group %d was replaced by a later fetch into arena %d", g, a);
+  hipStream_t caller = static_cast<hipStream_t>(stream);
+  hipStream_t s = caller;
+  if (h->work) {
+    HIPCHK(h, hipEventRecord(h->ev_in, caller));
+    HIPCHK(h, hipStreamWaitEvent(h->work, h->ev_in, 0));
+    s = h->work;
+  }
+  // the latest selection's locations and payload, read by the new queries
+  AttnArgs at;
+  at.q = static_cast<const uint16_t*>(queries);
+  at.loc = P.loc;
+  at.causal = causal_pos;
+  at.ring_lo = G.ring_lo;
+  at.hot = G.hot;
+  at.staging = h->arena[a];
+  at.resident = G.resident;
+  at.ring = G.ring;
+  at.zero = h->zero_row;
+  at.out = static_cast<uint16_t*>(out);
+  at.part_o = h->part_o;
+  at.part_ml = h->part_ml;
+  at.N = c.n_req;
+  at.Q = c.q_max;
+  at.k = c.topk;
+  at.H = c.n_heads;
+  at.W = c.ring_window;
+  at.Rd = h->Rd;
+  at.block_only = c.ring_block_only ? 1 : 0;
+  at.head_groups = h->head_groups;
+  const float scale = c.softmax_scale > 0.f ? c.softmax_scale : 1.0f / std::sqrt(float(c.d_qk));
+  at.scale_log2 = scale * 1.4426950408889634f;
+  for (int ch = 0; ch < h->n_chunks; ++ch) {
+    at.r0 = h->chunk_lo[ch];
+    at.r1 = h->chunk_lo[ch + 1];
+    at.splits = h->chunk_splits[ch];
+    int ti = time_begin(h, K_ATTN, g, s);
+    HIPCHK(h, launch_attn(at, c.row_elems, c.d_qk, c.v_off, c.d_v, s));
+    time_end(h, ti, s);
+    if (at.splits > 1) {
+      ti = time_begin(h, K_COMBINE, g, s);
+      HIPCHK(h, launch_attn_combine(at, c.d_v, s));
+      time_end(h, ti, s);
+    }
+  }
+  // the arena is released once this reader and the step's own readers and
+  // copy-backs are done: the release events now follow all of them
+  for (int ch = 0; ch < h->n_chunks; ++ch) {
+    if (h->free_recorded[a][ch]) HIPCHK(h, hipStreamWaitEvent(s, h->ev_free[a][ch], 0));
+    HIPCHK(h, hipEventRecord(h->ev_free[a][ch], s));
+    h->free_recorded[a][ch] = 1;
+  }
   if (h->work) {
     HIPCHK(h, hipEventRecord(h->ev_out, s));
     HIPCHK(h, hipStreamWaitEvent(caller, h->ev_out, 0));
@@ -1189,6 +1272,7 @@ int kv_hier_commit(kv_hier_t* h, const int32_t* accepted, void* stream) {
                           h->tail_rows, h->row16, s));
   for (int r = 0; r < N; ++r)
     if (accepted[r] >= 0) h->hist_len[r] += 1 + accepted[r];
+  for (Group& G : h->grp) G.sel_valid = false;     // the step's selections end with its commit
   return KV_OK;
 }
 

@@ -67,7 +67,8 @@ enum { KV_TIER_HOT = 0, KV_TIER_STAGED = 1, KV_TIER_RESIDENT = 2, KV_TIER_RING =
 
 enum {
   KV_FLAG_TIMING = 1,    /* time every kernel with HIP events (kv_hier_stats ms_*) */
-  KV_FLAG_POISON = 2,    /* debug: fill a staging arena with NaN after its readers finish */
+  KV_FLAG_POISON = 2,    /* debug: fill a staging-arena chunk with NaN between its last readers
+                            and its next fetch (and a dynamic pool at create)            */
   KV_FLAG_TIMING_ATTN = 4, /* time only the attention (and split-combine) launches: the
                               events then sit on no stream that gates the host fetch   */
   KV_FLAG_SERIAL = 8      /* measurement: the step's attention starts only after its whole
@@ -218,7 +219,9 @@ int kv_hier_ring_load(kv_hier_t *h, int g, int r, int32_t first_pos, const void 
  *   causal_pos device int32 [N][q_max]: n_r + j for active queries, -1 for an
  *              inactive suffix (request inactive when causal_pos[r][0] < 0)
  *   ring_rows  device bf16 [N][q_max][row_elems]: new KV row of each query's
- *              position, written to the ring at phi(r, p_j) (eq. 10)
+ *              position, written to the ring at phi(r, p_j) (eq. 10); NULL for a
+ *              Reindex consumer of a shared source, whose producer already wrote
+ *              this step's rows (the ring is left as it is)
  *   out        device bf16 [N][q_max][n_heads][d_v]; zero for inactive queries
  * Resolves the union of each request's selections, probes resident map then
  * hot cache, fetches every distinct missing row once from pinned host memory
@@ -232,10 +235,27 @@ int kv_hier_ring_load(kv_hier_t *h, int g, int r, int32_t first_pos, const void 
  * topk_idx and starts the host fetch of every layer of the set; a follower
  * group's step (after its leader's, once per step, else KV_ESTATE) ignores
  * topk_idx (may be NULL), attends over its own payload through the leader's
- * locations and copies back into its own hot cache. */
+ * locations and copies back into its own hot cache.
+ * Shared KV sources ("Adaptive DHiSparse" §2 physical-source sharing, §3.2):
+ * a group is one physical source; a Reindex consumer is another verify_step
+ * on the same group within the step (fresh topk_idx, ring_rows NULL): it
+ * resolves against the cache state the earlier consumers left, so only rows
+ * absent from it are fetched.  A Reuse consumer is kv_hier_verify_reuse. */
 int kv_hier_verify_step(kv_hier_t *h, int g, const void *queries, const int32_t *topk_idx,
                         const int32_t *causal_pos, const void *ring_rows, void *out,
                         void *stream);
+
+/* A Reuse consumer of source g ("Adaptive DHiSparse" §2, §3.2): new queries
+ * (device bf16 [N][q_max][n_heads][d_qk]) attend, exactly as in verify_step,
+ * over the latest selection of g through its location vector and the payload
+ * it materialized (hot cache, staged rows, resident pool, ring): no
+ * resolution, fetch or cache update.  causal_pos must equal the one given to
+ * that selection's verify_step (caller contract); out as in verify_step.
+ * Asynchronous on `stream`.  KV_ESTATE when g has no selection in this step
+ * (none yet, or a commit since) or when a later fetch of another group has
+ * replaced its staged rows (arena g mod n_arenas). */
+int kv_hier_verify_reuse(kv_hier_t *h, int g, const void *queries, const int32_t *causal_pos, void *out,
+                         void *stream);
 
 /* Acceptance (eq. 7) for every request: accepted[r] = A_r in [0, q_max-1], or
  * -1 for no commit.  Copies the ring rows of positions n_r .. n_r+A_r of every

@@ -255,24 +255,27 @@ def test_inactive_requests_and_queries():
 
 
 def test_poisoned_arena_after_readers():
-    """With arena poisoning the step's outputs are unchanged: the arena is
-    overwritten only after attention and copy-back have read it.  Timing
-    events and the serialised attention leave the outputs unchanged too."""
-    w = _mla_small(n_groups=1, var_k=False)
+    """With arena poisoning (NaN between a chunk's last readers and its next
+    fetch) the outputs of two groups sharing one arena are unchanged: every
+    fetch waits for the previous readers and every attention for its fetch.
+    The staged rows stay readable after the step (a Reuse consumer may still
+    read them).  Timing events and the serialised attention leave the outputs
+    unchanged too."""
+    w = _mla_small(n_groups=2, n_arenas=1, var_k=False)
     outs = []
     for flags in (0, 2, 1, 4 | 8):
         pair = build_pair(w, with_oracle=False, lib_kw=dict(flags=flags, n_chunks=2))
-        si = make_step_inputs(w, 0, 0, pair.hist_len)
-        outs.append(run_lib_step(pair, 0, si))
+        outs.append([run_lib_step(pair, g, make_step_inputs(w, g, 0, pair.hist_len)) for g in range(2)])
         if flags == 2:
-            L = pair.lib.last_lists(0, 0)
-            staged = L["loc"][L["loc"] >= 0]
-            staged = staged[(staged >> 29) == 1][:4]
-            if staged.size:
-                assert (pair.lib.read_rows(0, staged) == 0x7fc0).all()
+            L = pair.lib.last_lists(1, 0)
+            sel = np.flatnonzero((L["loc"].ravel() >= 0) & ((L["loc"].ravel() >> 29) == 1))[:8]
+            if sel.size:
+                rows = pair.lib.read_rows(1, L["loc"].ravel()[sel])
+                assert not (rows == 0x7fc0).all(axis=1).any()
         pair.lib.close()
     for o in outs[1:]:
-        assert np.array_equal(outs[0], o)
+        for g in range(2):
+            assert np.array_equal(outs[0][g], o[g])
 
 
 def test_full_size_mla128_sampled():
