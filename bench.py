@@ -57,6 +57,12 @@ def parse():
     ap.add_argument("--page-rows", type=int, default=64, help="rows per optional-history page")
     ap.add_argument("--populate-pages", type=int, default=512, help="population bound per step (pages)")
     ap.add_argument("--reserve-pages", type=int, default=64, help="admission reserve (pages)")
+    ap.add_argument("--shared-source", action="store_true",
+                    help="shared KV sources: selecting, re-selecting and reusing layers per source")
+    ap.add_argument("--reuse-per-selection", type=int, default=2,
+                    help="layers reusing each selection (shared-source run)")
+    ap.add_argument("--reselect-new", type=float, default=0.25,
+                    help="share of a re-selecting layer's entries that differ from the first selection")
     return ap.parse_args()
 
 
@@ -71,6 +77,9 @@ def main():
 
     if args.load_step:
         load_step(args)
+        return
+    if args.shared_source:
+        shared_source(args)
         return
 
     import numpy as np
@@ -404,6 +413,119 @@ def load_step(args):
                        "steps": [s_lo, s_hi, s_rec], "reclaim_order": "admission order (oldest first)"},
             "arms": report}
     print(json.dumps(line), flush=True)
+
+
+def shared_source(args):
+    """Shared KV sources ("Adaptive DHiSparse" §2 physical-source sharing, §3.2,
+    Table 3): per source and step a selecting layer (resolve, fetch, attend), a
+    re-selecting layer (a fresh top-k sharing most entries with the first,
+    resolved against the state the first left: only absent rows are fetched) and, after
+    each, layers that reuse the latest selection with their own queries.  Arm
+    "reuse" runs those layers through kv_hier_verify_reuse; arm "resolve"
+    resolves the same selection again for each of them (same outputs)."""
+    import numpy as np
+    import torch
+
+    from tests.pair import build_pair, to_device
+    from workloads import WORKLOADS, make_history, make_step_inputs, shrink
+    from workloads.gen import make_hist_len
+
+    w = WORKLOADS["ds_shared"] if args.workload == "mla128" else WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    G, R = w.n_groups, args.reuse_per_selection
+    hl = make_hist_len(w)
+    hists = [make_history(w, g, hl) for g in range(G)]
+    pair = build_pair(w, with_oracle=False, histories=hists)
+    lib = pair.lib
+    dev = torch.device("cuda")
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    layers = []          # per source: (selection A inputs, reindex topk, consumer query sets)
+    for g in range(G):
+        si = make_step_inputs(w, g, 0, hl)
+        sb = make_step_inputs(w, g, 1, hl)
+        # the re-selection keeps the first selection's entries except a seeded
+        # share, which it takes from another draw of the same generator
+        keep = np.random.default_rng([20261009, 6, g, 77]).random(si.topk.shape) >= args.reselect_new
+        topk_b = np.where(keep, si.topk, sb.topk).astype(np.int32)
+        qs = [t(make_step_inputs(w, g, 2 + i, hl).queries.view(np.int16)) for i in range(2 * R)]
+        layers.append(dict(d=to_device(si), topk_b=t(topk_b), qb=t(sb.queries.view(np.int16)), qs=qs))
+    out = torch.zeros((w.n_req, w.q_max, w.n_heads, w.d_v), dtype=torch.int16, device="cuda")
+    for g in range(G):
+        lib.save_cache(g)
+    torch.cuda.synchronize()
+
+    def step(arm):
+        for g in range(G):
+            L = layers[g]
+            d = L["d"]
+            lib.verify_step(g, d["queries"], d["topk"], d["causal"], d["ring"], out)
+            for i in range(R):
+                if arm == "reuse":
+                    lib.verify_reuse(g, L["qs"][i], d["causal"], out)
+                else:
+                    lib.verify_step(g, L["qs"][i], d["topk"], d["causal"], None, out)
+            lib.verify_step(g, L["qb"], L["topk_b"], d["causal"], None, out)
+            for i in range(R, 2 * R):
+                if arm == "reuse":
+                    lib.verify_reuse(g, L["qs"][i], d["causal"], out)
+                else:
+                    lib.verify_step(g, L["qs"][i], L["topk_b"], d["causal"], None, out)
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    report = {}
+    for arm in ("reuse", "resolve"):
+        for _ in range(args.warmup):
+            for g in range(G):
+                lib.restore_cache(g)
+            step(arm)
+        torch.cuda.synchronize()
+        lib.reset_stats()
+        times = []
+        for _ in range(args.steps):
+            for g in range(G):
+                lib.restore_cache(g)
+            torch.cuda.synchronize()
+            ev0.record()
+            step(arm)
+            ev1.record()
+            torch.cuda.synchronize()
+            times.append(ev0.elapsed_time(ev1))
+        cum = [lib.stats(g)[0] for g in range(G)]
+        ms = float(np.mean(times))
+        calls = sum(int(c["calls"]) for c in cum) / args.steps
+        fetched = sum(int(c["union_miss"]) for c in cum) / args.steps
+        union = sum(int(c["union_rows"]) for c in cum) / args.steps
+        tokens = w.n_req * w.q_max
+        report[arm] = dict(ms_per_step=round(ms, 4), ms_min=round(min(times), 4), ms_max=round(max(times), 4),
+                           query_tokens_per_s=round(tokens / (ms / 1000.0), 1),
+                           resolver_calls_per_step=calls, attention_layers_per_step=G * (2 + 2 * R),
+                           fetched_rows_per_step=fetched, fetched_mb_per_step=round(fetched * 2 * w.row_elems / 1e6, 2),
+                           union_rows_per_step=union)
+        log("shared source: arm %s: %s" % (arm, report[arm]))
+    # the re-selecting layer alone: rows it fetches against those of the first selection
+    lib.reset_stats()
+    for g in range(G):
+        lib.restore_cache(g)
+    first, second = 0, 0
+    for g in range(G):
+        L = layers[g]
+        d = L["d"]
+        lib.verify_step(g, d["queries"], d["topk"], d["causal"], d["ring"], out)
+        first += int(lib.stats(g)[1]["union_miss"])
+        lib.verify_step(g, L["qb"], L["topk_b"], d["causal"], None, out)
+        second += int(lib.stats(g)[1]["union_miss"])
+    torch.cuda.synchronize()
+    line = {"metric": "verified query-tokens/s with shared KV sources (reuse vs re-resolution)",
+            "unit": "query-tokens/s", "n_gpus": 1, "data": "synthetic", "steps": args.steps,
+            "warmup": args.warmup,
+            "config": {"workload": w.name, "requests": w.n_req, "sources": G, "q_max": w.q_max, "topk": w.topk,
+                       "hot_slots": w.hot_slots, "heads": w.n_heads, "row_bytes": 2 * w.row_elems,
+                       "reuse_layers_per_selection": R, "reselect_new_share": args.reselect_new,
+                       "layers_per_source": "select, %d reuse, re-select, %d reuse" % (R, R)},
+            "arms": report,
+            "reselect_fetched_rows": second, "select_fetched_rows": first}
+    print(json.dumps(line), flush=True)
+    lib.close()
 
 
 def measure_h2d(torch, mib=512, reps=3):

@@ -137,6 +137,7 @@ struct kv_hier {
   uint16_t* zero_row = nullptr;   // one all-zero row: target of masked attention reads
   float* part_ml = nullptr;
   int splits = 1, head_groups = 1, n_chunks = 1;   // splits: the largest of chunk_splits
+  int all_splits = 1;               // key splits of one launch over every request (Reuse layers)
   std::vector<int> chunk_lo, chunk_splits;
   int chunk_words = 0, sort_cap = 1;
   size_t plan_lds = 0;
@@ -630,13 +631,23 @@ static int create_impl(kv_hier* h) {
     const int tiles = (c.topk + c.ring_window + 31) / 32;
     size_t blocks = 0;
     h->splits = 1;
+    auto split_for = [&](int64_t wgs) {
+      int s = wgs < 256 ? int(std::min<int64_t>(8, std::max<int64_t>(1, 256 / std::max<int64_t>(1, wgs)))) : 1;
+      return std::max(1, std::min(s, tiles / 4));
+    };
     for (int ch = 0; ch < h->n_chunks; ++ch) {
       const int64_t wgs = int64_t(h->chunk_lo[ch + 1] - h->chunk_lo[ch]) * c.q_max * h->head_groups;
-      int s = wgs < 256 ? int(std::min<int64_t>(8, std::max<int64_t>(1, 256 / std::max<int64_t>(1, wgs)))) : 1;
-      s = std::max(1, std::min(s, tiles / 4));
+      const int s = split_for(wgs);
       h->chunk_splits.push_back(s);
       h->splits = std::max(h->splits, s);
       if (s > 1) blocks = std::max(blocks, size_t(wgs) * s);
+    }
+    {
+      // a Reuse layer has no fetch to overlap: one launch over every request
+      const int64_t wgs = int64_t(N) * c.q_max * h->head_groups;
+      h->all_splits = split_for(wgs);
+      h->splits = std::max(h->splits, h->all_splits);
+      if (h->all_splits > 1) blocks = std::max(blocks, size_t(wgs) * h->all_splits);
     }
     if (blocks > 0) {
       rc = dev_alloc(h, &h->part_o, blocks * hpw * c.d_v, &h->bytes_maps);
@@ -1220,10 +1231,10 @@ int kv_hier_verify_reuse(kv_hier_t* h, int g, const void* queries, const int32_t
   at.head_groups = h->head_groups;
   const float scale = c.softmax_scale > 0.f ? c.softmax_scale : 1.0f / std::sqrt(float(c.d_qk));
   at.scale_log2 = scale * 1.4426950408889634f;
-  for (int ch = 0; ch < h->n_chunks; ++ch) {
-    at.r0 = h->chunk_lo[ch];
-    at.r1 = h->chunk_lo[ch + 1];
-    at.splits = h->chunk_splits[ch];
+  {
+    at.r0 = 0;
+    at.r1 = c.n_req;
+    at.splits = h->all_splits;
     int ti = time_begin(h, K_ATTN, g, s);
     HIPCHK(h, launch_attn(at, c.row_elems, c.d_qk, c.v_off, c.d_v, s));
     time_end(h, ti, s);
