@@ -5,7 +5,7 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 (``hierarchical_sparse_kv_verify_amd``) and never imports it.
 """
 from .model import (  # noqa: F401
-    CLS_HOT, CLS_MISS, CLS_RESIDENT, HOT, RESIDENT, STAGED,
+    CLS_HOT, CLS_MISS, CLS_RESIDENT, CLS_TAIL, HOT, RESIDENT, RING, STAGED,
     HierOracle, OracleConfig, StepResult, loc_code, ring_addr, ring_rows, staging_bytes,
     to_bf16_bits,
 )

@@ -46,6 +46,13 @@ Readings where the pages leave a step open (each marked READING below):
   R7 resident pool indices are handed out per layer group in call order of
      set_resident, ascending row order within a call.
   R8 the step counter of a group starts above every age given to set_hot.
+  R9 the tail (Figure 2 callout 1; §3.1 "mutable tail"; Figure 3 callout 4):
+     a selected history row still held by the request's ring resolves there
+     directly, before the optional map and the hot cache.  The ring holds
+     position u while u >= ring_lo and u >= n_r + K_max - R_d (slots of
+     older positions may already carry this step's new rows, eq. 10);
+     location tier 3, index r*R_d + (u mod R_d).  Tail rows are never
+     inserted in the hot cache.
 
 Dynamic optional residency (§3.1, eqs. 3-4) is modelled in ``residency.py``;
 once attached, its ready map (shared by every group) is what step (1) of the
@@ -61,8 +68,8 @@ import numpy as np
 
 from . import native
 
-HOT, STAGED, RESIDENT = 0, 1, 2          # tiers of a location code (R6)
-CLS_RESIDENT, CLS_HOT, CLS_MISS = 0, 1, 2  # class of a union row
+HOT, STAGED, RESIDENT, RING = 0, 1, 2, 3  # tiers of a location code (R6)
+CLS_RESIDENT, CLS_HOT, CLS_MISS, CLS_TAIL = 0, 1, 2, 3  # class of a union row
 
 
 def loc_code(tier: int, index: int) -> int:
@@ -292,9 +299,14 @@ class HierOracle:
             # Figure 2 / §3.2: (1) direct map, (2) hot cache, (3) host; R3
             cls = {}
             res_at = {}
+            tail_lo = max(st.ring_lo, n_r + Q - self.r_d)          # R9
             for u in U:
                 ri = self._resident(g, r, u)
-                if ri is not None:
+                if u >= tail_lo:
+                    if u not in st.ring:
+                        raise RuntimeError("tail row %d of request %d not in the ring" % (u, r))
+                    cls[u] = CLS_TAIL
+                elif ri is not None:
                     res_at[u] = ri
                     cls[u] = CLS_RESIDENT
                 elif u in st.slot_of:
@@ -307,7 +319,7 @@ class HierOracle:
             # §3.5 eq. (12): one location per list entry, in selection order (R6)
             seg = r * Q * k
             loc = np.full((Q, k), -1, dtype=np.int32)
-            sel_cls = [0, 0, 0]
+            sel_cls = [0, 0, 0, 0]
             for j in J:
                 for i, e in enumerate(topk[r][j]):
                     e = int(e)
@@ -315,7 +327,9 @@ class HierOracle:
                         continue
                     c = cls[e]
                     sel_cls[c] += 1
-                    if c == CLS_RESIDENT:
+                    if c == CLS_TAIL:
+                        loc[j, i] = loc_code(RING, r * self.r_d + e % self.r_d)
+                    elif c == CLS_RESIDENT:
                         loc[j, i] = loc_code(RESIDENT, res_at[e])
                     elif c == CLS_HOT:
                         loc[j, i] = loc_code(HOT, r * B + st.slot_of[e])
@@ -345,6 +359,7 @@ class HierOracle:
                           union_hot=sum(1 for u in U if cls[u] == CLS_HOT),
                           union_miss=len(D), promoted=n_prom, overflow=len(D) - n_prom,
                           sel_resident=sel_cls[0], sel_hot=sel_cls[1], sel_miss=sel_cls[2],
+                          union_tail=sum(1 for u in U if cls[u] == CLS_TAIL), sel_tail=sel_cls[3],
                           queries=len(J))
             res[r] = ReqResult(active=True, k_active=len(J), union=U,
                                cls=[cls[u] for u in U], miss=D, victims=victims,

@@ -9,7 +9,8 @@ bf16 (round to nearest even).  Selections follow a "core + Zipf" recipe: a
 shared core of round(f_sh * k) rows drawn uniformly without replacement from
 the request's history, plus, for every query, k - core distinct rows drawn
 from a Zipf(s) law over a seeded permutation of the remaining rows; each list
-is then shuffled.  Correctness suites may replace a fraction of entries by the
+is then shuffled.  Optionally a share of each list is replaced by distinct
+rows among the most recent ones (recently generated history).  Correctness suites may replace a fraction of entries by the
 pad value -1 or by out-of-range values.
 
 The module holds no step of the verified method: it never resolves, places or
@@ -63,6 +64,8 @@ class Workload:
     ring_prefill: bool = True  # load the W-1 committed positions below n_r into the ring
     plan_share: int = 1       # payload layers per index producer: consecutive groups of this
                               # size share one selection (and warm set / resident map)
+    recent_frac: float = 0.0  # share of each list replaced by distinct rows of the last
+    recent_span: int = 0      # recent_span history rows (recently generated rows)
     note: str = ""
 
     @property
@@ -314,6 +317,12 @@ def make_step_inputs(w: Workload, group: int, step: int, hist_len: np.ndarray,
             lst = lst[rng.permutation(lst.size)]
             row = np.full(k, -1, dtype=np.int64)
             row[: lst.size] = lst
+            if w.recent_frac > 0:
+                cand = np.setdiff1d(np.arange(max(0, n_r - w.recent_span), n_r), row)
+                m = min(int(round(w.recent_frac * k)), cand.size)
+                if m:
+                    at = rng.choice(k, size=m, replace=False)
+                    row[at] = rng.choice(cand, size=m, replace=False)
             if w.pad_frac > 0 or w.invalid_frac > 0:
                 u = rng.random(k)
                 row[u < w.pad_frac] = -1
