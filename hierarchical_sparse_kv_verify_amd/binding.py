@@ -59,10 +59,14 @@ TIMING_FIELDS = ("ms_ring", "ms_plan", "ms_gather", "ms_attn", "ms_combine", "ms
 TIMING_COUNTS = ("n_ring", "n_plan", "n_gather", "n_attn", "n_combine", "n_promote", "n_victims")
 
 
+TAIL_FIELDS = ("union_tail", "sel_tail")
+
+
 class Counters(ctypes.Structure):
     _fields_ = ([(n, ctypes.c_int64) for n in COUNTER_FIELDS] +
                 [(n, ctypes.c_double) for n in TIMING_FIELDS] +
-                [(n, ctypes.c_int64) for n in TIMING_COUNTS])
+                [(n, ctypes.c_int64) for n in TIMING_COUNTS] +
+                [(n, ctypes.c_int64) for n in TAIL_FIELDS])
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

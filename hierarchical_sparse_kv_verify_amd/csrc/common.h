@@ -20,7 +20,7 @@ __host__ __device__ inline int32_t loc_index(int32_t code) { return code & kInde
 // the same order as the counter fields of kv_hier_stats.
 enum Counter {
   C_ACTIVE_REQ = 0, C_ACTIVE_Q, C_SEL, C_PAD, C_INVALID, C_UNION, C_U_RES, C_U_HOT, C_U_MISS,
-  C_PROMOTED, C_OVERFLOW, C_S_RES, C_S_HOT, C_S_MISS, C_NUM
+  C_PROMOTED, C_OVERFLOW, C_S_RES, C_S_HOT, C_S_MISS, C_U_TAIL, C_S_TAIL, C_NUM
 };
 
 // per-request info written by the plan kernel
@@ -31,6 +31,7 @@ struct PlanArgs {
   const int32_t* topk;       // [N][Q][k]
   const int32_t* causal;     // [N][Q]
   const int32_t* res_map;    // [N][L] row -> resident pool index or -1
+  const int32_t* ring_lo;    // [N] first position the ring has held
   int32_t* slot_map;         // [N][L] row -> hot slot or -1
   int32_t* slot_row;         // [N][B]
   int32_t* slot_lu;          // [N][B]
@@ -44,6 +45,7 @@ struct PlanArgs {
   int64_t* req_counts;       // [N][C_NUM] last step
   unsigned long long* cum;   // [C_NUM] cumulative
   int N, Q, k, B, L, t;
+  int Rd;                    // ring rows per request (the tail: positions >= max(ring_lo, n_r + Q - Rd))
   int has_resident;          // 0: the resident map holds no row (its lookups are skipped)
   int chunk_words;           // bitmap words per row chunk (rows per chunk = 32 * chunk_words)
   int sort_cap;              // power of two >= B

@@ -4,8 +4,9 @@
 // "Adaptive DHiSparse" (arXiv 2610.13708):
 //  - §3.3 eq. (6): the retrieval union U_r of the K_r queries' selections and
 //    the missing set D_r = U_r \ R_r; each distinct missing row is fetched once.
-//  - §3.2 / Figure 2: probe order (1) ready optional-history map,
-//    (2) hot cache, (3) host; locations emitted in selection order (eq. 12).
+//  - §3.2 / Figure 2: probe order (1) the tail (rows the request's ring
+//    still holds) or the ready optional-history map, (2) hot cache,
+//    (3) host; locations emitted in selection order (eq. 12).
 //  - §2.2 "Fixed-cache offloading": selected rows in the cache are protected,
 //    unselected rows are LRU victims.
 //  - §3.3 (overflow paragraph) and §3.4: missing rows are staged in the
@@ -99,14 +100,17 @@ __global__ __launch_bounds__(kThreads) void plan_resolve_kernel(PlanArgs a) {
     return;
   }
   const int n_r = n_raw < L ? n_raw : L;
+  // the ring still holds positions >= tail_lo: this step's block (n_r ..
+  // n_r+Q-1) takes the slots of the positions below (eq. 10)
+  const int tail_lo = max(a.ring_lo[r], n_r + Q - a.Rd);
   uint32_t amask = 0;
   for (int j = 0; j < Q; ++j) amask |= (cp[j] >= 0 ? 1u : 0u) << j;
 
   for (int w = tid; w < pwords; w += kThreads) protect[w] = 0;
   if (tid < 32) cnt[tid] = 0;
 
-  int c_sel = 0, c_pad = 0, c_bad = 0, c_sres = 0, c_shot = 0, c_smiss = 0;
-  int c_ures = 0, c_uhot = 0, c_umiss = 0;
+  int c_sel = 0, c_pad = 0, c_bad = 0, c_sres = 0, c_shot = 0, c_smiss = 0, c_stail = 0;
+  int c_ures = 0, c_uhot = 0, c_umiss = 0, c_utail = 0;
   int union_base = 0, miss_base = 0;
   const int WPT = (CW + kThreads - 1) / kThreads;
 
@@ -160,7 +164,8 @@ __global__ __launch_bounds__(kThreads) void plan_resolve_kernel(PlanArgs a) {
     }
     __syncthreads();
     // probe every union row (strided, so each thread's map loads are
-    // independent): resident map first, then the hot cache (Figure 2)
+    // independent): the tail and the resident map first, then the hot cache
+    // (Figure 2)
     for (int x0 = tid; x0 < chunk_union; x0 += kBatch * kThreads) {
       int uv[kBatch], rmv[kBatch], smv[kBatch];
 #pragma unroll
@@ -180,7 +185,10 @@ __global__ __launch_bounds__(kThreads) void plan_resolve_kernel(PlanArgs a) {
         const int rm = rmv[b], sm = smv[b];
         if (sm >= 0) atomicOr(&protect[sm >> 5], 1u << (sm & 31));
         int code;
-        if (rm >= 0) {
+        if (uv[b] >= tail_lo) {
+          code = make_loc(kTierRing, r * a.Rd + uv[b] % a.Rd);
+          ++c_utail;
+        } else if (rm >= 0) {
           code = make_loc(kTierResident, rm);
           ++c_ures;
         } else if (sm >= 0) {
@@ -236,6 +244,7 @@ __global__ __launch_bounds__(kThreads) void plan_resolve_kernel(PlanArgs a) {
           c_sres += tier == kTierResident;
           c_shot += tier == kTierHot;
           c_smiss += tier == kTierStaged;
+          c_stail += tier == kTierRing;
         }
       }
     }
@@ -255,10 +264,11 @@ __global__ __launch_bounds__(kThreads) void plan_resolve_kernel(PlanArgs a) {
 
   // block totals of the per-thread counters: wave sums, one LDS atomic per wave
   {
-    const int v[9] = {c_sel, c_pad, c_bad, c_sres, c_shot, c_smiss, c_ures, c_uhot, c_umiss};
-    const int slot[9] = {C_SEL, C_PAD, C_INVALID, C_S_RES, C_S_HOT, C_S_MISS, C_U_RES, C_U_HOT, C_U_MISS};
+    const int v[11] = {c_sel, c_pad, c_bad, c_sres, c_shot, c_smiss, c_ures, c_uhot, c_umiss, c_utail, c_stail};
+    const int slot[11] = {C_SEL, C_PAD, C_INVALID, C_S_RES, C_S_HOT, C_S_MISS, C_U_RES, C_U_HOT, C_U_MISS,
+                          C_U_TAIL, C_S_TAIL};
 #pragma unroll
-    for (int q = 0; q < 9; ++q) {
+    for (int q = 0; q < 11; ++q) {
       const int tot = wave_sum(v[q]);
       if ((tid & 63) == 0 && tot) atomicAdd(&cnt[slot[q]], tot);
     }

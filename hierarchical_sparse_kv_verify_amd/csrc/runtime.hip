@@ -158,6 +158,11 @@ struct kv_hier {
   int32_t* h_commit = nullptr;
   hipEvent_t ev_commit = nullptr;
   bool commit_pending = false;
+  // host backup of committed rows (eq. 7) on its own stream, after verification
+  hipStream_t backup = nullptr;     // null: backups run on the caller's stream
+  hipEvent_t ev_verified = nullptr; // the step's ring rows are written (caller's stream)
+  hipEvent_t ev_backup[2] = {nullptr, nullptr};
+  int64_t n_commits = 0;
   CommitGroup* d_commit_groups = nullptr;
   std::vector<Timed> pending;
   std::vector<hipEvent_t> pool;
@@ -388,6 +393,10 @@ void free_all(kv_hier* h) {
   if (h->ev_out) (void)hipEventDestroy(h->ev_out);
   if (h->work) (void)hipStreamDestroy(h->work);
   if (h->ev_commit) (void)hipEventDestroy(h->ev_commit);
+  if (h->ev_verified) (void)hipEventDestroy(h->ev_verified);
+  for (hipEvent_t e : h->ev_backup)
+    if (e) (void)hipEventDestroy(e);
+  if (h->backup) (void)hipStreamDestroy(h->backup);
   for (auto& v : h->ev_fetched) for (hipEvent_t e : v) (void)hipEventDestroy(e);
   for (auto& v : h->ev_free) for (hipEvent_t e : v) (void)hipEventDestroy(e);
   for (hipEvent_t e : h->ev_attn) (void)hipEventDestroy(e);
@@ -800,6 +809,14 @@ static int create_impl(kv_hier* h) {
   HIPCHK(h, hipEventCreateWithFlags(&h->ev_in, hipEventDisableTiming));
   HIPCHK(h, hipEventCreateWithFlags(&h->ev_out, hipEventDisableTiming));
   HIPCHK(h, hipEventCreateWithFlags(&h->ev_commit, hipEventDisableTiming));
+  // Asynchronous host backup needs every row of the last commit to stay in the
+  // ring's tail through the next step (R_d >= 2 K_max); otherwise the backup
+  // runs on the caller's stream, ahead of the next step.
+  if (h->Rd >= 2 * c.q_max) {
+    HIPCHK(h, hipStreamCreateWithFlags(&h->backup, hipStreamNonBlocking));
+    HIPCHK(h, hipEventCreateWithFlags(&h->ev_verified, hipEventDisableTiming));
+    for (hipEvent_t& e : h->ev_backup) HIPCHK(h, hipEventCreateWithFlags(&e, hipEventDisableTiming));
+  }
   h->ev_fetched.assign(h->share, std::vector<hipEvent_t>(h->n_chunks, nullptr));
   for (auto& v : h->ev_fetched)
     for (auto& e : v) HIPCHK(h, hipEventCreateWithFlags(&e, hipEventDisableTiming));
@@ -1026,6 +1043,14 @@ int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t*
   Group& G = h->grp[g];
   Group& P = h->grp[G.leader];      // owner of the plan state (G itself unless a follower)
   const bool lead = G.member == 0;
+  // rows of the last commit are still in the tail (resolved from the ring);
+  // those of the commit before may be fetched from the host or have their ring
+  // slots rewritten by this step: its backup must be complete
+  if (h->backup && h->n_commits >= 2) {
+    hipEvent_t eb = h->ev_backup[h->n_commits % 2];
+    HIPCHK(h, hipStreamWaitEvent(s, eb, 0));
+    if (lead) HIPCHK(h, hipStreamWaitEvent(h->side, eb, 0));
+  }
   const int N = c.n_req;
   const int a = g % c.n_arenas;
   if (lead) {
@@ -1054,6 +1079,8 @@ int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t*
     pa.topk = topk_idx;
     pa.causal = causal_pos;
     pa.res_map = G.res_map;
+    pa.ring_lo = G.ring_lo;
+    pa.Rd = h->Rd;
     pa.has_resident = (h->opt.on ? h->opt.n_published > 0 : G.res_cursor > 0) ? 1 : 0;
     pa.slot_map = G.slot_map;
     pa.slot_row = G.slot_row;
@@ -1276,11 +1303,20 @@ int kv_hier_commit(kv_hier_t* h, const int32_t* accepted, void* stream) {
     h->h_commit[r] = h->hist_len[r];
     h->h_commit[N + r] = accepted[r];
   }
-  HIPCHK(h, hipMemcpyAsync(h->d_commit, h->h_commit, size_t(2) * N * 4, hipMemcpyHostToDevice, s));
-  HIPCHK(h, hipEventRecord(h->ev_commit, s));
+  // the backup reads the ring rows the step wrote: after the caller's work
+  hipStream_t b = s;
+  if (h->backup) {
+    HIPCHK(h, hipEventRecord(h->ev_verified, s));
+    HIPCHK(h, hipStreamWaitEvent(h->backup, h->ev_verified, 0));
+    b = h->backup;
+  }
+  HIPCHK(h, hipMemcpyAsync(h->d_commit, h->h_commit, size_t(2) * N * 4, hipMemcpyHostToDevice, b));
+  HIPCHK(h, hipEventRecord(h->ev_commit, b));
   h->commit_pending = true;
   HIPCHK(h, launch_commit(h->d_commit_groups, c.n_groups, h->d_commit, h->d_commit + N, N, c.q_max, h->Rd, h->plen,
-                          h->tail_rows, h->row16, s));
+                          h->tail_rows, h->row16, b));
+  if (h->backup) HIPCHK(h, hipEventRecord(h->ev_backup[h->n_commits % 2], b));
+  h->n_commits += 1;
   for (int r = 0; r < N; ++r)
     if (accepted[r] >= 0) h->hist_len[r] += 1 + accepted[r];
   for (Group& G : h->grp) G.sel_valid = false;     // the step's selections end with its commit
@@ -1315,6 +1351,8 @@ int kv_hier_stats(kv_hier_t* h, int g, kv_hier_counters* cum, kv_hier_counters* 
     o->sel_resident = v[C_S_RES];
     o->sel_hot = v[C_S_HOT];
     o->sel_miss = v[C_S_MISS];
+    o->union_tail = v[C_U_TAIL];
+    o->sel_tail = v[C_S_TAIL];
     if (timing) {
       o->ms_ring = G.ms[K_RING];
       o->ms_plan = G.ms[K_PLAN];

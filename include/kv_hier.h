@@ -42,7 +42,8 @@
  *   - Location code (int32): tier in bits 30..29, index in bits 28..0,
  *     -1 = none.  Tier 0: hot slot r*B + slot; tier 1: staged row
  *     r*K_max*k + i of the group's arena; tier 2: resident pool index;
- *     tier 3 (kv_hier_read_rows only): ring row r*R_d + (pos mod R_d).
+ *     tier 3: ring row r*R_d + (pos mod R_d) (a selected row still in the
+ *     request's tail, Figure 2 callout 1).
  */
 #ifndef KV_HIER_H
 #define KV_HIER_H
@@ -146,6 +147,8 @@ typedef struct {
   /* kernel time in ms summed over timed calls (KV_FLAG_TIMING), and launch counts */
   double ms_ring, ms_plan, ms_gather, ms_attn, ms_combine, ms_promote, ms_victims;
   int64_t n_ring, n_plan, n_gather, n_attn, n_combine, n_promote, n_victims;
+  int64_t union_tail;       /* distinct rows resolved from the tail (the ring)           */
+  int64_t sel_tail;         /* selections resolved from the tail                         */
 } kv_hier_counters;
 
 /* Per-request lists of the last verify_step of a group (kv_hier_last_lists).
@@ -223,8 +226,10 @@ int kv_hier_ring_load(kv_hier_t *h, int g, int r, int32_t first_pos, const void 
  *              Reindex consumer of a shared source, whose producer already wrote
  *              this step's rows (the ring is left as it is)
  *   out        device bf16 [N][q_max][n_heads][d_v]; zero for inactive queries
- * Resolves the union of each request's selections, probes resident map then
- * hot cache, fetches every distinct missing row once from pinned host memory
+ * Resolves the union of each request's selections, probes the tail (rows the
+ * request's ring still holds: positions >= max(first ring position,
+ * n_r + q_max - R_d)) and the resident map, then the hot cache, fetches every
+ * distinct missing row once from pinned host memory
  * into the group's staging arena (on a side stream, overlapped with attention
  * of earlier request chunks), runs exact sparse attention of every query over
  * its own list plus its ring window, and copies promoted rows into their
@@ -260,8 +265,12 @@ int kv_hier_verify_reuse(kv_hier_t *h, int g, const void *queries, const int32_t
 /* Acceptance (eq. 7) for every request: accepted[r] = A_r in [0, q_max-1], or
  * -1 for no commit.  Copies the ring rows of positions n_r .. n_r+A_r of every
  * group into the pinned host backing and advances n_r by 1 + A_r; rejected
- * rows are never published.  Asynchronous on `stream`; accepted is host
- * memory read before return.  Caller contract: A_r < K_r of the last step. */
+ * rows are never published.  The host backup runs after `stream`'s work on a
+ * library stream, beside the next step (when R_d >= 2 q_max; else on
+ * `stream`): the rows it writes stay in the tail through the next step, which
+ * therefore never fetches them, and each step waits for the backup of the
+ * commit before the last.  accepted is host memory read before return.
+ * Caller contract: A_r < K_r of the last step. */
 int kv_hier_commit(kv_hier_t *h, const int32_t *accepted, void *stream);
 
 /* Waits for all work of the handle, then returns group g's counters:

@@ -12,7 +12,7 @@ from workloads import WORKLOADS, make_accepted, make_step_inputs, shrink
 
 pytestmark = pytest.mark.gpu
 
-TIER_TO_CLS = {2: 0, 0: 1, 1: 2}     # resident, hot, staged(miss) -> oracle class
+TIER_TO_CLS = {2: 0, 0: 1, 1: 2, 3: 3}     # resident, hot, staged(miss), ring(tail) -> oracle class
 
 
 def _cls_of(codes):
@@ -58,6 +58,7 @@ def compare_counts(pair, g, res):
                     ("union_hot", "union_hot"), ("union_miss", "union_miss"),
                     ("promoted", "promoted"), ("overflow", "overflow"),
                     ("sel_resident", "sel_resident"), ("sel_hot", "sel_hot"), ("sel_miss", "sel_miss"),
+                    ("union_tail", "union_tail"), ("sel_tail", "sel_tail"),
                     ("queries", "active_queries")):
         assert last[lk] == tot.get(key, 0), (key, last[lk], tot.get(key, 0))
     assert last["fetched_bytes"] == last["union_miss"] * 2 * pair.w.row_elems
@@ -301,4 +302,64 @@ def test_full_size_mla128_sampled():
         assert 0.12 < last["union_miss"] / last["union_rows"] < 0.16
         for r in reqs:
             _exact_vs_topk(pair, g, r, si.topk[r])
+    pair.lib.close()
+
+
+@pytest.mark.parametrize("window,page", [(8, 4), (2, 1)])
+def test_tail_rows_and_async_backup_over_rounds(window, page):
+    """Selections favour recently generated rows: rows still in the ring
+    resolve from it (tail), rows that left it are fetched from the host copy
+    that the asynchronous backup wrote.  R_d = 16 >= 2 K_max runs the backup
+    beside the next step; R_d = 6 < 2 K_max runs it ahead of it."""
+    w = _tiny(n_req=3, ring_window=window, ring_page=page, q_max=4, var_k=True, recent_frac=0.3,
+              recent_span=24)
+    pair = build_pair(w)
+    n = pair.hist_len.copy()
+    tail_seen = 0
+    for step in range(8):
+        si = make_step_inputs(w, 0, step + 1, n)
+        res = pair.orc.verify_step(0, si.topk, si.causal_pos, si.queries, si.block_rows)
+        out = run_lib_step(pair, 0, si)
+        compare_step(pair, 0, si, res, out)
+        compare_counts(pair, 0, res)
+        for r in range(w.n_req):
+            # every location holds its row; rows committed in earlier rounds are
+            # compared with the oracle's history, which its commits extended
+            L = pair.lib.last_lists(0, r)
+            loc = L["loc"].ravel()
+            sel = np.flatnonzero(loc >= 0)
+            rows = pair.lib.read_rows(0, loc[sel])
+            for x, e in zip(rows, si.topk[r].ravel()[sel]):
+                assert np.array_equal(x, pair.orc.hist[0].row(r, int(e))), ("row at location", r, int(e))
+        tail_seen += pair.lib.stats(0)[1]["union_tail"]
+        acc = make_accepted(w, step, si.k_active)
+        pair.orc.commit(acc)
+        pair.lib.commit(acc)
+        n = n + 1 + acc
+    pair.lib.sync()
+    for r in range(w.n_req):
+        np.testing.assert_array_equal(pair.lib.host_rows(0, 1, r)[: n[r]], pair.orc.hist[0].tails[r, : n[r]])
+    assert tail_seen > 0
+    pair.lib.close()
+
+
+def test_mla_recent_rows_two_groups():
+    w = _mla_small(recent_frac=0.05, recent_span=256)
+    pair = build_pair(w)
+    n = pair.hist_len.copy()
+    for step in range(3):
+        sis = []
+        for g in range(w.n_groups):
+            si = make_step_inputs(w, g, step, n)
+            res = pair.orc.verify_step(g, si.topk, si.causal_pos, si.queries, si.block_rows, n_threads=8)
+            out = run_lib_step(pair, g, si)
+            compare_step(pair, g, si, res, out)
+            compare_counts(pair, g, res)
+            sis.append(si)
+        acc = make_accepted(w, step, sis[0].k_active)
+        pair.orc.commit(acc)
+        pair.lib.commit(acc)
+        n = n + 1 + acc
+    _, last = pair.lib.stats(0)
+    assert last["union_tail"] > 0
     pair.lib.close()
