@@ -54,6 +54,15 @@ Readings where the pages leave a step open (each marked READING below):
      location tier 3, index r*R_d + (u mod R_d).  Tail rows are never
      inserted in the hot cache.
 
+Compressed sources (§3.3 eq. 8): a group whose stored rows each pack m
+consecutive token positions.  Its history rows are source rows; a list entry
+s is valid iff 0 <= s < floor(n_r / m) (complete rows only: the incomplete
+group stays in the tail as positions, reached by the ring branch); a commit
+from n to n' completes the source rows floor(n/m) <= s < floor(n'/m), whose
+bytes (the model's compressed rows) the caller supplies.  Selections of such
+a source never resolve from the tail (the ring holds positions, not source
+rows).
+
 Dynamic optional residency (§3.1, eqs. 3-4) is modelled in ``residency.py``;
 once attached, its ready map (shared by every group) is what step (1) of the
 resolution order consults, in place of the static resident sets.
@@ -87,6 +96,12 @@ def ring_rows(window: int, page: int, k_max: int) -> int:
 def ring_addr(slot: int, pos: int, r_d: int) -> int:
     """Eq. (10): phi(i, t) = i * R_d + (t mod R_d)."""
     return slot * r_d + (pos % r_d)
+
+
+def completed_rows(n: int, n_new: int, m: int) -> range:
+    """Eq. (8): source rows completed when the frontier moves from n to n_new,
+    floor(n/m) <= s < floor(n_new/m) (complete rows only)."""
+    return range(n // m, n_new // m)
 
 
 def staging_bytes(chi: int, n_slots: int, k_max: int, k: int, d_kv: int) -> int:
@@ -172,6 +187,7 @@ class HierOracle:
         self.last_k = {r: 0 for r in self.requests}
         self.opt = None                                   # dynamic optional residency (residency.py)
         self.last_sel = [None] * cfg.n_groups             # (topk, causal_pos, per-request activity)
+        self.m = [1] * cfg.n_groups                       # positions per stored row (eq. 8)
         self.st = [{r: _Req(slot_row=[-1] * cfg.hot_slots, slot_lu=[0] * cfg.hot_slots,
                             slot_of={}, res_idx={}, ring={}, ring_lo=self.n[r])
                     for r in self.requests} for _ in range(cfg.n_groups)]
@@ -211,6 +227,12 @@ class HierOracle:
             st.res_idx[s] = self.res_cursor[g]
             self.res_cursor[g] += 1
         st.resident_set = True
+
+    def set_compression(self, g: int, m: int):
+        """Group g stores one row per m consecutive positions (eq. 8)."""
+        if m < 1:
+            raise ValueError("m must be >= 1")
+        self.m[g] = int(m)
 
     def attach_residency(self, opt):
         """Dynamic optional residency: the ready map of `opt` (shared by every
@@ -267,13 +289,14 @@ class HierOracle:
         for r in self.requests:
             st = self.st[g][r]
             cp = [int(x) for x in causal_pos[r]]
-            n_r = cp[0]
-            if n_r < 0:
+            if cp[0] < 0:
                 res[r] = ReqResult(active=False, loc=np.full((Q, k), -1, dtype=np.int32))
                 self.last_k[r] = 0
                 continue
             J = [j for j in range(Q) if cp[j] >= 0]
             self.last_k[r] = len(J)
+            m = self.m[g]
+            n_r = cp[0] // m                              # complete stored rows (eq. 8)
             # Figure 3 callout 4: the rows of all K queries are written; eq. (10) places them.
             # A Reindex consumer of a shared source passes no rows: the source's
             # producer already wrote this step's block (§2, physical-source sharing).
@@ -299,7 +322,7 @@ class HierOracle:
             # Figure 2 / §3.2: (1) direct map, (2) hot cache, (3) host; R3
             cls = {}
             res_at = {}
-            tail_lo = max(st.ring_lo, n_r + Q - self.r_d)          # R9
+            tail_lo = max(st.ring_lo, n_r + Q - self.r_d) if m == 1 else n_r   # R9
             for u in U:
                 ri = self._resident(g, r, u)
                 if u >= tail_lo:
@@ -404,13 +427,14 @@ class HierOracle:
         for qi, (r, j) in enumerate(pairs):
             st = self.st[g][r]
             n_r = int(causal_pos[r][0])
+            n_src = n_r // self.m[g]
             p_j = int(causal_pos[r][j])
             qa = np.ascontiguousarray(queries[r][j], dtype=np.uint16)
             keep.append(qa)
             q_ptrs[qi] = qa.ctypes.data
             for e in topk[r][j]:
                 e = int(e)
-                if 0 <= e < n_r:
+                if 0 <= e < n_src:
                     ptrs.append(self.host_row(g, r, e).ctypes.data)
             for pos in self.window(g, r, n_r, p_j):
                 if pos not in st.ring:
@@ -423,10 +447,12 @@ class HierOracle:
         return {pr: out[i] for i, pr in enumerate(pairs)}
 
     # ------------------------------------------------------------- acceptance
-    def commit(self, accepted):
+    def commit(self, accepted, src_rows=None):
         """Eq. (7): the anchor and A_r accepted drafts join history,
         n' = n + 1 + A; committed rows get their host copy and rejected rows
-        are never published (§3.3, after eq. 8).  The step's selections end
+        are never published (§3.3, after eq. 8).  A compressed group (m > 1)
+        instead gains the source rows floor(n/m) <= s < floor(n'/m) (eq. 8),
+        taken from src_rows[g][r][s - floor(n/m)].  The step's selections end
         with it: nothing is left to reuse."""
         self.last_sel = [None] * self.cfg.n_groups
         for r in self.requests:
@@ -441,9 +467,15 @@ class HierOracle:
                 raise ValueError("history capacity exceeded")
             for g in range(self.cfg.n_groups):
                 st = self.st[g][r]
-                for pos in range(n, new_n):
-                    assert pos >= self.cfg.plen
-                    self.hist[g].tails[r, pos - self.cfg.plen] = st.ring[pos]
+                m = self.m[g]
+                if m == 1:
+                    for pos in range(n, new_n):
+                        assert pos >= self.cfg.plen
+                        self.hist[g].tails[r, pos - self.cfg.plen] = st.ring[pos]
+                else:
+                    for i, s_row in enumerate(completed_rows(n, new_n, m)):
+                        assert s_row >= self.cfg.plen
+                        self.hist[g].tails[r, s_row - self.cfg.plen] = np.asarray(src_rows[g][r][i], np.uint16)
                 for pos in [p for p in st.ring if p >= new_n]:
                     del st.ring[pos]
             self.n[r] = new_n

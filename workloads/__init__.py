@@ -16,5 +16,7 @@ from .gen import (  # noqa: F401
     make_hot_warm_set,
     make_resident_bitmaps,
     make_accepted,
+    make_source_rows,
+    positions_per_row,
     shrink,
 )

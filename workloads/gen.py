@@ -66,6 +66,8 @@ class Workload:
                               # size share one selection (and warm set / resident map)
     recent_frac: float = 0.0  # share of each list replaced by distinct rows of the last
     recent_span: int = 0      # recent_span history rows (recently generated rows)
+    compress: int = 1         # positions per stored row of the groups in compress_groups
+    compress_groups: tuple = ()
     note: str = ""
 
     @property
@@ -149,6 +151,11 @@ WORKLOADS = {w.name: w for w in (_tiny(), _mla32(), _mla128(), _mla128_res(), _m
 
 def _leader(w: Workload, group: int) -> int:
     return group - group % max(1, w.plan_share)
+
+
+def positions_per_row(w: Workload, group: int) -> int:
+    """m of a compressed source, 1 otherwise."""
+    return w.compress if group in w.compress_groups else 1
 
 
 def shrink(w: Workload, **kw) -> Workload:
@@ -297,9 +304,11 @@ def make_step_inputs(w: Workload, group: int, step: int, hist_len: np.ndarray,
             k_active = kr.integers(1, Q + 1, size=N).astype(np.int32)
     drawn = [None] * N
     req_iter = range(N) if requests is None else [int(x) for x in requests]
+    m = positions_per_row(w, group)
     for r in req_iter:
         rng = rngs[r]
-        n_r = int(hist_len[r])
+        n_pos = int(hist_len[r])
+        n_r = n_pos // m                  # stored rows the selections draw from
         kr = int(k_active[r])
         core_n = min(int(round(w.f_sh * k)), n_r)
         core = rng.choice(n_r, size=core_n, replace=False)
@@ -333,7 +342,7 @@ def make_step_inputs(w: Workload, group: int, step: int, hist_len: np.ndarray,
                 row[bad] = choices[rng.integers(0, choices.size, size=nb)]
             if j < kr:
                 topk[r, j] = row.astype(np.int32)
-                causal[r, j] = n_r + j
+                causal[r, j] = n_pos + j
                 privs.append(priv)
             queries[r, j] = _normal_bf16(rng, (w.n_heads, w.d_qk))
             block[r, j] = _normal_bf16(rng, (w.row_elems,))
@@ -356,9 +365,10 @@ def make_hot_warm_set(w: Workload, group: int, hist_len: np.ndarray, step_in: St
     rngs = _seeds(w, _leader(w, group), _P_WARM, n=w.n_req)
     out = [None] * w.n_req
     req_iter = range(w.n_req) if requests is None else [int(x) for x in requests]
+    m = positions_per_row(w, group)
     for r in req_iter:
         rng = rngs[r]
-        n_r = int(hist_len[r])
+        n_r = int(hist_len[r]) // m
         core, privs = step_in.drawn[r]
         drawn_all = np.unique(np.concatenate([core] + list(privs))) if privs else np.unique(core)
         core_sh = core[rng.permutation(core.size)]
@@ -395,6 +405,16 @@ def make_resident_bitmaps(w: Workload, group: int, hist_len: np.ndarray, rho: fl
         n_r = int(hist_len[r])
         bm[r, :n_r] = (rngs[r].random(n_r) < rho).astype(np.uint8)
     return bm
+
+
+def make_source_rows(w: Workload, group: int, step: int) -> np.ndarray:
+    """Stored rows a commit completes in a compressed source (the model's
+    compressed KV of each completed group of m positions): bf16
+    [N, ceil(q_max / m), row_elems], N(0, 1)."""
+    m = positions_per_row(w, group)
+    cmax = -(-w.q_max // m)
+    rng = _seeds(w, group, _P_ACCEPT, step, 5, n=1)[0]
+    return _normal_bf16(rng, (w.n_req, cmax, w.row_elems))
 
 
 def make_accepted(w: Workload, step: int, k_active: np.ndarray) -> np.ndarray:
