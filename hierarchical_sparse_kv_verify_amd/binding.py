@@ -33,6 +33,7 @@ EXPORTED = [
     "kv_hier_last_lists", "kv_hier_slot_table", "kv_hier_read_rows", "kv_hier_sync",
     "kv_hier_set_flags", "kv_hier_cache_snapshot", "kv_hier_opt_admit", "kv_hier_opt_complete",
     "kv_hier_opt_populate", "kv_hier_opt_publish", "kv_hier_opt_query", "kv_hier_verify_reuse",
+    "kv_hier_set_compression", "kv_hier_commit_src",
 ]
 
 
@@ -141,6 +142,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "kv_hier_verify_step": ([vp, i32, vp, vp, vp, vp, vp, vp], i32),
         "kv_hier_verify_reuse": ([vp, i32, vp, vp, vp, vp], i32),
         "kv_hier_commit": ([vp, vp, vp], i32),
+        "kv_hier_commit_src": ([vp, vp, vp, vp], i32),
+        "kv_hier_set_compression": ([vp, i32, ctypes.c_int32], i32),
         "kv_hier_stats": ([vp, i32, ctypes.POINTER(Counters), ctypes.POINTER(Counters)], i32),
         "kv_hier_reset_stats": ([vp], i32),
         "kv_hier_last_lists": ([vp, i32, i32, ctypes.POINTER(Lists)], i32),
@@ -293,9 +296,18 @@ class KVHier:
         self._check(self._lib.kv_hier_verify_reuse(self._h, g, _dev_ptr(queries), _dev_ptr(causal_pos),
                                                    _dev_ptr(out), _stream_handle(stream)))
 
-    def commit(self, accepted, stream=None):
+    def commit(self, accepted, stream=None, src_rows=None):
+        """src_rows: per group a device tensor of completed stored rows (compressed
+        sources) or None."""
         a = _i32(accepted)
-        self._check(self._lib.kv_hier_commit(self._h, a.ctypes.data, _stream_handle(stream)))
+        if src_rows is None:
+            self._check(self._lib.kv_hier_commit(self._h, a.ctypes.data, _stream_handle(stream)))
+            return
+        ptrs = (ctypes.c_void_p * len(src_rows))(*[None if x is None else _dev_ptr(x) for x in src_rows])
+        self._check(self._lib.kv_hier_commit_src(self._h, a.ctypes.data, ptrs, _stream_handle(stream)))
+
+    def set_compression(self, g: int, m: int):
+        self._check(self._lib.kv_hier_set_compression(self._h, g, int(m)))
 
     # -------------------------------------------------------------- read-back
     def stats(self, g: int):

@@ -46,6 +46,7 @@ struct PlanArgs {
   unsigned long long* cum;   // [C_NUM] cumulative
   int N, Q, k, B, L, t;
   int Rd;                    // ring rows per request (the tail: positions >= max(ring_lo, n_r + Q - Rd))
+  int m;                     // positions per stored row (compressed source when > 1: no tail)
   int has_resident;          // 0: the resident map holds no row (its lookups are skipped)
   int chunk_words;           // bitmap words per row chunk (rows per chunk = 32 * chunk_words)
   int sort_cap;              // power of two >= B
@@ -76,11 +77,14 @@ hipError_t launch_ring_write(const uint4* rows, const int32_t* causal, uint4* ri
 // setup gather from host: dst[dst_idx[i]] = host row (req[i], row[i]), i < n
 hipError_t launch_host_rows_to_dev(const HostRowSrc& src, const int32_t* req, const int32_t* rows,
                                    const int64_t* dst_idx, int n, uint4* dst, hipStream_t s);
-// commit: for r with acc[r] >= 0, rows pos = nbefore[r] .. nbefore[r]+acc[r] of every group:
-//   host tail row (pos - prefix_len) of r = ring row
-struct CommitGroup { const uint4* ring; uint4* tails; };
+// commit: for r with acc[r] >= 0, n = nbefore[r], n' = n + 1 + acc[r]:
+//   a group with m == 1: host tail row (pos - prefix_len) = ring row of pos, n <= pos < n';
+//   a group with m > 1 (eq. 8): host tail row (s - prefix_len) = src[g][r*cmax + s - n/m],
+//   n/m <= s < n'/m.  compressed = 0 handles the m == 1 groups, 1 the others.
+struct CommitGroup { const uint4* ring; uint4* tails; int m, cmax; };
 hipError_t launch_commit(const CommitGroup* groups, int G, const int32_t* nbefore, const int32_t* acc,
-                         int N, int Qmax, int Rd, int prefix_len, int tail_rows, int row16, hipStream_t s);
+                         const uint4* const* src, int compressed, int N, int Qmax, int Rd, int prefix_len,
+                         int tail_rows, int row16, hipStream_t s);
 // read rows at location codes into dst [n][row]
 struct PoolView { const uint4* hot; const uint4* staging; const uint4* resident; const uint4* ring; };
 hipError_t launch_read_rows(const PoolView& pv, const int32_t* locs, int n, uint4* dst, int row16,

@@ -99,20 +99,33 @@ __global__ __launch_bounds__(256) void host_rows_to_dev_kernel(HostRowSrc src, c
 
 __global__ __launch_bounds__(256) void commit_kernel(const CommitGroup* __restrict__ groups,
                                                      const int32_t* __restrict__ nbefore,
-                                                     const int32_t* __restrict__ acc, int Qmax, int Rd,
-                                                     int prefix_len, int tail_rows, int row16) {
+                                                     const int32_t* __restrict__ acc,
+                                                     const uint4* const* __restrict__ src, int compressed,
+                                                     int Qmax, int Rd, int prefix_len, int tail_rows, int row16) {
   const int r = blockIdx.y, g = blockIdx.z;
   const int a = acc[r];
-  if (a < 0) return;
+  const int m = groups[g].m;
+  if (a < 0 || (m > 1) != (compressed != 0)) return;
   const int n0 = nbefore[r];
-  const int total = (a + 1) * row16;
-  const uint4* ring = groups[g].ring;
   uint4* tails = groups[g].tails;
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x) {
-    const int d = i / row16, c = i % row16;
-    const int pos = n0 + d;
-    tails[(size_t(r) * tail_rows + (pos - prefix_len)) * row16 + c] =
-        ring[(size_t(r) * Rd + size_t(pos % Rd)) * row16 + c];
+  if (m == 1) {
+    const int total = (a + 1) * row16;
+    const uint4* ring = groups[g].ring;
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x) {
+      const int d = i / row16, c = i % row16;
+      const int pos = n0 + d;
+      tails[(size_t(r) * tail_rows + (pos - prefix_len)) * row16 + c] =
+          ring[(size_t(r) * Rd + size_t(pos % Rd)) * row16 + c];
+    }
+  } else {
+    // eq. (8): the stored rows completed by the new frontier
+    const int s0 = n0 / m, s1 = (n0 + a + 1) / m;
+    const int total = (s1 - s0) * row16;
+    const uint4* rows = src[g] + size_t(r) * groups[g].cmax * row16;
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x) {
+      const int d = i / row16, c = i % row16;
+      tails[(size_t(r) * tail_rows + (s0 + d - prefix_len)) * row16 + c] = rows[size_t(d) * row16 + c];
+    }
   }
   __threadfence_system();
 }
@@ -233,11 +246,12 @@ hipError_t launch_host_rows_to_dev(const HostRowSrc& src, const int32_t* req, co
   return hipGetLastError();
 }
 
-hipError_t launch_commit(const CommitGroup* groups, int G, const int32_t* nbefore, const int32_t* acc, int N,
-                         int Qmax, int Rd, int prefix_len, int tail_rows, int row16, hipStream_t s) {
+hipError_t launch_commit(const CommitGroup* groups, int G, const int32_t* nbefore, const int32_t* acc,
+                         const uint4* const* src, int compressed, int N, int Qmax, int Rd, int prefix_len,
+                         int tail_rows, int row16, hipStream_t s) {
   const unsigned gx = static_cast<unsigned>((Qmax * row16 + 255) / 256);
-  hipLaunchKernelGGL(commit_kernel, dim3(gx, N, G), dim3(256), 0, s, groups, nbefore, acc, Qmax, Rd,
-                     prefix_len, tail_rows, row16);
+  hipLaunchKernelGGL(commit_kernel, dim3(gx, N, G), dim3(256), 0, s, groups, nbefore, acc, src, compressed, Qmax,
+                     Rd, prefix_len, tail_rows, row16);
   return hipGetLastError();
 }
 

@@ -99,10 +99,13 @@ __global__ __launch_bounds__(kThreads) void plan_resolve_kernel(PlanArgs a) {
     if (tid < C_NUM) a.req_counts[size_t(r) * C_NUM + tid] = 0;
     return;
   }
-  const int n_r = n_raw < L ? n_raw : L;
+  // stored rows: complete groups of m positions (eq. 8)
+  const int n_src = n_raw / a.m;
+  const int n_r = n_src < L ? n_src : L;
   // the ring still holds positions >= tail_lo: this step's block (n_r ..
-  // n_r+Q-1) takes the slots of the positions below (eq. 10)
-  const int tail_lo = max(a.ring_lo[r], n_r + Q - a.Rd);
+  // n_r+Q-1) takes the slots of the positions below (eq. 10).  A compressed
+  // source's ring holds positions, not stored rows: no tail.
+  const int tail_lo = a.m == 1 ? max(a.ring_lo[r], n_r + Q - a.Rd) : n_r;
   uint32_t amask = 0;
   for (int j = 0; j < Q; ++j) amask |= (cp[j] >= 0 ? 1u : 0u) << j;
 

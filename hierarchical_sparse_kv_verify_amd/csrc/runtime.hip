@@ -64,6 +64,7 @@ struct Group {
   hipEvent_t ev_done = nullptr;     // copy-backs of the group's last step finished
   bool done_recorded = false;
   bool sel_valid = false;           // this step's selection may be reused (until commit)
+  int m = 1;                        // positions per stored row (compressed source when > 1)
   int64_t* req_counts = nullptr;
   unsigned long long* cum = nullptr;
   std::vector<void*> prefix_host;
@@ -156,6 +157,8 @@ struct kv_hier {
   std::vector<int32_t> hist_len;
   int32_t* d_commit = nullptr;
   int32_t* h_commit = nullptr;
+  const uint4** d_src = nullptr;    // per group: the caller's completed stored rows of a commit
+  const uint4** h_src = nullptr;    // pinned staging of those pointers
   hipEvent_t ev_commit = nullptr;
   bool commit_pending = false;
   // host backup of committed rows (eq. 7) on its own stream, after verification
@@ -387,6 +390,8 @@ void free_all(kv_hier* h) {
   (void)hipFree(h->d_commit);
   (void)hipFree(h->d_commit_groups);
   if (h->h_commit) (void)hipHostFree(h->h_commit);
+  (void)hipFree(const_cast<uint4**>(h->d_src));
+  if (h->h_src) (void)hipHostFree(const_cast<uint4**>(h->h_src));
   for (auto& t : h->pending) { (void)hipEventDestroy(t.a); (void)hipEventDestroy(t.b); }
   for (hipEvent_t e : h->pool) (void)hipEventDestroy(e);
   if (h->ev_in) (void)hipEventDestroy(h->ev_in);
@@ -772,6 +777,8 @@ static int create_impl(kv_hier* h) {
     for (int g = 0; g < c.n_groups; ++g) {
       cg[g].ring = reinterpret_cast<const uint4*>(h->grp[g].ring);
       cg[g].tails = const_cast<uint4*>(h->grp[g].tails_dev);
+      cg[g].m = 1;
+      cg[g].cmax = c.q_max;
     }
     if ((rc = dev_alloc(h, &h->d_commit_groups, cg.size(), nullptr))) return rc;
     if ((rc = upload(h, h->d_commit_groups, cg.data(), cg.size() * sizeof(CommitGroup)))) return rc;
@@ -781,6 +788,13 @@ static int create_impl(kv_hier* h) {
       return fail(h, KV_ENOMEM, "pinned commit buffer");
     }
     h->h_commit = static_cast<int32_t*>(hc);
+    const uint4** ds = nullptr;
+    if ((rc = dev_alloc(h, &ds, size_t(c.n_groups), nullptr))) return rc;
+    h->d_src = ds;
+    void* hs = nullptr;
+    if (hipHostMalloc(&hs, size_t(c.n_groups) * sizeof(void*), hipHostMallocDefault) != hipSuccess)
+      return fail(h, KV_ENOMEM, "pinned commit buffer");
+    h->h_src = static_cast<const uint4**>(hs);
   }
   if (c.fetch_cus > 0) {
     // partition the CUs: a few for the PCIe-latency-bound fetch, the rest for the step
@@ -963,7 +977,7 @@ int kv_hier_set_resident(kv_hier_t* h, int g, int r, const uint8_t* bitmap) {
   if (h->opt.on) return fail(h, KV_ESTATE, "static resident sets are not used with dynamic residency");
   Group& G = h->grp[g];
   if (G.res_set[r]) return fail(h, KV_ESTATE, "resident set of request %d already given", r);
-  const int lim = std::min(h->hist_len[r], h->L);
+  const int lim = std::min(h->hist_len[r] / G.m, h->L);
   std::vector<int64_t> idx, dst;
   std::vector<int32_t> val, req, src;
   for (int s = 0; s < lim; ++s)
@@ -1081,6 +1095,7 @@ int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t*
     pa.res_map = G.res_map;
     pa.ring_lo = G.ring_lo;
     pa.Rd = h->Rd;
+    pa.m = G.m;
     pa.has_resident = (h->opt.on ? h->opt.n_published > 0 : G.res_cursor > 0) ? 1 : 0;
     pa.slot_map = G.slot_map;
     pa.slot_row = G.slot_row;
@@ -1285,16 +1300,26 @@ int kv_hier_verify_reuse(kv_hier_t* h, int g, const void* queries, const int32_t
   return KV_OK;
 }
 
-int kv_hier_commit(kv_hier_t* h, const int32_t* accepted, void* stream) {
+int kv_hier_commit_src(kv_hier_t* h, const int32_t* accepted, const void* const* src_rows, void* stream) {
   if (!h || !accepted) return KV_EINVAL;
   const kv_hier_config& c = h->cfg;
-  const int N = c.n_req;
+  const int N = c.n_req, G = c.n_groups;
+  bool any_compressed = false;
+  for (int g = 0; g < G; ++g) {
+    if (h->grp[g].m == 1) continue;
+    any_compressed = true;
+    if (!src_rows || !src_rows[g])
+      return fail(h, KV_EINVAL, "group %d stores compressed rows: its completed rows are needed", g);
+  }
   for (int r = 0; r < N; ++r) {
     const int a = accepted[r];
     if (a < -1 || a >= c.q_max) return fail(h, KV_EINVAL, "accepted[%d] = %d outside [-1, %d)", r, a, c.q_max);
     if (a >= 0) {
       if (int64_t(h->hist_len[r]) + 1 + a > c.hist_cap) return fail(h, KV_EINVAL, "request %d: history full", r);
       if (h->hist_len[r] < h->plen) return fail(h, KV_EINVAL, "request %d: frontier inside the shared prefix", r);
+      for (int g = 0; g < G; ++g)
+        if (h->grp[g].m > 1 && h->hist_len[r] / h->grp[g].m < h->plen)
+          return fail(h, KV_EINVAL, "request %d: stored rows of group %d inside the shared prefix", r, g);
     }
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -1303,24 +1328,58 @@ int kv_hier_commit(kv_hier_t* h, const int32_t* accepted, void* stream) {
     h->h_commit[r] = h->hist_len[r];
     h->h_commit[N + r] = accepted[r];
   }
-  // the backup reads the ring rows the step wrote: after the caller's work
+  for (int g = 0; g < G; ++g)
+    h->h_src[g] = (src_rows && h->grp[g].m > 1) ? static_cast<const uint4*>(src_rows[g]) : nullptr;
+  // the previous backup still reads the commit buffers until it ends
+  if (h->backup && h->n_commits >= 1) HIPCHK(h, hipStreamWaitEvent(s, h->ev_backup[(h->n_commits - 1) % 2], 0));
+  HIPCHK(h, hipMemcpyAsync(h->d_commit, h->h_commit, size_t(2) * N * 4, hipMemcpyHostToDevice, s));
+  HIPCHK(h, hipMemcpyAsync(const_cast<uint4**>(h->d_src), h->h_src, size_t(G) * sizeof(void*),
+                           hipMemcpyHostToDevice, s));
+  HIPCHK(h, hipEventRecord(h->ev_commit, s));
+  h->commit_pending = true;
+  // compressed sources: the caller's rows are consumed in its stream order, so
+  // their host copy exists before the next step fetches (they have no tail)
+  if (any_compressed)
+    HIPCHK(h, launch_commit(h->d_commit_groups, G, h->d_commit, h->d_commit + N, h->d_src, 1, N, c.q_max, h->Rd,
+                            h->plen, h->tail_rows, h->row16, s));
+  // the other groups' backup reads the ring rows the step wrote: after the
+  // caller's work, on the backup stream when there is one
   hipStream_t b = s;
   if (h->backup) {
     HIPCHK(h, hipEventRecord(h->ev_verified, s));
     HIPCHK(h, hipStreamWaitEvent(h->backup, h->ev_verified, 0));
     b = h->backup;
   }
-  HIPCHK(h, hipMemcpyAsync(h->d_commit, h->h_commit, size_t(2) * N * 4, hipMemcpyHostToDevice, b));
-  HIPCHK(h, hipEventRecord(h->ev_commit, b));
-  h->commit_pending = true;
-  HIPCHK(h, launch_commit(h->d_commit_groups, c.n_groups, h->d_commit, h->d_commit + N, N, c.q_max, h->Rd, h->plen,
-                          h->tail_rows, h->row16, b));
+  HIPCHK(h, launch_commit(h->d_commit_groups, G, h->d_commit, h->d_commit + N, h->d_src, 0, N, c.q_max, h->Rd,
+                          h->plen, h->tail_rows, h->row16, b));
   if (h->backup) HIPCHK(h, hipEventRecord(h->ev_backup[h->n_commits % 2], b));
   h->n_commits += 1;
   for (int r = 0; r < N; ++r)
     if (accepted[r] >= 0) h->hist_len[r] += 1 + accepted[r];
-  for (Group& G : h->grp) G.sel_valid = false;     // the step's selections end with its commit
+  for (Group& G2 : h->grp) G2.sel_valid = false;     // the step's selections end with its commit
   return KV_OK;
+}
+
+int kv_hier_commit(kv_hier_t* h, const int32_t* accepted, void* stream) {
+  return kv_hier_commit_src(h, accepted, nullptr, stream);
+}
+
+int kv_hier_set_compression(kv_hier_t* h, int g, int32_t m) {
+  int rc = check_group(h, g);
+  if (rc) return rc;
+  Group& G = h->grp[g];
+  if (m < 1) return fail(h, KV_EINVAL, "positions per stored row must be >= 1");
+  if (G.calls > 0) return fail(h, KV_ESTATE, "group %d has already run a step", g);
+  if (m > 1 && h->opt.on) return fail(h, KV_ESTATE, "dynamic residency pages assume uncompressed sources");
+  if (m > 1 && h->share > 1) return fail(h, KV_ESTATE, "plan-sharing sets assume uncompressed sources");
+  if ((rc = sync_all(h))) return rc;
+  G.m = m;
+  CommitGroup cg;
+  cg.ring = reinterpret_cast<const uint4*>(G.ring);
+  cg.tails = const_cast<uint4*>(G.tails_dev);
+  cg.m = m;
+  cg.cmax = (h->cfg.q_max + m - 1) / m;
+  return upload(h, h->d_commit_groups + g, &cg, sizeof cg);
 }
 
 int kv_hier_stats(kv_hier_t* h, int g, kv_hier_counters* cum, kv_hier_counters* last) {

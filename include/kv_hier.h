@@ -273,6 +273,28 @@ int kv_hier_verify_reuse(kv_hier_t *h, int g, const void *queries, const int32_t
  * Caller contract: A_r < K_r of the last step. */
 int kv_hier_commit(kv_hier_t *h, const int32_t *accepted, void *stream);
 
+/* Compressed sources ("Adaptive DHiSparse" §3.3 eq. 8): group g stores one
+ * row per m consecutive token positions.  Its history rows (host rows,
+ * set_hot / set_resident indexes, topk_idx entries) are stored-row indexes;
+ * an entry s is a valid selection iff 0 <= s < floor(n_r / m): the
+ * incomplete group stays in the tail as positions, reached by the ring
+ * branch, whose rows (ring_rows, ring_load) stay per position.  Selections of
+ * such a group never resolve from the ring.  Call before the group's first
+ * step; m = 1 restores an uncompressed source.  KV_ESTATE with dynamic
+ * residency or plan-sharing sets (both assume uncompressed sources). */
+int kv_hier_set_compression(kv_hier_t *h, int g, int32_t m);
+
+/* kv_hier_commit for handles with compressed sources: src_rows is a host
+ * array of n_groups device pointers; for a group with m > 1 it points to bf16
+ * [N][ceil(q_max/m)][row_elems], row i of request r being the stored row
+ * floor(n_r/m) + i completed by the commit (eq. 8: floor(n_r/m) <= s <
+ * floor(n_r'/m)); entries of uncompressed groups are ignored (may be NULL).
+ * The completed rows get their host copy in `stream`'s order (before the next
+ * step can fetch them); the caller's buffers must stay valid until `stream`
+ * passes the commit.  kv_hier_commit on a handle with a compressed group is
+ * KV_EINVAL. */
+int kv_hier_commit_src(kv_hier_t *h, const int32_t *accepted, const void *const *src_rows, void *stream);
+
 /* Waits for all work of the handle, then returns group g's counters:
  * cumulative over all steps and of the last step.  Either pointer may be NULL. */
 int kv_hier_stats(kv_hier_t *h, int g, kv_hier_counters *cumulative, kv_hier_counters *last);

@@ -363,3 +363,46 @@ def test_mla_recent_rows_two_groups():
     _, last = pair.lib.stats(0)
     assert last["union_tail"] > 0
     pair.lib.close()
+
+
+def test_compressed_source_rounds():
+    """Eq. (8): group 1 stores one row per 4 positions.  Its selections name
+    complete stored rows, its ring holds positions, and each commit adds the
+    stored rows the new frontier completes (the caller's compressed rows).
+    Group 0 (uncompressed) runs beside it with the asynchronous backup."""
+    import torch
+    from hierarchical_sparse_kv_verify_amd import KVHierError
+    from workloads import make_source_rows
+    w = _mla_small(compress=4, compress_groups=(1,), var_k=True, n_prefix=0, prefix_len=0)
+    pair = build_pair(w)
+    pair.lib.set_compression(1, 4)
+    pair.orc.set_compression(1, 4)
+    n = pair.hist_len.copy()
+    for step in range(4):
+        sis = []
+        for g in range(w.n_groups):
+            si = make_step_inputs(w, g, step, n)
+            res = pair.orc.verify_step(g, si.topk, si.causal_pos, si.queries, si.block_rows, n_threads=8)
+            out = run_lib_step(pair, g, si)
+            compare_step(pair, g, si, res, out)
+            compare_counts(pair, g, res)
+            sis.append(si)
+        _, last = pair.lib.stats(1)
+        assert last["union_tail"] == 0 and last["selections"] > 0
+        acc = make_accepted(w, step, sis[0].k_active)
+        src = make_source_rows(w, 1, step)
+        if step == 0:
+            with pytest.raises(KVHierError):                   # compressed rows are required
+                pair.lib.commit(acc)
+        pair.orc.commit(acc, src_rows=[None, src])
+        pair.lib.commit(acc, src_rows=[None, torch.from_numpy(src.view(np.int16)).cuda()])
+        n = n + 1 + acc
+    pair.lib.sync()
+    for g in range(2):
+        for r in range(w.n_req):
+            np.testing.assert_array_equal(pair.lib.host_rows(g, 1, r), pair.orc.hist[g].tails[r],
+                                          err_msg="host rows g=%d r=%d" % (g, r))
+    with pytest.raises(KVHierError) as ei:                      # only before the group's first step
+        pair.lib.set_compression(1, 2)
+    assert ei.value.code == -4
+    pair.lib.close()

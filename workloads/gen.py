@@ -328,10 +328,10 @@ def make_step_inputs(w: Workload, group: int, step: int, hist_len: np.ndarray,
             row[: lst.size] = lst
             if w.recent_frac > 0:
                 cand = np.setdiff1d(np.arange(max(0, n_r - w.recent_span), n_r), row)
-                m = min(int(round(w.recent_frac * k)), cand.size)
-                if m:
-                    at = rng.choice(k, size=m, replace=False)
-                    row[at] = rng.choice(cand, size=m, replace=False)
+                n_rec = min(int(round(w.recent_frac * k)), cand.size)
+                if n_rec:
+                    at = rng.choice(k, size=n_rec, replace=False)
+                    row[at] = rng.choice(cand, size=n_rec, replace=False)
             if w.pad_frac > 0 or w.invalid_frac > 0:
                 u = rng.random(k)
                 row[u < w.pad_frac] = -1
