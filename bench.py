@@ -63,6 +63,13 @@ def parse():
                     help="layers reusing each selection (shared-source run)")
     ap.add_argument("--reselect-new", type=float, default=0.25,
                     help="share of a re-selecting layer's entries that differ from the first selection")
+    ap.add_argument("--rounds", type=int, default=0,
+                    help="decode rounds with commits (fresh selections each round): host backup beside "
+                         "the next step vs ahead of it")
+    ap.add_argument("--recent", type=float, default=0.02,
+                    help="rounds run: share of each list drawn from the last 128 rows")
+    ap.add_argument("--drift", type=float, default=0.1,
+                    help="rounds run: share of each list redrawn every round (the rest repeats round 0's)")
     return ap.parse_args()
 
 
@@ -80,6 +87,9 @@ def main():
         return
     if args.shared_source:
         shared_source(args)
+        return
+    if args.rounds > 0:
+        rounds(args)
         return
 
     import numpy as np
@@ -526,6 +536,81 @@ def shared_source(args):
             "reselect_fetched_rows": second, "select_fetched_rows": first}
     print(json.dumps(line), flush=True)
     lib.close()
+
+
+def rounds(args):
+    """Decode rounds over the hierarchy (Figure 3): every round verifies all
+    layer groups, then commits (eq. 7); nothing is restored between rounds.
+    Selections drift: each round redraws a seeded share of every list (a
+    share of those from the most recent rows) and keeps the rest of the first
+    round's, so the hot cache follows a slowly moving working set.  Arm
+    "async": the committed rows' host backup runs beside the next round
+    (those rows resolve from the tail meanwhile); arm "sync": it runs ahead of
+    the next round on the caller's stream (KV_FLAG_SYNC_BACKUP)."""
+    import numpy as np
+    import torch
+
+    from hierarchical_sparse_kv_verify_amd import KV_FLAG_SYNC_BACKUP
+    from tests.pair import build_pair, to_device
+    from workloads import WORKLOADS, make_accepted, make_history, make_step_inputs, shrink
+    from workloads.gen import make_hist_len
+
+    w = shrink(WORKLOADS[args.workload], recent_frac=args.recent, recent_span=128)
+    torch.cuda.set_device(0)
+    G, R = w.n_groups, args.rounds
+    hl = make_hist_len(w)
+    hists = [make_history(w, g, hl) for g in range(G)]
+    log("rounds: generating %d rounds of inputs" % (R + args.warmup))
+    plan = []
+    n = hl.copy()
+    base = [make_step_inputs(w, g, 100, hl) for g in range(G)]
+    for i in range(R + args.warmup):
+        sis = [make_step_inputs(w, g, 101 + i, n) for g in range(G)]
+        for g, si in enumerate(sis):
+            keep = np.random.default_rng([20261009, 3, g, 500 + i]).random(si.topk.shape) >= args.drift
+            si.topk = np.where(keep & (si.topk >= 0), base[g].topk, si.topk).astype(np.int32)
+        acc = make_accepted(w, i, sis[0].k_active)
+        plan.append(([to_device(si) for si in sis], acc))
+        n = n + 1 + acc
+    report = {}
+    for arm in ("async", "sync"):
+        pair = build_pair(w, with_oracle=False, histories=hists,
+                          lib_kw=dict(flags=KV_FLAG_SYNC_BACKUP if arm == "sync" else 0))
+        lib = pair.lib
+        out = torch.zeros((w.n_req, w.q_max, w.n_heads, w.d_v), dtype=torch.int16, device="cuda")
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        tails = sels = fetched = 0
+        for i, (devs, acc) in enumerate(plan):
+            if i == args.warmup:
+                torch.cuda.synchronize()
+                lib.reset_stats()
+                ev0.record()
+            for g in range(G):
+                d = devs[g]
+                lib.verify_step(g, d["queries"], d["topk"], d["causal"], d["ring"], out)
+            lib.commit(acc)
+        ev1.record()
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / R
+        cum = [lib.stats(g)[0] for g in range(G)]
+        tok = sum(int(c["active_queries"]) for c in cum) / G / R
+        report[arm] = dict(ms_per_round=round(ms, 4), query_tokens_per_s=round(tok / (ms / 1000.0), 1),
+                           tail_share_selected=round(sum(int(c["sel_tail"]) for c in cum) /
+                                                     max(1, sum(int(c["selections"]) for c in cum)), 5),
+                           host_share_distinct=round(sum(int(c["union_miss"]) for c in cum) /
+                                                     max(1, sum(int(c["union_rows"]) for c in cum)), 5),
+                           fetched_mb_per_round=round(sum(int(c["union_miss"]) for c in cum) * 2 * w.row_elems
+                                                      / R / 1e6, 2))
+        log("rounds: arm %s: %s" % (arm, report[arm]))
+        lib.close()
+        del pair, lib
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "decode rounds with commits: host backup beside vs ahead of the next round",
+                      "unit": "ms per round", "n_gpus": 1, "data": "synthetic", "rounds": R,
+                      "warmup": args.warmup,
+                      "config": {"workload": w.name, "requests": w.n_req, "layer_groups": G,
+                                 "recent_share": args.recent, "recent_span": 128, "drift": args.drift},
+                      "arms": report}), flush=True)
 
 
 def measure_h2d(torch, mib=512, reps=3):

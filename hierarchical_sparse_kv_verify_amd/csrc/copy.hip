@@ -127,7 +127,9 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitGroup* __restri
       tails[(size_t(r) * tail_rows + (s0 + d - prefix_len)) * row16 + c] = rows[size_t(d) * row16 + c];
     }
   }
-  __threadfence_system();
+  // no fence: later readers of these host rows are kernels ordered after this
+  // one by stream events (its completion makes the writes visible) or the host
+  // after a synchronisation
 }
 
 __global__ __launch_bounds__(256) void read_rows_kernel(PoolView pv, const int32_t* __restrict__ locs, int n,
@@ -249,8 +251,8 @@ hipError_t launch_host_rows_to_dev(const HostRowSrc& src, const int32_t* req, co
 hipError_t launch_commit(const CommitGroup* groups, int G, const int32_t* nbefore, const int32_t* acc,
                          const uint4* const* src, int compressed, int N, int Qmax, int Rd, int prefix_len,
                          int tail_rows, int row16, hipStream_t s) {
-  const unsigned gx = static_cast<unsigned>((Qmax * row16 + 255) / 256);
-  hipLaunchKernelGGL(commit_kernel, dim3(gx, N, G), dim3(256), 0, s, groups, nbefore, acc, src, compressed, Qmax,
+  // one workgroup per (request, group): at most K_max rows of row16 chunks each
+  hipLaunchKernelGGL(commit_kernel, dim3(1, N, G), dim3(256), 0, s, groups, nbefore, acc, src, compressed, Qmax,
                      Rd, prefix_len, tail_rows, row16);
   return hipGetLastError();
 }

@@ -162,7 +162,7 @@ struct kv_hier {
   hipEvent_t ev_commit = nullptr;
   bool commit_pending = false;
   // host backup of committed rows (eq. 7) on its own stream, after verification
-  hipStream_t backup = nullptr;     // null: backups run on the caller's stream
+  hipStream_t backup = nullptr;     // the copy-back stream, or null: backups run on the caller's stream
   hipEvent_t ev_verified = nullptr; // the step's ring rows are written (caller's stream)
   hipEvent_t ev_backup[2] = {nullptr, nullptr};
   int64_t n_commits = 0;
@@ -401,7 +401,6 @@ void free_all(kv_hier* h) {
   if (h->ev_verified) (void)hipEventDestroy(h->ev_verified);
   for (hipEvent_t e : h->ev_backup)
     if (e) (void)hipEventDestroy(e);
-  if (h->backup) (void)hipStreamDestroy(h->backup);
   for (auto& v : h->ev_fetched) for (hipEvent_t e : v) (void)hipEventDestroy(e);
   for (auto& v : h->ev_free) for (hipEvent_t e : v) (void)hipEventDestroy(e);
   for (hipEvent_t e : h->ev_attn) (void)hipEventDestroy(e);
@@ -826,8 +825,10 @@ static int create_impl(kv_hier* h) {
   // Asynchronous host backup needs every row of the last commit to stay in the
   // ring's tail through the next step (R_d >= 2 K_max); otherwise the backup
   // runs on the caller's stream, ahead of the next step.
+  // It shares the copy-back stream: one more stream would share a hardware
+  // queue with another and add false dependencies.
   if (h->Rd >= 2 * c.q_max) {
-    HIPCHK(h, hipStreamCreateWithFlags(&h->backup, hipStreamNonBlocking));
+    h->backup = h->aux;
     HIPCHK(h, hipEventCreateWithFlags(&h->ev_verified, hipEventDisableTiming));
     for (hipEvent_t& e : h->ev_backup) HIPCHK(h, hipEventCreateWithFlags(&e, hipEventDisableTiming));
   }
@@ -1345,7 +1346,8 @@ int kv_hier_commit_src(kv_hier_t* h, const int32_t* accepted, const void* const*
   // the other groups' backup reads the ring rows the step wrote: after the
   // caller's work, on the backup stream when there is one
   hipStream_t b = s;
-  if (h->backup) {
+  const bool async = h->backup && !(c.flags & KV_FLAG_SYNC_BACKUP);
+  if (async) {
     HIPCHK(h, hipEventRecord(h->ev_verified, s));
     HIPCHK(h, hipStreamWaitEvent(h->backup, h->ev_verified, 0));
     b = h->backup;
@@ -1537,7 +1539,7 @@ int kv_hier_sync(kv_hier_t* h) {
 
 int kv_hier_set_flags(kv_hier_t* h, int32_t flags) {
   if (!h) return KV_EINVAL;
-  if (flags & ~(KV_FLAG_TIMING | KV_FLAG_POISON | KV_FLAG_TIMING_ATTN | KV_FLAG_SERIAL))
+  if (flags & ~(KV_FLAG_TIMING | KV_FLAG_POISON | KV_FLAG_TIMING_ATTN | KV_FLAG_SERIAL | KV_FLAG_SYNC_BACKUP))
     return fail(h, KV_EINVAL, "unknown flags %d", flags);
   int rc = sync_all(h);
   if (rc) return rc;

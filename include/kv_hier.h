@@ -72,8 +72,10 @@ enum {
                             and its next fetch (and a dynamic pool at create)            */
   KV_FLAG_TIMING_ATTN = 4, /* time only the attention (and split-combine) launches: the
                               events then sit on no stream that gates the host fetch   */
-  KV_FLAG_SERIAL = 8      /* measurement: the step's attention starts only after its whole
+  KV_FLAG_SERIAL = 8,     /* measurement: the step's attention starts only after its whole
                              host fetch, so it runs alone on the GPU (slower steps)     */
+  KV_FLAG_SYNC_BACKUP = 16 /* measurement: commit's host backup runs on the caller's stream,
+                             ahead of the next step, instead of beside it             */
 };
 
 typedef struct kv_hier kv_hier_t;  /* opaque, owned by the library */
