@@ -17,15 +17,20 @@
 //    meet in LDS) and the value width for O^T; each of the four then owns a
 //    quarter of the tile's rows for the softmax (reduce-scatter), so every
 //    score is exponentiated once; probabilities go to LDS as bf16 P^T.
-//  - a tile lives in LDS once, row-major with a 1168-byte row stride (36
-//    banks apart), double-buffered; K fragments are plain 16-byte reads and
-//    V^T fragments come from the same rows through ds_read_b64_tr_b16, with
-//    the value dims of an MFMA block interleaved (8 dims from each 32-dim
-//    group) so that both read patterns hit every bank once.
-//  - rows are gathered one tile ahead into registers: the 32 location codes
-//    of a tile are loaded one tile earlier, each wave decodes the codes of
-//    its own rows into wave-uniform addresses, and masked positions read a
-//    zero row, so no load depends on a per-lane branch.
+//  - a tile lives in LDS once; K fragments are plain 16-byte reads and V^T
+//    fragments come from the same rows through ds_read_b64_tr_b16, with the
+//    value dims of an MFMA block interleaved (8 dims from each 32-dim group)
+//    so that both read patterns hit every bank once per half-wave.
+//  - rows of 72 16-byte chunks (absorbed MLA) go straight from memory to LDS
+//    (global_load_lds, three tile buffers, tile t+2 issued while tile t
+//    computes): chunks 0..63 of a row land in its head-region slot (1040-byte
+//    stride, 4 banks apart), chunks 64..71 in a swizzled tail region; the
+//    location codes travel the same way, two tiles ahead.  Other row widths
+//    are gathered one tile ahead into registers and stored to a double
+//    buffer with a 36-bank stride.  Either way each wave decodes the codes
+//    of its own rows into wave-uniform addresses (readlane / lane permute),
+//    and masked positions read a zero row, so no load depends on a per-lane
+//    branch.
 //  - online softmax in fp32 with exp2 (scale folded with log2 e): the running
 //    max of a head is raised only when a score exceeds it by more than 2^8,
 //    detected per tile with one ballot; the rare raise takes a second pass
@@ -84,15 +89,28 @@ struct Cfg {
   static constexpr int KSTR = ROW + 2 * ((36 - ROW_DW % 64 + 64) % 64);
   static constexpr int KBUF = TILE * KSTR;   // elements per tile buffer
   static constexpr int PSTR = TILE + 8;      // P^T row stride (elements): 20 banks
-  static constexpr size_t LDS_K = size_t(2) * KBUF * 2;
+  // LDS DMA layout (rows of 72 chunks): chunks 0..63 of tile row r at
+  // r*HSTR (260 dwords: 16 consecutive rows hit distinct banks), chunks 64..71
+  // at TAILO + r*64 in slot order c ^ tail_swz(r); three buffers, and per
+  // wave three 64-entry slots of location codes.
+  static constexpr bool DMA = WIDE && REST == 8;
+  static constexpr int HSTR = 520;
+  static constexpr int TAILO = TILE * HSTR;
+  static constexpr int NBUF = DMA ? 3 : 2;
+  static constexpr int BSTR = DMA ? TAILO + TILE * 64 : KBUF;   // elements per tile buffer
+  static constexpr int RSTR = DMA ? HSTR : KSTR;                 // row stride of the K / V reads
+  static constexpr int NVM = RPW + 2;      // DMA instructions per wave and tile (rows, tail, codes)
+  static constexpr size_t LDS_K = size_t(NBUF) * BSTR * 2;
   static constexpr size_t LDS_S = size_t(NW) * 4 * 64 * 16;
   static constexpr size_t LDS_P = size_t(HB) * 32 * PSTR * 2;
   static constexpr size_t LDS_M = size_t(NW) * 32 * 4;
-  static constexpr size_t LDS = LDS_K + LDS_S + LDS_P + LDS_M + 16;
+  static constexpr size_t LDS_C = DMA ? size_t(3) * NW * 64 * 4 : 0;
+  static constexpr size_t LDS = LDS_K + LDS_S + LDS_P + LDS_M + LDS_C + 16;
   static_assert(D_QK % (NDP * 16) == 0 && D_V % (NDP * 32) == 0 && ROW % 8 == 0, "shape");
   static_assert(V_OFF % 8 == 0 && V_OFF + D_V <= ROW && D_QK <= ROW, "row layout");
   static_assert(WIDE ? (REST <= 64 && 64 % REST == 0) : (64 % RCH == 0 && (RPW * RCH) % 64 == 0), "gather");
   static_assert(LDS <= 160 * 1024, "LDS");
+  static_assert(!DMA || (RPW * 8 <= 64 && NVM <= 15), "DMA tile");
 };
 
 struct RowCtx {
@@ -196,6 +214,77 @@ __device__ __forceinline__ void gather_store(const Gather<C>& g, uint16_t* kb, i
   }
 }
 
+// LDS DMA: each lane's 16 (or 4) bytes land at the wave-uniform LDS address
+// plus lane*16 (lane*4).  Issued as inline assembly so that the compiler
+// neither counts these loads nor inserts waits for them: each wait is explicit
+// (vmcnt before the barrier that publishes a tile).  Waiting with vmcnt(N)
+// completes every vector-memory instruction older than the N most recent, so
+// other loads interleaved by the compiler can only lengthen a wait.  The LDS
+// offset is the low word of the generic address of dynamic shared memory.
+__device__ __forceinline__ void dma16(uintptr_t gaddr, const void* lds_dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_dst)));
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gaddr), "{m0}"(m0) : "memory");
+}
+__device__ __forceinline__ void dma4(uintptr_t gaddr, const void* lds_dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_dst)));
+  asm volatile("global_load_lds_dword %0, off" ::"v"(gaddr), "{m0}"(m0) : "memory");
+}
+
+// Workgroup barrier after this wave's LDS writes completed; vector-memory
+// loads (tile DMA) stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+}
+// The same after all but the N most recent vector-memory instructions
+// completed (s_waitcnt encoding: vmcnt bits 3:0 and 15:14, lgkmcnt 0).
+template <int N>
+__device__ __forceinline__ void lds_vm_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70);
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// Tail-region slot swizzle of tile row r: chunk 64+c sits in slot c ^ tail_swz(r)
+// (16 consecutive rows reading one chunk hit distinct banks).
+__device__ __forceinline__ int tail_swz(int r) { return (r >> 1) & 7; }
+
+// DMA of the raw codes of tile t into this wave's 64-entry slot (lanes l and
+// l+32 load the code of row l; positions past the list are clamped into it
+// and rewritten by final_code).  One instruction.
+template <class C>
+__device__ __forceinline__ void dma_codes(int32_t* slot, const RowCtx& c, int t, int w, int lane) {
+  const int idx = min(t * TILE + (lane & 31), c.k - 1);
+  dma4(reinterpret_cast<uintptr_t>(c.loc + idx), slot + w * 64);
+}
+
+// DMA of one tile: lanes l and l+32 hold the code of tile row l; wave w moves
+// rows w*RPW .. w*RPW+RPW-1, one instruction per row for chunks 0..63 and one
+// for the rows' chunks 64..71 (RPW*8 lanes).  RPW+1 instructions.  Returns
+// the tile's live-row mask.
+template <class C>
+__device__ __forceinline__ uint32_t dma_tile(uint16_t* dst, const RowCtx& ctx, int code, int w, int lane) {
+  const uint32_t live = static_cast<uint32_t>(__builtin_amdgcn_ballot_w64(code >= 0));
+  const uintptr_t my = row_addr<C::ROW>(ctx, code);
+  const int mlo = static_cast<int>(static_cast<uint32_t>(my));
+  const int mhi = static_cast<int>(static_cast<uint32_t>(my >> 32));
+  {
+    const int row = w * C::RPW + ((lane >> 3) & (C::RPW - 1));
+    const uintptr_t base = (uintptr_t(uint32_t(__shfl(mhi, row, 64))) << 32) | uint32_t(__shfl(mlo, row, 64));
+    const int cp = (lane & 7) ^ tail_swz(row);
+    if (C::RPW * 8 == 64 || lane < C::RPW * 8)
+      dma16(base + size_t(64 + cp) * 16, dst + C::TAILO + w * C::RPW * 64);
+  }
+#pragma unroll
+  for (int u = 0; u < C::RPW; ++u) {
+    const int row = w * C::RPW + u;
+    const uintptr_t base = (uintptr_t(uint32_t(__builtin_amdgcn_readlane(mhi, row))) << 32) |
+                           uint32_t(__builtin_amdgcn_readlane(mlo, row));
+    dma16(base + size_t(lane) * 16, dst + row * C::HSTR);
+  }
+  return live;
+}
+
 template <class C>
 __global__ __launch_bounds__(C::NT, 1) void attn_kernel(AttnArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
@@ -203,7 +292,8 @@ __global__ __launch_bounds__(C::NT, 1) void attn_kernel(AttnArgs a) {
   float4* Sx = reinterpret_cast<float4*>(lds + C::LDS_K);
   uint16_t* Pb = reinterpret_cast<uint16_t*>(lds + C::LDS_K + C::LDS_S);
   float* Mx = reinterpret_cast<float*>(lds + C::LDS_K + C::LDS_S + C::LDS_P);
-  uint8_t* flags = reinterpret_cast<uint8_t*>(lds + C::LDS_K + C::LDS_S + C::LDS_P + C::LDS_M);
+  int32_t* Cs = reinterpret_cast<int32_t*>(lds + C::LDS_K + C::LDS_S + C::LDS_P + C::LDS_M);   // DMA only
+  uint8_t* flags = reinterpret_cast<uint8_t*>(lds + C::LDS_K + C::LDS_S + C::LDS_P + C::LDS_M + C::LDS_C);
 
   const int nreq = a.r1 - a.r0;
   const int per_req = a.Q * a.head_groups * a.splits;
@@ -280,24 +370,51 @@ __global__ __launch_bounds__(C::NT, 1) void attn_kernel(AttnArgs a) {
   const float sl2 = a.scale_log2;
   const int crow = lane & 31;                          // tile row whose code this lane holds
 
-  // prologue: tile tb into LDS buffer 0, tile tb+1 in flight, codes of tb+2 in flight
+  // tile t lives in buffer (t - tb) mod NBUF; with DMA its codes in slot (t - tb) mod 3
+  auto kbuf = [&](int t) { return Kb + ((t - tb) % C::NBUF) * C::BSTR; };
+  auto cslot = [&](int t) { return Cs + ((t - tb) % 3) * (C::NW * 64); };
   Gather<C> g;
-  int code = final_code(ctx, tb * TILE + crow, raw_code(ctx, tb * TILE + crow));
-  uint32_t live_cur = gather_issue<C>(g, ctx, code, w, lane);
-  int raw = raw_code(ctx, (tb + 1) * TILE + crow);
-  gather_store<C>(g, Kb, w, lane);
-  uint32_t live_n1 = gather_issue<C>(g, ctx, final_code(ctx, (tb + 1) * TILE + crow, raw), w, lane);
-  raw = raw_code(ctx, (tb + 2) * TILE + crow);
-  __syncthreads();
+  uint32_t live_cur, live_n1;
+  int raw = 0;
+  if constexpr (C::DMA) {
+    // prologue: codes of tb and tb+1; DMA of tiles tb, tb+1 and of the codes
+    // of tb+2, tb+3; tile tb landed in every wave before the first scores
+    __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0): Q fragments in registers
+    dma_codes<C>(cslot(tb), ctx, tb, w, lane);
+    dma_codes<C>(cslot(tb + 1), ctx, tb + 1, w, lane);
+    __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0)
+    live_cur = dma_tile<C>(kbuf(tb), ctx, final_code(ctx, tb * TILE + crow, cslot(tb)[w * 64 + lane]), w, lane);
+    dma_codes<C>(cslot(tb + 2), ctx, tb + 2, w, lane);
+    const int code1 = tb + 1 < te ? final_code(ctx, (tb + 1) * TILE + crow, cslot(tb + 1)[w * 64 + lane]) : -1;
+    live_n1 = dma_tile<C>(kbuf(tb + 1), ctx, code1, w, lane);
+    dma_codes<C>(cslot(tb + 3), ctx, tb + 3, w, lane);
+    lds_vm_barrier<C::NVM>();
+  } else {
+    // prologue: tile tb into LDS buffer 0, tile tb+1 in flight, codes of tb+2 in flight
+    int code = final_code(ctx, tb * TILE + crow, raw_code(ctx, tb * TILE + crow));
+    live_cur = gather_issue<C>(g, ctx, code, w, lane);
+    raw = raw_code(ctx, (tb + 1) * TILE + crow);
+    gather_store<C>(g, Kb, w, lane);
+    live_n1 = gather_issue<C>(g, ctx, final_code(ctx, (tb + 1) * TILE + crow, raw), w, lane);
+    raw = raw_code(ctx, (tb + 2) * TILE + crow);
+    __syncthreads();
+  }
 
-  // per-lane LDS offsets (elements) inside a tile buffer
-  const int k_off = (lane & 31) * C::KSTR + dq * (C::D_QK / C::NDP) + hi_half * 8;
+  // per-lane LDS offsets (elements) inside a tile buffer: K fragment of k-step
+  // ks = row crow, chunk of dims dq*D_QK/4 + 16ks + 8hi
+  int koff[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    const int c = (dq * (C::D_QK / C::NDP) + ks * 16 + hi_half * 8) / 8;
+    koff[ks] = !C::DMA || c < 64 ? crow * C::RSTR + c * 8
+                                 : C::TAILO + crow * 64 + (((c - 64) ^ tail_swz(crow)) * 8);
+  }
   int v_off;
   {
     const int gq = (lane >> 4) & 3, s = lane & 15, aq = s & 3;
     const int row = (gq >> 1) * 8 + (s >> 2);
     const int dim = C::V_OFF + vq0 + ((gq & 1) * 2 + (aq >> 1)) * (8 * C::DVB) + (aq & 1) * 4;
-    v_off = row * C::KSTR + dim;
+    v_off = row * C::RSTR + dim;
   }
   float4* sx_own = Sx + size_t(w) * 4 * 64 + lane;
   const float4* sx_red = Sx + size_t(hb * C::NDP) * 4 * 64 + dq * 64 + lane;   // + q * 256
@@ -306,8 +423,7 @@ __global__ __launch_bounds__(C::NT, 1) void attn_kernel(AttnArgs a) {
   const int sbit0 = dq * 8 + hi_half * 4;              // first tile row of this lane's quarter
 
   for (int t = tb; t < te; ++t) {
-    const int buf = (t - tb) & 1;
-    const uint16_t* kb = Kb + buf * C::KBUF;
+    const uint16_t* kb = kbuf(t);
 
     // partial scores over this wave's part of the key width
     f32x16 acc;
@@ -315,20 +431,32 @@ __global__ __launch_bounds__(C::NT, 1) void attn_kernel(AttnArgs a) {
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-      const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + k_off + ks * 16));
+      const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + koff[ks]));
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[ks], acc, 0, 0, 0);
     }
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4)
       sx_own[i4 * 64] = make_float4(acc[4 * i4], acc[4 * i4 + 1], acc[4 * i4 + 2], acc[4 * i4 + 3]);
-    __syncthreads();
-
-    // tile t+1 into the other buffer (its last reader, PV of tile t-1, is done);
-    // issue tile t+2 and the codes of tile t+3 (unconditional: positions past
-    // the range read the zero row and are never used)
-    gather_store<C>(g, Kb + (buf ^ 1) * C::KBUF, w, lane);
-    const uint32_t live_n2 = gather_issue<C>(g, ctx, final_code(ctx, (t + 2) * TILE + crow, raw), w, lane);
-    raw = raw_code(ctx, (t + 3) * TILE + crow);
+    uint32_t live_n2;
+    if constexpr (C::DMA) {
+      lds_barrier();
+      // DMA of tile t+2 into the buffer of tile t-1 (its last readers, the PV
+      // products of t-1, finished before the barrier) and of the codes of
+      // tile t+4 into the slot of t+1; issued unconditionally so that every
+      // wave keeps NVM instructions per tile (tiles past the range read the
+      // zero row and are never used)
+      const int code = t + 2 < te ? final_code(ctx, (t + 2) * TILE + crow, cslot(t + 2)[w * 64 + lane]) : -1;
+      live_n2 = dma_tile<C>(kbuf(t + 2), ctx, code, w, lane);
+      dma_codes<C>(cslot(t + 4), ctx, t + 4, w, lane);
+    } else {
+      __syncthreads();
+      // tile t+1 into the other buffer (its last reader, PV of tile t-1, is done);
+      // issue tile t+2 and the codes of tile t+3 (unconditional: positions past
+      // the range read the zero row and are never used)
+      gather_store<C>(g, kbuf(t + 1), w, lane);
+      live_n2 = gather_issue<C>(g, ctx, final_code(ctx, (t + 2) * TILE + crow, raw), w, lane);
+      raw = raw_code(ctx, (t + 3) * TILE + crow);
+    }
 
     // this wave's quarter of the rows: scores summed over the key parts in order
     float s[4];
@@ -363,7 +491,10 @@ __global__ __launch_bounds__(C::NT, 1) void attn_kernel(AttnArgs a) {
     }
     const bool any_over = __builtin_amdgcn_ballot_w64(over) != 0;
     if (lane == 0) flags[w] = any_over ? 1 : 0;
-    __syncthreads();
+    if constexpr (C::DMA)
+      lds_vm_barrier<C::NVM>();                        // and tile t+1 landed in every wave
+    else
+      __syncthreads();
 
     const bool slow = C::NW == 8 ? *reinterpret_cast<const uint64_t*>(flags) != 0
                                  : *reinterpret_cast<const uint32_t*>(flags) != 0;
@@ -408,9 +539,9 @@ __global__ __launch_bounds__(C::NT, 1) void attn_kernel(AttnArgs a) {
       const bf16x8 pb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p_rd + ks2 * 16));
 #pragma unroll
       for (int d = 0; d < C::DVB; ++d) {
-        const uint16_t* vp = kb + v_off + ks2 * 16 * C::KSTR + d * 8;
+        const uint16_t* vp = kb + v_off + ks2 * 16 * C::RSTR + d * 8;
         const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp));
-        const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 4 * C::KSTR));
+        const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 4 * C::RSTR));
         const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
         O[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, O[d], 0, 0, 0);
       }
@@ -418,6 +549,7 @@ __global__ __launch_bounds__(C::NT, 1) void attn_kernel(AttnArgs a) {
     live_cur = live_n1;
     live_n1 = live_n2;
   }
+  if constexpr (C::DMA) __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0): no DMA outlives the loop
 
   // normaliser: this wave's rows, both lane halves, then the four quarters in order
   float l2 = l_run + __shfl_xor(l_run, 32, 64);

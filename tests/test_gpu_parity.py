@@ -202,6 +202,22 @@ def test_mla_128_heads_split_keys():
     pair.lib.close()
 
 
+@pytest.mark.parametrize("n_heads", [32, 16])
+def test_mla_one_head_block_split_keys(n_heads):
+    """Absorbed-MLA rows with at most 32 heads: one 32-head block per
+    workgroup (four waves, eight rows of every tile per wave), heads past H
+    masked, key splits merged by the combine pass."""
+    w = _mla_small(n_req=2, n_groups=1, n_heads=n_heads, q_max=4, topk=1024, ring_window=64,
+                   n_prefix=2, hot_slots=2048, var_k=True)
+    pair = build_pair(w)
+    assert pair.lib.info["attn_head_groups"] == 1 and pair.lib.info["attn_splits"] > 1
+    si = make_step_inputs(w, 0, 0, pair.hist_len)
+    res = pair.orc.verify_step(0, si.topk, si.causal_pos, si.queries, si.block_rows, n_threads=8)
+    out = run_lib_step(pair, 0, si)
+    compare_step(pair, 0, si, res, out)
+    pair.lib.close()
+
+
 def test_ring_block_only_reading():
     w = _tiny()
     pair = build_pair(w, block_only=True)
