@@ -70,7 +70,21 @@ def parse():
                     help="rounds run: share of each list drawn from the last 128 rows")
     ap.add_argument("--drift", type=float, default=0.1,
                     help="rounds run: share of each list redrawn every round (the rest repeats round 0's)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="a plain 1 GiB device copy, three times after a 1 GiB fill: the reference reading "
+                         "that scales the FETCH_SIZE / WRITE_SIZE counters to bytes")
     return ap.parse_args()
+
+
+def copy_probe():
+    """Known traffic for counter calibration: 3 x 1 GiB read, 4 x 1 GiB written."""
+    import torch
+    a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": a.numel() * 4, "copies": 3}))
 
 
 def main():
@@ -82,6 +96,9 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.copy_probe:
+        copy_probe()
+        return
     if args.load_step:
         load_step(args)
         return
