@@ -70,10 +70,90 @@ def parse():
                     help="rounds run: share of each list drawn from the last 128 rows")
     ap.add_argument("--drift", type=float, default=0.1,
                     help="rounds run: share of each list redrawn every round (the rest repeats round 0's)")
+    ap.add_argument("--resolver", action="store_true",
+                    help="resolver cost against the unique host-miss bytes of one call (mla32 shape): shared, "
+                         "partial and disjoint selections across the queries, cold and retained caches")
+    ap.add_argument("--resolver-reps", type=int, default=9, help="timings per resolver point")
     ap.add_argument("--copy-probe", action="store_true",
                     help="a plain 1 GiB device copy, three times after a 1 GiB fill: the reference reading "
                          "that scales the FETCH_SIZE / WRITE_SIZE counters to bytes")
     return ap.parse_args()
+
+
+def resolver_sweep(args):
+    """Resolution apart from the attention ("Adaptive DHiSparse" §4.3.3, Fig. 8a):
+    one call of 32 requests x 8 queries (k = 2048, B = 4096, MLA rows) with
+    selections shared by all queries, half shared, or disjoint, each against
+    an empty hot cache (cold) or the cache one identical call left (retained).
+    Resolver time = plan + host fetch + victim choice (per-kernel HIP events,
+    one fetch chunk); host-miss bytes = distinct fetched rows x row bytes.  A
+    least-squares line through the six points gives the rate."""
+    import numpy as np
+    import torch
+
+    from hierarchical_sparse_kv_verify_amd import KV_FLAG_TIMING
+    from tests.pair import build_pair, to_device
+    from workloads import WORKLOADS, make_step_inputs, shrink
+
+    torch.cuda.set_device(0)
+    base = shrink(WORKLOADS["mla32"], var_k=False, pad_frac=0.0, invalid_frac=0.0)
+    patterns = [("shared", dict(f_sh=1.0)), ("partial", dict(f_sh=0.5)), ("disjoint", dict(f_sh=0.0, disjoint=True))]
+    points = []
+    for name, kw in patterns:
+        w = shrink(base, **kw)
+        pair = build_pair(w, warm=False, with_oracle=False, lib_kw=dict(n_chunks=1))
+        lib = pair.lib
+        si = make_step_inputs(w, 0, 0, pair.hist_len)
+        d = to_device(si)
+        out = torch.zeros((w.n_req, w.q_max, w.n_heads, w.d_v), dtype=torch.int16, device="cuda")
+        lib.set_flags(KV_FLAG_TIMING)
+        lib.save_cache(0)                                   # empty hot caches
+        for cache in ("cold", "retained"):
+            if cache == "retained":
+                lib.restore_cache(0)
+                lib.verify_step(0, d["queries"], d["topk"], d["causal"], d["ring"], out)
+                torch.cuda.synchronize()
+                lib.save_cache(0)                           # the state one call left
+            lib.restore_cache(0)                            # warm-up call
+            lib.verify_step(0, d["queries"], d["topk"], d["causal"], d["ring"], out)
+            torch.cuda.synchronize()
+            ms, parts = [], []
+            for _ in range(args.resolver_reps):
+                lib.restore_cache(0)
+                lib.reset_stats()
+                torch.cuda.synchronize()
+                lib.verify_step(0, d["queries"], d["topk"], d["causal"], d["ring"], out)
+                torch.cuda.synchronize()
+                last = lib.stats(0)[0]                      # this call alone (stats reset before it)
+                part = (float(last["ms_plan"]), float(last["ms_gather"]), float(last["ms_victims"]))
+                parts.append(part)
+                ms.append(sum(part))
+            mb = int(last["union_miss"]) * w.row_bytes / 1e6
+            med = float(np.median(ms))
+            pm = [float(np.median([p[i] for p in parts])) for i in range(3)]
+            points.append(dict(pattern=name, cache=cache, union_rows=int(last["union_rows"]),
+                               missed_rows=int(last["union_miss"]), miss_mb=round(mb, 2),
+                               resolver_ms=dict(min=round(min(ms), 4), median=round(med, 4), max=round(max(ms), 4)),
+                               plan_ms=round(pm[0], 4), fetch_ms=round(pm[1], 4), victims_ms=round(pm[2], 4)))
+            log("bench: %-8s %-8s union %7d missed %7d  %8.2f MB  resolver %.3f ms (plan %.3f fetch %.3f "
+                "victims %.3f)" % (name, cache, points[-1]["union_rows"], points[-1]["missed_rows"], mb, med,
+                                   pm[0], pm[1], pm[2]))
+        lib.set_flags(0)
+        lib.close()
+        del pair, lib
+    x = np.array([p["miss_mb"] for p in points])
+    y = np.array([p["resolver_ms"]["median"] for p in points])
+    A = np.stack([x, np.ones_like(x)], axis=1)
+    (slope, icpt), *_ = np.linalg.lstsq(A, y, rcond=None)
+    pred = A @ np.array([slope, icpt])
+    r2 = 1.0 - float(((y - pred) ** 2).sum()) / max(1e-30, float(((y - y.mean()) ** 2).sum()))
+    cold = {p["pattern"]: p["resolver_ms"]["median"] for p in points if p["cache"] == "cold"}
+    print(json.dumps({
+        "metric": "resolver time against unique host-miss bytes per call", "workload": "mla32 (32 requests, Q=8, "
+        "k=2048, B=4096, MLA rows of 1152 B)", "points": points,
+        "fit": {"rate_GBs": round(1.0 / slope, 2) if slope > 0 else None, "intercept_ms": round(float(icpt), 4),
+                "r2": round(r2, 5)},
+        "disjoint_over_shared_cold": round(cold["disjoint"] / cold["shared"], 2)}))
 
 
 def copy_probe():
@@ -98,6 +178,9 @@ def main():
 
     if args.copy_probe:
         copy_probe()
+        return
+    if args.resolver:
+        resolver_sweep(args)
         return
     if args.load_step:
         load_step(args)

@@ -68,6 +68,8 @@ class Workload:
     recent_span: int = 0      # recent_span history rows (recently generated rows)
     compress: int = 1         # positions per stored row of the groups in compress_groups
     compress_groups: tuple = ()
+    disjoint: bool = False    # private parts drawn from disjoint uniform ranges of one
+                              # permutation (no overlap between a request's queries)
     note: str = ""
 
     @property
@@ -318,10 +320,15 @@ def make_step_inputs(w: Workload, group: int, step: int, hist_len: np.ndarray,
         perm = rest[rng.permutation(rest.size)]
         priv_n = min(k - core_n, rest.size)
         cdf = _zipf_cdf(rest.size, w.zipf_s) if rest.size else np.zeros(0)
+        if w.disjoint:
+            priv_n = min(priv_n, rest.size // Q)
         privs = []
         for j in range(Q):
-            ranks = _zipf_distinct(rng, cdf, priv_n)
-            priv = perm[ranks]
+            if w.disjoint:
+                priv = perm[j * priv_n:(j + 1) * priv_n]
+            else:
+                ranks = _zipf_distinct(rng, cdf, priv_n)
+                priv = perm[ranks]
             lst = np.concatenate([core, priv]).astype(np.int64)
             lst = lst[rng.permutation(lst.size)]
             row = np.full(k, -1, dtype=np.int64)
