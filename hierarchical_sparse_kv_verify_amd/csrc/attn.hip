@@ -43,6 +43,8 @@
 //    rows shared by a request's queries are re-read from that XCD's L2.
 #include "common.h"
 
+#include <type_traits>
+
 namespace kvh {
 namespace {
 
@@ -422,51 +424,76 @@ __global__ __launch_bounds__(C::NT, 1) void attn_kernel(AttnArgs a) {
   const uint16_t* p_rd = Pb + (size_t(hb) * 32 + (lane & 31)) * C::PSTR + hi_half * 8;
   const int sbit0 = dq * 8 + hi_half * 4;              // first tile row of this lane's quarter
 
-  for (int t = tb; t < te; ++t) {
-    const uint16_t* kb = kbuf(t);
+  // K fragments of tile tb (every later tile's are read right after the
+  // barrier that publishes it, one tile ahead of their products)
+  bf16x8 kfr[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks)
+    kfr[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kbuf(tb) + koff[ks]));
+
+  // One tile; B = (t - tb) mod NBUF is a compile-time constant (the loop below
+  // is unrolled NBUF times), so buffer and slot offsets fold into the LDS
+  // instructions.
+  auto tile = [&](int t, auto bconst) {
+    constexpr int B = decltype(bconst)::value;
+    const uint16_t* kb = Kb + B * C::BSTR;
+    // codes of tile t+2 (landed before the last barrier; DMA path)
+    if constexpr (C::DMA) raw = (Cs + ((B + 2) % 3) * (C::NW * 64))[w * 64 + lane];
 
     // partial scores over this wave's part of the key width
     f32x16 acc;
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + koff[ks]));
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[ks], acc, 0, 0, 0);
-    }
+    for (int ks = 0; ks < C::KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[ks], qreg[ks], acc, 0, 0, 0);
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4)
       sx_own[i4 * 64] = make_float4(acc[4 * i4], acc[4 * i4 + 1], acc[4 * i4 + 2], acc[4 * i4 + 3]);
+    if constexpr (C::DMA)
+      lds_barrier();
+    else
+      __syncthreads();
+
+    // LDS reads first (this wave's partial scores, the tile's V^T fragments),
+    // then the next tiles' loads while they land
+    float4 sxv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sxv[q] = sx_red[q * 256];
+    bf16x8 vfr[2][C::DVB];
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+      for (int d = 0; d < C::DVB; ++d) {
+        const uint16_t* vp = kb + v_off + ks2 * 16 * C::RSTR + d * 8;
+        const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp));
+        const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 4 * C::RSTR));
+        vfr[ks2][d] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
     uint32_t live_n2;
     if constexpr (C::DMA) {
-      lds_barrier();
       // DMA of tile t+2 into the buffer of tile t-1 (its last readers, the PV
       // products of t-1, finished before the barrier) and of the codes of
       // tile t+4 into the slot of t+1; issued unconditionally so that every
       // wave keeps NVM instructions per tile (tiles past the range read the
       // zero row and are never used)
-      const int code = t + 2 < te ? final_code(ctx, (t + 2) * TILE + crow, cslot(t + 2)[w * 64 + lane]) : -1;
-      live_n2 = dma_tile<C>(kbuf(t + 2), ctx, code, w, lane);
-      dma_codes<C>(cslot(t + 4), ctx, t + 4, w, lane);
+      const int code = t + 2 < te ? final_code(ctx, (t + 2) * TILE + crow, raw) : -1;
+      live_n2 = dma_tile<C>(Kb + ((B + 2) % 3) * C::BSTR, ctx, code, w, lane);
+      dma_codes<C>(Cs + ((B + 1) % 3) * (C::NW * 64), ctx, t + 4, w, lane);
     } else {
-      __syncthreads();
       // tile t+1 into the other buffer (its last reader, PV of tile t-1, is done);
       // issue tile t+2 and the codes of tile t+3 (unconditional: positions past
       // the range read the zero row and are never used)
-      gather_store<C>(g, kbuf(t + 1), w, lane);
+      gather_store<C>(g, Kb + ((B + 1) % C::NBUF) * C::BSTR, w, lane);
       live_n2 = gather_issue<C>(g, ctx, final_code(ctx, (t + 2) * TILE + crow, raw), w, lane);
       raw = raw_code(ctx, (t + 3) * TILE + crow);
     }
 
     // this wave's quarter of the rows: scores summed over the key parts in order
     float s[4];
-    {
-      const float4 v0 = sx_red[0], v1 = sx_red[256], v2 = sx_red[512], v3 = sx_red[768];
-      s[0] = ((v0.x + v1.x) + v2.x) + v3.x;
-      s[1] = ((v0.y + v1.y) + v2.y) + v3.y;
-      s[2] = ((v0.z + v1.z) + v2.z) + v3.z;
-      s[3] = ((v0.w + v1.w) + v2.w) + v3.w;
-    }
+    s[0] = ((sxv[0].x + sxv[1].x) + sxv[2].x) + sxv[3].x;
+    s[1] = ((sxv[0].y + sxv[1].y) + sxv[2].y) + sxv[3].y;
+    s[2] = ((sxv[0].z + sxv[1].z) + sxv[2].z) + sxv[3].z;
+    s[3] = ((sxv[0].w + sxv[1].w) + sxv[2].w) + sxv[3].w;
     const uint32_t lb = live_cur >> sbit0;
     bool over = false;
 #pragma unroll
@@ -496,6 +523,15 @@ __global__ __launch_bounds__(C::NT, 1) void attn_kernel(AttnArgs a) {
     else
       __syncthreads();
 
+    // K fragments of tile t+1 (published by this barrier) for its scores
+    // after this tile's PV products
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+      kfr[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Kb + ((B + 1) % C::NBUF) * C::BSTR + koff[ks]));
+    bf16x8 pbf[2];
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2)
+      pbf[ks2] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p_rd + ks2 * 16));
     const bool slow = C::NW == 8 ? *reinterpret_cast<const uint64_t*>(flags) != 0
                                  : *reinterpret_cast<const uint32_t*>(flags) != 0;
     if (slow) {
@@ -530,24 +566,25 @@ __global__ __launch_bounds__(C::NT, 1) void attn_kernel(AttnArgs a) {
              (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(p[3]))) << 16);
       *reinterpret_cast<uint2*>(p_own) = pk;
       __syncthreads();
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2)
+        pbf[ks2] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p_rd + ks2 * 16));
     }
     l_run += ps;
 
     // O^T += V^T P^T over the tile's 32 rows (two 16-row k-steps)
 #pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2) {
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p_rd + ks2 * 16));
+    for (int ks2 = 0; ks2 < 2; ++ks2)
 #pragma unroll
-      for (int d = 0; d < C::DVB; ++d) {
-        const uint16_t* vp = kb + v_off + ks2 * 16 * C::RSTR + d * 8;
-        const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp));
-        const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 4 * C::RSTR));
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-        O[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, O[d], 0, 0, 0);
-      }
-    }
+      for (int d = 0; d < C::DVB; ++d) O[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[ks2][d], pbf[ks2], O[d], 0, 0, 0);
     live_cur = live_n1;
     live_n1 = live_n2;
+  };
+  for (int t = tb; t < te; t += C::NBUF) {
+    tile(t, std::integral_constant<int, 0>{});
+    if (t + 1 < te) tile(t + 1, std::integral_constant<int, 1>{});
+    if constexpr (C::NBUF == 3)
+      if (t + 2 < te) tile(t + 2, std::integral_constant<int, 2>{});
   }
   if constexpr (C::DMA) __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0): no DMA outlives the loop
 
