@@ -632,20 +632,31 @@ __global__ __launch_bounds__(C::NT, 1) void attn_kernel(AttnArgs a) {
   }
 }
 
-// Merge of key splits: out = sum_s 2^(m_s-m) O_s / sum_s 2^(m_s-m) l_s.
-// One 128-thread block per (query, head); threads run over value dims.
+// Merge of key splits: out = sum_s 2^(m_s-m) O_s / sum_s 2^(m_s-m) l_s, the
+// sums in split order.  One 256-thread block per (query, head group, 8 heads):
+// 32 threads per head, each over float4 groups of value dims 128g + 4(t mod
+// 32), so every load instruction reads 512 contiguous bytes.  Block index ->
+// request as in the attention kernel, so the partials are read on the XCD
+// (and from the L2) where they were written.
 template <int D_V, int HB>
-__global__ __launch_bounds__(128) void combine_kernel(AttnArgs a) {
-  constexpr int HPW = 32 * HB;
-  const int per_q = a.head_groups * HPW;
-  const int qi = a.r0 * a.Q + blockIdx.x / per_q;
-  const int hx = blockIdx.x % per_q;
-  const int hg = hx / HPW, hl = hx % HPW;
+__global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
+  constexpr int HPW = 32 * HB, N8 = HPW / 8;
+  const int nreq = a.r1 - a.r0;
+  const int per_req = a.Q * a.head_groups * N8;
+  const int b = blockIdx.x;
+  const int rr = ((b >> 3) / per_req) * 8 + (b & 7);
+  if (rr >= nreq) return;
+  const int sub = (b >> 3) % per_req;
+  const int j = sub / (a.head_groups * N8);
+  const int hg = (sub / N8) % a.head_groups;
+  const int hl = (sub % N8) * 8 + int(threadIdx.x >> 5);
+  const int qi = (a.r0 + rr) * a.Q + j;
   const int head = hg * HPW + hl;
   if (head >= a.H) return;
+  const int d0 = 4 * int(threadIdx.x & 31);
   uint16_t* op = a.out + (size_t(qi) * a.H + head) * D_V;
   if (a.causal[qi] < 0) {
-    for (int d = threadIdx.x; d < D_V; d += blockDim.x) op[d] = 0;
+    for (int d = d0; d < D_V; d += 128) *reinterpret_cast<uint2*>(op + d) = make_uint2(0, 0);
     return;
   }
   const size_t blk0 = (size_t(qi - a.r0 * a.Q) * a.head_groups + hg) * a.splits;
@@ -662,10 +673,21 @@ __global__ __launch_bounds__(128) void combine_kernel(AttnArgs a) {
     }
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
-  for (int d = threadIdx.x; d < D_V; d += blockDim.x) {
-    float num = 0.f;
-    for (int s = 0; s < a.splits; ++s) num += a.part_o[((blk0 + s) * HPW + hl) * D_V + d] * wsum[s];
-    op[d] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(num * inv));
+  for (int d = d0; d < D_V; d += 128) {
+    float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = 0; s < a.splits; ++s) {
+      const float4 o = *reinterpret_cast<const float4*>(a.part_o + ((blk0 + s) * HPW + hl) * D_V + d);
+      num.x += o.x * wsum[s];
+      num.y += o.y * wsum[s];
+      num.z += o.z * wsum[s];
+      num.w += o.w * wsum[s];
+    }
+    uint2 pk;
+    pk.x = uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(num.x * inv))) |
+           (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(num.y * inv))) << 16);
+    pk.y = uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(num.z * inv))) |
+           (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(num.w * inv))) << 16);
+    *reinterpret_cast<uint2*>(op + d) = pk;
   }
 }
 
@@ -712,13 +734,13 @@ hipError_t launch_attn_combine(const AttnArgs& a, int d_v, hipStream_t s) {
   const int nreq = a.r1 - a.r0;
   if (nreq <= 0 || a.splits <= 1) return hipSuccess;
   const int hpw = attn_heads_per_wg(a.H);
-  const dim3 grid(unsigned(nreq * a.Q * a.head_groups * hpw));
+  const dim3 grid(unsigned(((nreq + 7) / 8) * 8 * a.Q * a.head_groups * (hpw / 8)));
   if (d_v == 512) {
-    if (hpw == 32) hipLaunchKernelGGL((combine_kernel<512, 1>), grid, dim3(128), 0, s, a);
-    else hipLaunchKernelGGL((combine_kernel<512, 2>), grid, dim3(128), 0, s, a);
+    if (hpw == 32) hipLaunchKernelGGL((combine_kernel<512, 1>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((combine_kernel<512, 2>), grid, dim3(256), 0, s, a);
   } else if (d_v == 128) {
-    if (hpw == 32) hipLaunchKernelGGL((combine_kernel<128, 1>), grid, dim3(128), 0, s, a);
-    else hipLaunchKernelGGL((combine_kernel<128, 2>), grid, dim3(128), 0, s, a);
+    if (hpw == 32) hipLaunchKernelGGL((combine_kernel<128, 1>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((combine_kernel<128, 2>), grid, dim3(256), 0, s, a);
   } else {
     return hipErrorInvalidValue;
   }
