@@ -627,10 +627,12 @@ static int create_impl(kv_hier* h) {
     if (h->plan_lds > 160 * 1024) return fail(h, KV_EUNSUPPORTED, "plan LDS %zu", h->plan_lds);
   }
   // request chunks for the fetch/attention pipeline
-  // Automatic layout for N >= 64: four quarters with the last one halved, so
-  // the attention left after the last fetch (nothing overlaps it) is short.
+  // Automatic layout: four quarters for N >= 64.  Each attention launch then
+  // has N/4 x Q x head-groups workgroups (a full wave of the GPU at N = 128)
+  // and needs no key splits; a smaller last chunk shortens the attention left
+  // after the last fetch but its split launch and merge cost more than that.
   if (c.n_chunks == 0 && N >= 64) {
-    for (int x : {0, 2, 4, 6, 7, 8}) h->chunk_lo.push_back(int(int64_t(N) * x / 8));
+    for (int x : {0, 1, 2, 3, 4}) h->chunk_lo.push_back(int(int64_t(N) * x / 4));
   } else {
     const int nch = c.n_chunks > 0 ? std::min(c.n_chunks, N) : (N >= 16 ? 2 : 1);
     for (int i = 0; i <= nch; ++i) h->chunk_lo.push_back(int(int64_t(N) * i / nch));
