@@ -627,12 +627,16 @@ static int create_impl(kv_hier* h) {
     if (h->plan_lds > 160 * 1024) return fail(h, KV_EUNSUPPORTED, "plan LDS %zu", h->plan_lds);
   }
   // request chunks for the fetch/attention pipeline
-  // Automatic layout: four quarters for N >= 64.  Each attention launch then
-  // has N/4 x Q x head-groups workgroups (a full wave of the GPU at N = 128)
-  // and needs no key splits; a smaller last chunk shortens the attention left
-  // after the last fetch but its split launch and merge cost more than that.
+  // Automatic layout for N >= 64: four quarters, the last one halved when each
+  // half still fills the GPU with attention workgroups (N/8 x Q x head groups
+  // >= 256).  The halving shortens the attention left after the last fetch
+  // (nothing overlaps it); below a full wave a chunk needs key splits and a
+  // merge, which cost more than the shorter tail saves.
   if (c.n_chunks == 0 && N >= 64) {
-    for (int x : {0, 1, 2, 3, 4}) h->chunk_lo.push_back(int(int64_t(N) * x / 4));
+    const int64_t hgroups = (c.n_heads + attn_heads_per_wg(c.n_heads) - 1) / attn_heads_per_wg(c.n_heads);
+    const bool halve = int64_t(N / 8) * c.q_max * hgroups >= 256;
+    const std::vector<int> eighths = halve ? std::vector<int>{0, 2, 4, 6, 7, 8} : std::vector<int>{0, 2, 4, 6, 8};
+    for (int x : eighths) h->chunk_lo.push_back(int(int64_t(N) * x / 8));
   } else {
     const int nch = c.n_chunks > 0 ? std::min(c.n_chunks, N) : (N >= 16 ? 2 : 1);
     for (int i = 0; i <= nch; ++i) h->chunk_lo.push_back(int(int64_t(N) * i / nch));
