@@ -361,6 +361,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_min_median_max": [round(1000 * min(times), 4), round(1000 * float(np.median(times)), 4),
+                                       round(1000 * max(times), 4)],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -751,6 +753,16 @@ def attn_traffic(algo_bytes_per_launch):
     return round(float(vals["bytes_per_algo_byte"]) * algo_bytes_per_launch, 1)
 
 
+def _cpu_model():
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, hists, hl, si, n_req_sample):
     """The oracle, as it stands, on the host cores over the first requests of
     layer group 0 (resolution + attention of all their queries)."""
@@ -778,6 +790,7 @@ def cpu_baseline(w, hists, hl, si, n_req_sample):
     value = nq / (dt * w.n_groups)
     log("bench: oracle %.2fs for %d query tokens of one group" % (dt, nq))
     return {"value": round(value, 3), "unit": "query-tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": _cpu_model(),
             "sample": "%d requests x %d queries of layer group 0 of %s (resolution + attention), "
                       "scaled by %d layer groups per step; %.2f s" % (len(reqs), w.q_max, w.name,
                                                                        w.n_groups, dt)}
