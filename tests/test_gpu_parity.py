@@ -218,6 +218,23 @@ def test_mla_one_head_block_split_keys(n_heads):
     pair.lib.close()
 
 
+@pytest.mark.parametrize("topk,window", [(8, 8), (40, 16), (3, 64)])
+def test_mla_short_lists(topk, window):
+    """Absorbed-MLA rows with lists and windows that fill one partial tile, or
+    two with a ragged second one: the tile pipeline's first tiles are also its
+    last (DMA of tiles past the range reads the zero row)."""
+    w = _mla_small(n_req=3, n_groups=1, q_max=2, topk=topk, ring_window=window, ring_page=8,
+                   hot_slots=64, var_k=True)
+    pair = build_pair(w)
+    for step in range(2):
+        si = make_step_inputs(w, 0, step, pair.hist_len)
+        res = pair.orc.verify_step(0, si.topk, si.causal_pos, si.queries, si.block_rows, n_threads=8)
+        out = run_lib_step(pair, 0, si)
+        compare_step(pair, 0, si, res, out)
+        compare_counts(pair, 0, res)
+    pair.lib.close()
+
+
 def test_ring_block_only_reading():
     w = _tiny()
     pair = build_pair(w, block_only=True)
