@@ -31,6 +31,11 @@
 //    of its own rows into wave-uniform addresses (readlane / lane permute),
 //    and masked positions read a zero row, so no load depends on a per-lane
 //    branch.
+//  - two barriers per tile: after the partial scores (then the next tiles'
+//    loads are issued and the softmax runs) and after the probabilities
+//    (which also publishes the next tile); the next tile's K fragments are
+//    read right after the second, one tile ahead of their products, and the
+//    tile's V^T fragments right after the first.
 //  - online softmax in fp32 with exp2 (scale folded with log2 e): the running
 //    max of a head is raised only when a score exceeds it by more than 2^8,
 //    detected per tile with one ballot; the rare raise takes a second pass
