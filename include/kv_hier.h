@@ -98,7 +98,12 @@ typedef struct {
   int32_t ring_window;      /* W                                                         */
   int32_t ring_page;        /* p                                                         */
   int32_t ring_block_only;  /* 1: ring branch limited to positions >= n_r (eq. 5 literal) */
-  int32_t n_chunks;         /* request chunks pipelined fetch -> attention (0 = auto)    */
+  int32_t n_chunks;         /* request chunks pipelined fetch -> attention.  0 = auto:
+                               for N >= 64 four quarters of the requests, the last one
+                               halved when each half still has >= 256 attention workgroups
+                               (N/8 x q_max x head groups); below 64 requests two chunks
+                               (one under 16).  A chunk under 256 attention workgroups
+                               splits each query's keys (merged by a combine pass)       */
   int64_t resident_cap;     /* rows of the resident pool per group (0 = no resident tier) */
   float softmax_scale;      /* <= 0 selects 1/sqrt(d_qk)                                 */
   int32_t flags;            /* KV_FLAG_*                                                 */
@@ -168,8 +173,8 @@ typedef struct {
   int32_t ring_rows;        /* R_d of eq. (9)                                            */
   int32_t n_chunks;
   int64_t bytes_hot, bytes_staging, bytes_ring, bytes_maps, bytes_resident, bytes_host;
-  int32_t attn_splits;      /* key splits per query chosen for this shape                */
-  int32_t attn_head_groups;
+  int32_t attn_splits;      /* the largest key split count of a chunk (1: none)          */
+  int32_t attn_head_groups; /* 64-head (or one 32-head) workgroups per query             */
 } kv_hier_info;
 
 /* Creates a handle: allocates hot caches, slot tables, maps, rings, staging
