@@ -235,6 +235,35 @@ def test_mla_short_lists(topk, window):
     pair.lib.close()
 
 
+@pytest.mark.parametrize("n_req,n_heads,q_max,chunks,splits", [
+    (128, 64, 8, [0, 32, 64, 96, 128], 1),            # quarters of one GPU wave each
+    (128, 128, 8, [0, 32, 64, 96, 112, 128], 1),      # halves of the last quarter still fill the GPU
+    (64, 64, 4, [0, 16, 32, 48, 64], 4),              # quarters under a wave: key splits (17 tiles)
+    (32, 64, 8, [0, 16, 32], 2),                      # fewer than 64 requests: two chunks
+])
+def test_automatic_chunk_layout(n_req, n_heads, q_max, chunks, splits):
+    """The automatic request chunks of the fetch/attention pipeline, read back
+    through kv_hier_info, and one step over them against the oracle."""
+    from hierarchical_sparse_kv_verify_amd import KVHier
+    from tests.pair import lib_config
+    w = _mla_small(n_req=n_req, n_groups=1, n_heads=n_heads, q_max=q_max, topk=512, ring_window=32,
+                   hot_slots=1024, hist_lo=900, hist_hi=1000, hist_cap=1100, prefix_len=256, var_k=True)
+    lib = KVHier(**lib_config(w))
+    info = lib.info
+    lib.close()
+    assert info["n_chunks"] == len(chunks) - 1
+    assert info["attn_splits"] == splits
+    assert info["attn_head_groups"] == (n_heads + 63) // 64
+    # the first and last request of every chunk against the oracle
+    reqs = sorted({x for a, b in zip(chunks, chunks[1:]) for x in (a, b - 1)})
+    pair = build_pair(w, oracle_requests=reqs)
+    si = make_step_inputs(w, 0, 0, pair.hist_len)
+    res = pair.orc.verify_step(0, si.topk, si.causal_pos, si.queries, si.block_rows, n_threads=8)
+    out = run_lib_step(pair, 0, si)
+    compare_step(pair, 0, si, res, out, requests=reqs)
+    pair.lib.close()
+
+
 def test_ring_block_only_reading():
     w = _tiny()
     pair = build_pair(w, block_only=True)
