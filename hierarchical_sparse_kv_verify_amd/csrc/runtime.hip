@@ -882,6 +882,7 @@ int kv_hier_info_get(kv_hier_t* h, kv_hier_info* out) {
   out->bytes_host = h->bytes_host;
   out->attn_splits = h->splits;
   out->attn_head_groups = h->head_groups;
+  out->plan_rows_per_pass = h->chunk_words * 32;
   return KV_OK;
 }
 

@@ -93,8 +93,12 @@ typedef struct {
   int32_t d_v;
   int32_t n_heads;          /* query heads sharing each row                              */
   int32_t q_max;            /* K_max verification queries per request (<= 32)           */
-  int32_t topk;             /* k selections per query                                    */
-  int32_t hot_slots;        /* B                                                         */
+  int32_t topk;             /* k >= 1 selections per query (a query with nothing selected
+                               passes a list of -1 pads).  The resolution keeps the
+                               q_max*topk location codes of a request in LDS beside the
+                               hot-slot bitmap: above about 40,000 entries create returns
+                               KV_EUNSUPPORTED                                           */
+  int32_t hot_slots;        /* B (<= 16384)                                              */
   int32_t ring_window;      /* W                                                         */
   int32_t ring_page;        /* p                                                         */
   int32_t ring_block_only;  /* 1: ring branch limited to positions >= n_r (eq. 5 literal) */
@@ -175,6 +179,10 @@ typedef struct {
   int64_t bytes_hot, bytes_staging, bytes_ring, bytes_maps, bytes_resident, bytes_host;
   int32_t attn_splits;      /* the largest key split count of a chunk (1: none)          */
   int32_t attn_head_groups; /* 64-head (or one 32-head) workgroups per query             */
+  int32_t plan_rows_per_pass; /* history rows the resolution's LDS row bitmap covers at once:
+                               a longer history is resolved in ceil(n_r / this) passes
+                               over row ranges (the q_max*topk location codes share the
+                               bitmap's LDS)                                             */
 } kv_hier_info;
 
 /* Creates a handle: allocates hot caches, slot tables, maps, rings, staging

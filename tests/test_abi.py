@@ -52,6 +52,8 @@ def _cfg(**kw):
     (dict(topk=0), -1),
     (dict(q_max=33), -5),
     (dict(q_max=32, topk=4096), -5),
+    (dict(q_max=32, topk=2047), -5),                        # 65,504 codes: over the plan's LDS
+    (dict(q_max=32, topk=1272), -5),                        # 40,704 codes: just over it at B = 128
     (dict(row_elems=300, d_qk=256, d_v=256), -5),
     (dict(d_qk=600), -1),
     (dict(n_prefix=0, prefix_len=10), -1),

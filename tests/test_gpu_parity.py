@@ -264,6 +264,31 @@ def test_automatic_chunk_layout(n_req, n_heads, q_max, chunks, splits):
     pair.lib.close()
 
 
+def test_maximum_queries_hot_slots_and_plan_passes():
+    """The largest shapes create accepts: Q = 32 verification queries, B = 16384
+    hot slots, and Q*k = 38,400 list entries, whose location codes leave the
+    resolution's LDS row bitmap about 38K rows, so a ~100K-row history is
+    resolved in three passes over row ranges (union ranks, probe and staging
+    order carried across passes); the victim choice sorts 16384 slots."""
+    w = _tiny(n_req=2, q_max=32, topk=1200, hot_slots=16384, hist_lo=99000, hist_hi=100000,
+              hist_cap=100100, var_k=False)
+    pair = build_pair(w)
+    info = pair.lib.info
+    n_r = int(pair.hist_len.min())
+    assert 2 * info["plan_rows_per_pass"] < n_r <= 3 * info["plan_rows_per_pass"], info
+    for step in range(2):
+        si = make_step_inputs(w, 0, step, pair.hist_len)
+        res = pair.orc.verify_step(0, si.topk, si.causal_pos, si.queries, si.block_rows, n_threads=8)
+        out = run_lib_step(pair, 0, si)
+        compare_step(pair, 0, si, res, out)
+        compare_counts(pair, 0, res)
+        # rows from every pass were resolved, and misses were staged and promoted
+        assert any(len(rr.union) and max(rr.union) >= 2 * info["plan_rows_per_pass"] for rr in res.req.values())
+        assert sum(len(rr.victims) for rr in res.req.values()) > 0
+    _exact_vs_topk(pair, 0, 1, si.topk[1])
+    pair.lib.close()
+
+
 def test_ring_block_only_reading():
     w = _tiny()
     pair = build_pair(w, block_only=True)
