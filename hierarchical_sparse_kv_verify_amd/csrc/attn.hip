@@ -697,14 +697,13 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
 }
 
 template <class C>
+hipError_t set_lds_limit() {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(attn_kernel<C>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, int(C::LDS));
+}
+
+template <class C>
 hipError_t launch_cfg(const AttnArgs& a, hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_kernel<C>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(C::LDS));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
   const int nreq = a.r1 - a.r0;
   if (nreq <= 0) return hipSuccess;
   const int per_req = a.Q * a.head_groups * a.splits;
@@ -714,6 +713,14 @@ hipError_t launch_cfg(const AttnArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t attn_init_attributes() {
+  hipError_t e = set_lds_limit<Cfg<576, 0, 512, 576, 1>>();
+  if (e == hipSuccess) e = set_lds_limit<Cfg<576, 0, 512, 576, 2>>();
+  if (e == hipSuccess) e = set_lds_limit<Cfg<128, 128, 128, 256, 1>>();
+  if (e == hipSuccess) e = set_lds_limit<Cfg<128, 128, 128, 256, 2>>();
+  return e;
+}
 
 bool attn_layout_supported(int row_elems, int d_qk, int v_off, int d_v) {
   return (row_elems == 576 && d_qk == 576 && v_off == 0 && d_v == 512) ||

@@ -54,6 +54,9 @@ struct PlanArgs {
 size_t plan_lds_bytes(int Q, int k, int B, int chunk_words, int sort_cap);
 // union, probe, staging positions, locations (everything the fetch needs)
 hipError_t launch_plan(const PlanArgs& a, size_t lds, hipStream_t s);
+// dynamic-LDS limits of the plan and attention kernels, on the current device
+hipError_t plan_init_attributes();
+hipError_t attn_init_attributes();
 // LRU victims, promotions and slot-table updates (after launch_plan)
 hipError_t launch_plan_victims(const PlanArgs& a, size_t lds, hipStream_t s);
 

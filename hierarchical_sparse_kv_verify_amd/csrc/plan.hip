@@ -397,26 +397,21 @@ size_t plan_lds_bytes(int Q, int k, int B, int chunk_words, int sort_cap) {
   return resolve > victims ? resolve : victims;
 }
 
+hipError_t plan_init_attributes() {
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(plan_resolve_kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(plan_victims_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  return e;
+}
+
 hipError_t launch_plan(const PlanArgs& a, size_t lds, hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(plan_resolve_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
   hipLaunchKernelGGL(plan_resolve_kernel, dim3(a.N), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_plan_victims(const PlanArgs& a, size_t lds, hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(plan_victims_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
   hipLaunchKernelGGL(plan_victims_kernel, dim3(a.N), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }

@@ -174,6 +174,23 @@ struct kv_hier {
   int64_t bytes_hot = 0, bytes_staging = 0, bytes_ring = 0, bytes_maps = 0, bytes_res = 0, bytes_host = 0;
 };
 
+// Entry points run on the handle's device (its memory, streams and events
+// belong to the device that was current at create); the caller's current
+// device is restored on return.
+struct DeviceGuard {
+  int prev = -1;
+  explicit DeviceGuard(const kv_hier* h) {
+    int cur = -1;
+    if (h && hipGetDevice(&cur) == hipSuccess && cur != h->device && hipSetDevice(h->device) == hipSuccess)
+      prev = cur;
+  }
+  ~DeviceGuard() {
+    if (prev >= 0) (void)hipSetDevice(prev);
+  }
+  DeviceGuard(const DeviceGuard&) = delete;
+  DeviceGuard& operator=(const DeviceGuard&) = delete;
+};
+
 namespace {
 
 int fail(kv_hier* h, int code, const char* fmt, ...) {
@@ -590,6 +607,7 @@ static thread_local std::string g_create_error = "null handle";
 const char* kv_hier_last_error(const kv_hier_t* h) { return h ? h->err.c_str() : g_create_error.c_str(); }
 
 void kv_hier_destroy(kv_hier_t* h) {
+  DeviceGuard dg(h);
   if (!h) return;
   (void)hipDeviceSynchronize();
   free_all(h);
@@ -626,6 +644,10 @@ static int create_impl(kv_hier* h) {
     h->plan_lds = plan_lds_bytes(c.q_max, c.topk, B, h->chunk_words, sc);
     if (h->plan_lds > 160 * 1024) return fail(h, KV_EUNSUPPORTED, "plan LDS %zu", h->plan_lds);
   }
+  // the plan and attention kernels take more than 64 KB of dynamic LDS (set
+  // per device: every handle sets it on its own)
+  HIPCHK(h, plan_init_attributes());
+  HIPCHK(h, attn_init_attributes());
   // request chunks for the fetch/attention pipeline
   // Automatic layout for N >= 64: four quarters, the last one halved when each
   // half still fills the GPU with attention workgroups (N/8 x Q x head groups
@@ -887,6 +909,7 @@ int kv_hier_info_get(kv_hier_t* h, kv_hier_info* out) {
 }
 
 int kv_hier_host_rows(kv_hier_t* h, int g, int kind, int index, void** rows, int64_t* n_rows) {
+  DeviceGuard dg(h);
   int rc = check_group(h, g);
   if (rc) return rc;
   if (!rows || !n_rows) return fail(h, KV_EINVAL, "null output");
@@ -906,6 +929,7 @@ int kv_hier_host_rows(kv_hier_t* h, int g, int kind, int index, void** rows, int
 }
 
 int kv_hier_set_hist_len(kv_hier_t* h, const int32_t* hist_len) {
+  DeviceGuard dg(h);
   if (!h || !hist_len) return KV_EINVAL;
   for (int r = 0; r < h->cfg.n_req; ++r)
     if (hist_len[r] < 0 || hist_len[r] > h->cfg.hist_cap)
@@ -923,12 +947,14 @@ int kv_hier_set_hist_len(kv_hier_t* h, const int32_t* hist_len) {
 }
 
 int kv_hier_hist_len(kv_hier_t* h, int32_t* hist_len) {
+  DeviceGuard dg(h);
   if (!h || !hist_len) return KV_EINVAL;
   std::copy(h->hist_len.begin(), h->hist_len.end(), hist_len);
   return KV_OK;
 }
 
 int kv_hier_set_hot(kv_hier_t* h, int g, int r, const int32_t* rows, const int32_t* last_used, int n) {
+  DeviceGuard dg(h);
   int rc = check_group(h, g);
   if (rc) return rc;
   if ((rc = check_req(h, r))) return rc;
@@ -978,6 +1004,7 @@ int kv_hier_set_hot(kv_hier_t* h, int g, int r, const int32_t* rows, const int32
 }
 
 int kv_hier_set_resident(kv_hier_t* h, int g, int r, const uint8_t* bitmap) {
+  DeviceGuard dg(h);
   int rc = check_group(h, g);
   if (rc) return rc;
   if ((rc = check_req(h, r))) return rc;
@@ -1008,6 +1035,7 @@ int kv_hier_set_resident(kv_hier_t* h, int g, int r, const uint8_t* bitmap) {
 }
 
 int kv_hier_clear_resident(kv_hier_t* h, int g) {
+  DeviceGuard dg(h);
   int rc = check_group(h, g);
   if (rc) return rc;
   if (h->opt.on) return fail(h, KV_ESTATE, "static resident sets are not used with dynamic residency");
@@ -1021,6 +1049,7 @@ int kv_hier_clear_resident(kv_hier_t* h, int g) {
 }
 
 int kv_hier_ring_load(kv_hier_t* h, int g, int r, int32_t first_pos, const void* rows, int n) {
+  DeviceGuard dg(h);
   int rc = check_group(h, g);
   if (rc) return rc;
   if ((rc = check_req(h, r))) return rc;
@@ -1044,6 +1073,7 @@ int kv_hier_ring_load(kv_hier_t* h, int g, int r, int32_t first_pos, const void*
 
 int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t* topk_idx,
                         const int32_t* causal_pos, const void* ring_rows, void* out, void* stream) {
+  DeviceGuard dg(h);
   int rc = check_group(h, g);
   if (rc) return rc;
   if (!queries || !causal_pos || !out) return fail(h, KV_EINVAL, "null device pointer");
@@ -1240,6 +1270,7 @@ int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t*
 
 int kv_hier_verify_reuse(kv_hier_t* h, int g, const void* queries, const int32_t* causal_pos, void* out,
                          void* stream) {
+  DeviceGuard dg(h);
   int rc = check_group(h, g);
   if (rc) return rc;
   if (!queries || !causal_pos || !out) return fail(h, KV_EINVAL, "null device pointer");
@@ -1309,6 +1340,7 @@ int kv_hier_verify_reuse(kv_hier_t* h, int g, const void* queries, const int32_t
 }
 
 int kv_hier_commit_src(kv_hier_t* h, const int32_t* accepted, const void* const* src_rows, void* stream) {
+  DeviceGuard dg(h);
   if (!h || !accepted) return KV_EINVAL;
   const kv_hier_config& c = h->cfg;
   const int N = c.n_req, G = c.n_groups;
@@ -1370,10 +1402,12 @@ int kv_hier_commit_src(kv_hier_t* h, const int32_t* accepted, const void* const*
 }
 
 int kv_hier_commit(kv_hier_t* h, const int32_t* accepted, void* stream) {
+  DeviceGuard dg(h);
   return kv_hier_commit_src(h, accepted, nullptr, stream);
 }
 
 int kv_hier_set_compression(kv_hier_t* h, int g, int32_t m) {
+  DeviceGuard dg(h);
   int rc = check_group(h, g);
   if (rc) return rc;
   Group& G = h->grp[g];
@@ -1392,6 +1426,7 @@ int kv_hier_set_compression(kv_hier_t* h, int g, int32_t m) {
 }
 
 int kv_hier_stats(kv_hier_t* h, int g, kv_hier_counters* cum, kv_hier_counters* last) {
+  DeviceGuard dg(h);
   int rc = check_group(h, g);
   if (rc) return rc;
   if ((rc = sync_all(h))) return rc;
@@ -1453,6 +1488,7 @@ int kv_hier_stats(kv_hier_t* h, int g, kv_hier_counters* cum, kv_hier_counters* 
 }
 
 int kv_hier_reset_stats(kv_hier_t* h) {
+  DeviceGuard dg(h);
   if (!h) return KV_EINVAL;
   int rc = sync_all(h);
   if (rc) return rc;
@@ -1466,6 +1502,7 @@ int kv_hier_reset_stats(kv_hier_t* h) {
 }
 
 int kv_hier_last_lists(kv_hier_t* h, int g, int r, kv_hier_lists* o) {
+  DeviceGuard dg(h);
   int rc = check_group(h, g);
   if (rc) return rc;
   if ((rc = check_req(h, r))) return rc;
@@ -1488,6 +1525,7 @@ int kv_hier_last_lists(kv_hier_t* h, int g, int r, kv_hier_lists* o) {
 }
 
 int kv_hier_slot_table(kv_hier_t* h, int g, int r, int32_t* rows, int32_t* last_used) {
+  DeviceGuard dg(h);
   int rc = check_group(h, g);
   if (rc) return rc;
   if ((rc = check_req(h, r))) return rc;
@@ -1500,6 +1538,7 @@ int kv_hier_slot_table(kv_hier_t* h, int g, int r, int32_t* rows, int32_t* last_
 }
 
 int kv_hier_read_rows(kv_hier_t* h, int g, const int32_t* locs, int n, void* rows) {
+  DeviceGuard dg(h);
   int rc = check_group(h, g);
   if (rc) return rc;
   if (n < 0 || (n > 0 && (!locs || !rows))) return fail(h, KV_EINVAL, "bad read_rows arguments");
@@ -1540,11 +1579,13 @@ int kv_hier_read_rows(kv_hier_t* h, int g, const int32_t* locs, int n, void* row
 }
 
 int kv_hier_sync(kv_hier_t* h) {
+  DeviceGuard dg(h);
   if (!h) return KV_EINVAL;
   return sync_all(h);
 }
 
 int kv_hier_set_flags(kv_hier_t* h, int32_t flags) {
+  DeviceGuard dg(h);
   if (!h) return KV_EINVAL;
   if (flags & ~(KV_FLAG_TIMING | KV_FLAG_POISON | KV_FLAG_TIMING_ATTN | KV_FLAG_SERIAL | KV_FLAG_SYNC_BACKUP))
     return fail(h, KV_EINVAL, "unknown flags %d", flags);
@@ -1555,6 +1596,7 @@ int kv_hier_set_flags(kv_hier_t* h, int32_t flags) {
 }
 
 int kv_hier_cache_snapshot(kv_hier_t* h, int g, int op) {
+  DeviceGuard dg(h);
   int rc = check_group(h, g);
   if (rc) return rc;
   if (op != 0 && op != 1) return fail(h, KV_EINVAL, "snapshot op %d", op);
@@ -1590,6 +1632,7 @@ int kv_hier_cache_snapshot(kv_hier_t* h, int g, int op) {
 
 int kv_hier_opt_admit(kv_hier_t* h, int r, int32_t required_pages, const int32_t* order, int n_order,
                       int32_t* n_reclaimed) {
+  DeviceGuard dg(h);
   if (!h) return KV_EINVAL;
   Opt& o = h->opt;
   if (!o.on) return fail(h, KV_ESTATE, "dynamic residency is off (opt_page_rows = 0)");
@@ -1633,6 +1676,7 @@ int kv_hier_opt_admit(kv_hier_t* h, int r, int32_t required_pages, const int32_t
 }
 
 int kv_hier_opt_complete(kv_hier_t* h, int r) {
+  DeviceGuard dg(h);
   if (!h) return KV_EINVAL;
   Opt& o = h->opt;
   if (!o.on) return fail(h, KV_ESTATE, "dynamic residency is off (opt_page_rows = 0)");
@@ -1649,6 +1693,7 @@ int kv_hier_opt_complete(kv_hier_t* h, int r) {
 }
 
 int kv_hier_opt_populate(kv_hier_t* h, int32_t max_pages, int32_t* n_assigned) {
+  DeviceGuard dg(h);
   if (!h) return KV_EINVAL;
   Opt& o = h->opt;
   if (!o.on) return fail(h, KV_ESTATE, "dynamic residency is off (opt_page_rows = 0)");
@@ -1709,6 +1754,7 @@ int kv_hier_opt_populate(kv_hier_t* h, int32_t max_pages, int32_t* n_assigned) {
 }
 
 int kv_hier_opt_publish(kv_hier_t* h, int wait) {
+  DeviceGuard dg(h);
   if (!h) return KV_EINVAL;
   if (!h->opt.on) return fail(h, KV_ESTATE, "dynamic residency is off (opt_page_rows = 0)");
   if (wait != 0 && wait != 1) return fail(h, KV_EINVAL, "wait must be 0 or 1");
@@ -1717,6 +1763,7 @@ int kv_hier_opt_publish(kv_hier_t* h, int wait) {
 
 int kv_hier_opt_query(kv_hier_t* h, int r, int32_t n_pages, int32_t* held, uint8_t* ready,
                       kv_hier_opt_info* info) {
+  DeviceGuard dg(h);
   if (!h) return KV_EINVAL;
   const Opt& o = h->opt;
   if (!o.on) return fail(h, KV_ESTATE, "dynamic residency is off (opt_page_rows = 0)");

@@ -187,7 +187,10 @@ typedef struct {
 
 /* Creates a handle: allocates hot caches, slot tables, maps, rings, staging
  * arenas, plan buffers, a side stream and events on the current HIP device,
- * and pinned host history for every group.  Returns KV_EINVAL for
+ * and pinned host history for every group.  Every later call on the handle
+ * runs on that device whatever device is current when it is made (the
+ * caller's current device is restored before it returns); streams passed to
+ * it must belong to that device.  Returns KV_EINVAL for
  * inconsistent sizes, KV_EUNSUPPORTED for a row layout without kernels,
  * KV_ENOMEM when an allocation fails. */
 int kv_hier_create(const kv_hier_config *cfg, kv_hier_t **out);
