@@ -34,6 +34,7 @@
 #include <deque>
 #include <set>
 #include <string>
+#include <new>
 #include <vector>
 
 #include "common.h"
@@ -876,7 +877,11 @@ static int create_impl(kv_hier* h) {
 int kv_hier_create(const kv_hier_config* cfg, kv_hier_t** out) {
   if (!cfg || !out) return KV_EINVAL;
   *out = nullptr;
-  kv_hier* h = new kv_hier();
+  kv_hier* h = new (std::nothrow) kv_hier();
+  if (!h) {
+    g_create_error = "kv_hier_create: out of host memory";
+    return KV_ENOMEM;
+  }
   h->cfg = *cfg;
   int rc = validate(h, *cfg);
   if (!rc) rc = create_impl(h);
