@@ -49,7 +49,9 @@ def parse():
                     help="steps of the separate pass that times every kernel")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=128,
-                    help="requests of layer group 0 the oracle resolves and attends in the CPU baseline")
+                    help="requests per layer group the oracle resolves and attends in the CPU baseline")
+    ap.add_argument("--cpu-groups", type=int, default=2,
+                    help="layer groups the CPU baseline times (scaled to all groups of a step)")
     ap.add_argument("--load-step", action="store_true",
                     help="residency under a load step (low -> full -> low load), optional residency on and off")
     ap.add_argument("--load-lo", type=int, default=16, help="active requests at low load")
@@ -351,7 +353,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, hists, hl, sis[0], args.cpu_requests)
+        cpu = cpu_baseline(w, hists, hl, sis, args.cpu_requests, args.cpu_groups)
 
     line = {
         "metric": "verified query-tokens/s per GPU and selected-rows/s; % HBM and host-link peak",
@@ -763,37 +765,41 @@ def _cpu_model():
     return None
 
 
-def cpu_baseline(w, hists, hl, si, n_req_sample):
+def cpu_baseline(w, hists, hl, sis, n_req_sample, n_groups_sample):
     """The oracle, as it stands, on the host cores over the first requests of
-    layer group 0 (resolution + attention of all their queries)."""
-    import numpy as np
-
+    the first layer groups (resolution + attention of all their queries)."""
     import oracle
     from tests.pair import oracle_config, prefill_rows
     from workloads import make_hot_warm_set
 
     cores = min(len(os.sched_getaffinity(0)), 16)
     reqs = list(range(min(n_req_sample, w.n_req)))
+    groups = list(range(max(1, min(n_groups_sample, w.n_groups))))
     # no commit happens here, so the oracle may read the generator's rows in place
     orc = oracle.HierOracle(oracle_config(w), hists, hl, requests=reqs)
-    for r, hs in enumerate(make_hot_warm_set(w, 0, hl, si)):
-        orc.set_hot(0, r, hs[0], hs[1])
-    for r in reqs:
-        first, rows = prefill_rows(hists[0], w, r, int(hl[r]))
-        orc.ring_load(0, r, first, rows)
-    log("bench: oracle on %d requests x %d queries, %d threads" % (len(reqs), w.q_max, cores))
-    t0 = time.perf_counter()
-    res = orc.verify_step(0, si.topk, si.causal_pos, si.queries, si.block_rows, n_threads=cores)
-    dt = time.perf_counter() - t0
+    for g in groups:
+        for r, hs in enumerate(make_hot_warm_set(w, g, hl, sis[g])):
+            orc.set_hot(g, r, hs[0], hs[1])
+        for r in reqs:
+            first, rows = prefill_rows(hists[g], w, r, int(hl[r]))
+            orc.ring_load(g, r, first, rows)
+    log("bench: oracle on %d requests x %d queries x %d layer groups, %d threads" %
+        (len(reqs), w.q_max, len(groups), cores))
+    dt = 0.0
+    for g in groups:
+        si = sis[g]
+        t0 = time.perf_counter()
+        res = orc.verify_step(g, si.topk, si.causal_pos, si.queries, si.block_rows, n_threads=cores)
+        dt += time.perf_counter() - t0
     nq = len(res.out)
     # one query token of a step passes through every layer group
-    value = nq / (dt * w.n_groups)
-    log("bench: oracle %.2fs for %d query tokens of one group" % (dt, nq))
+    value = nq / (dt * w.n_groups / len(groups))
+    log("bench: oracle %.2fs for %d query tokens of %d layer groups" % (dt, nq, len(groups)))
     return {"value": round(value, 3), "unit": "query-tokens/s", "cores": cores, "kind": "oracle",
             "cpu_model": _cpu_model(),
-            "sample": "%d requests x %d queries of layer group 0 of %s (resolution + attention), "
-                      "scaled by %d layer groups per step; %.2f s" % (len(reqs), w.q_max, w.name,
-                                                                       w.n_groups, dt)}
+            "sample": "%d requests x %d queries of layer groups 0..%d of %s (resolution + attention), "
+                      "scaled to %d layer groups per step; %.2f s" % (len(reqs), w.q_max, len(groups) - 1,
+                                                                      w.name, w.n_groups, dt)}
 
 
 if __name__ == "__main__":
