@@ -392,6 +392,33 @@ def test_full_size_mla128_sampled():
     pair.lib.close()
 
 
+def test_full_request_shape_mla512_sampled():
+    """The 512-request, 500K-row shape at its full per-request size (~500K-row
+    histories, 128 heads in two 64-head workgroups per query, Q = 4, k = 2048,
+    B = 2048, W = 64, the shared core as the only warm rows, so ~38% of
+    distinct rows miss and most misses overflow the 2048 slots), with 128
+    requests over two host prefixes: four chunks of 32 requests, each one wave of
+    256 attention workgroups without key splits.  Sampled requests of both
+    prefixes bit-exact, sampled queries within tolerance."""
+    w = shrink(WORKLOADS["mla512"], n_req=128, n_prefix=2)
+    reqs = [0, 1, 64, 127]
+    pair = build_pair(w, oracle_requests=reqs)
+    info = pair.lib.info
+    assert info["n_chunks"] == 4 and info["attn_splits"] == 1 and info["attn_head_groups"] == 2, info
+    si = make_step_inputs(w, 0, 0, pair.hist_len)
+    attend = {(r, j) for r in reqs for j in (0, 3)}
+    res = pair.orc.verify_step(0, si.topk, si.causal_pos, si.queries, si.block_rows, attend=attend, n_threads=16)
+    out = run_lib_step(pair, 0, si)
+    compare_step(pair, 0, si, res, out, requests=reqs)
+    _, last = pair.lib.stats(0)
+    assert last["active_queries"] == w.n_req * w.q_max
+    assert last["union_miss"] == last["promoted"] + last["overflow"] and last["overflow"] > last["promoted"]
+    assert 0.3 < last["union_miss"] / last["union_rows"] < 0.45
+    for r in reqs:
+        _exact_vs_topk(pair, 0, r, si.topk[r])
+    pair.lib.close()
+
+
 @pytest.mark.parametrize("window,page", [(8, 4), (2, 1)])
 def test_tail_rows_and_async_backup_over_rounds(window, page):
     """Selections favour recently generated rows: rows still in the ring
