@@ -173,9 +173,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the verification step shards by request with no exchange; see DESIGN.md)",
-              file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (the verification "
+              "step would shard by request, with no exchange between GPUs)", file=sys.stderr)
         sys.exit(2)
 
     if args.copy_probe:
