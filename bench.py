@@ -208,7 +208,7 @@ def main():
     t_setup = time.perf_counter()
     log("bench: generating %s (%d requests x %d groups)" % (w.name, w.n_req, w.n_groups))
     hl = make_hist_len(w)
-    hists = [make_history(w, g, hl) for g in range(w.n_groups)]
+    hists = [make_history(w, g, hl, progress=log if w.n_prefix > 4 else None) for g in range(w.n_groups)]
     log("bench: host rows ready (%.1fs); creating the library state" % (time.perf_counter() - t_setup))
     pair = build_pair(w, rho=args.rho, with_oracle=False, histories=hists,
                       lib_kw=dict(n_chunks=args.n_chunks, fetch_cus=args.fetch_cus, fetch_wgs=args.fetch_wgs))

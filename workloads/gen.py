@@ -214,7 +214,10 @@ def make_hist_len(w: Workload) -> np.ndarray:
     return rng.integers(w.hist_lo, w.hist_hi + 1, size=w.n_req).astype(np.int32)
 
 
-def make_history(w: Workload, group: int, hist_len: Optional[np.ndarray] = None) -> History:
+def make_history(w: Workload, group: int, hist_len: Optional[np.ndarray] = None,
+                 progress=None) -> History:
+    """Host rows of one layer group; ``progress`` (optional callable) receives a
+    line after each shared prefix (large prefixes take seconds each)."""
     if hist_len is None:
         hist_len = make_hist_len(w)
     assert w.n_prefix == 0 or w.prefix_len <= int(hist_len.min())
@@ -225,6 +228,8 @@ def make_history(w: Workload, group: int, hist_len: Optional[np.ndarray] = None)
     prefix = np.empty((max(npfx, 1), plen, w.row_elems), dtype=np.uint16)
     for p in range(npfx):
         prefix[p] = _normal_bf16(rngs[p], (plen, w.row_elems))
+        if progress is not None:
+            progress("history of group %d: prefix %d of %d ready" % (group, p + 1, npfx))
     tails = np.zeros((w.n_req, w.hist_cap - plen, w.row_elems), dtype=np.uint16)
     for r in range(w.n_req):
         n_own = int(hist_len[r]) - plen
