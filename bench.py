@@ -344,7 +344,11 @@ def main():
     # dominant kernel bound by the GPU's own memory is the sparse attention.
     roofline = dict(rooflines["sparse_attn"])
     roofline["kernel"] = "sparse_attn"
-    roofline["traffic"] = attn_traffic(attn_bytes / n_attn_live)
+    # the counters were taken on the default mla128 step (four 32-request chunks,
+    # cold-to-restored caches, no residency): other launches get no figure
+    same_launch = (args.workload == "mla128" and args.rho == 0 and not args.retained and args.n_chunks == 0
+                   and args.fetch_cus == 0 and args.fetch_wgs == 0)
+    roofline["traffic"] = attn_traffic(attn_bytes / n_attn_live) if same_launch else None
     roofline["timing"] = "HIP events around every attention launch during the timed steps"
     rooflines["sparse_attn"]["traffic"] = roofline["traffic"]
     roofline_host = dict(rooflines["miss_gather"])
@@ -732,9 +736,10 @@ def measure_h2d(torch, mib=512, reps=3):
 
 
 def attn_traffic(algo_bytes_per_launch):
-    """HBM bytes per attention launch from the committed rocprofv3 counter
-    summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's reading), or
-    None when the kernel source changed since the counters were taken."""
+    """HBM bytes per attention launch of the default mla128 step from the
+    committed rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, scaled by a
+    plain copy's reading), or None when the kernel source changed since the
+    counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "sparse_attn_mla128_traffic.md")
     src = os.path.join(ROOT, "hierarchical_sparse_kv_verify_amd", "csrc", "attn.hip")
