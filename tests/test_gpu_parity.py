@@ -289,6 +289,42 @@ def test_maximum_queries_hot_slots_and_plan_passes():
     pair.lib.close()
 
 
+def test_two_handles_on_two_streams():
+    """Two handles in one process (the 256-element layout and the absorbed-MLA
+    layout), each driven on its own non-default caller stream, steps and
+    commits interleaved: each matches its own oracle, so no launch setting or
+    device state leaks between handles, and the library orders its work after
+    whatever the caller enqueued on the stream it is given."""
+    import torch
+    from tests.pair import to_device
+    pairs = [build_pair(_tiny(n_req=2, var_k=True)), build_pair(_mla_small(n_req=3, n_groups=1))]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    n = [p.hist_len.copy() for p in pairs]
+    for step in range(3):
+        pending = []
+        for p, s, nn in zip(pairs, streams, n):
+            w = p.w
+            si = make_step_inputs(w, 0, step + 1, nn)
+            with torch.cuda.stream(s):
+                d = to_device(si)
+                out = torch.zeros((w.n_req, w.q_max, w.n_heads, w.d_v), dtype=torch.int16, device="cuda")
+                p.lib.verify_step(0, d["queries"], d["topk"], d["causal"], d["ring"], out, stream=s)
+            pending.append((p, si, out, d))
+        torch.cuda.synchronize()
+        for k, (p, si, out, d) in enumerate(pending):
+            res = p.orc.verify_step(0, si.topk, si.causal_pos, si.queries, si.block_rows, n_threads=8)
+            compare_step(p, 0, si, res, out.cpu().numpy().view(np.uint16))
+            compare_counts(p, 0, res)
+            acc = make_accepted(p.w, step, si.k_active)
+            p.orc.commit(acc)
+            p.lib.commit(acc, stream=streams[k])
+            n[k] = n[k] + 1 + acc
+        torch.cuda.synchronize()
+    for p, nn in zip(pairs, n):
+        assert p.lib.hist_len().tolist() == nn.tolist()
+        p.lib.close()
+
+
 def test_ring_block_only_reading():
     w = _tiny()
     pair = build_pair(w, block_only=True)
