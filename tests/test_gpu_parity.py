@@ -325,6 +325,49 @@ def test_two_handles_on_two_streams():
         p.lib.close()
 
 
+def test_invalid_calls_are_rejected_and_change_nothing():
+    """Host-side argument checks of the entry points (a null device pointer, a
+    group or request outside the handle, a bad hot set, a ring load that does
+    not end at the frontier, an acceptance outside [-1, q_max)): each returns
+    its error code before any device work, and the next valid step still
+    matches the oracle exactly."""
+    import torch
+    from hierarchical_sparse_kv_verify_amd import KVHierError
+    from tests.pair import to_device
+    w = _tiny(n_req=2)
+    pair = build_pair(w)
+    lib = pair.lib
+    si = make_step_inputs(w, 0, 0, pair.hist_len)
+    d = to_device(si)
+    out = torch.zeros((w.n_req, w.q_max, w.n_heads, w.d_v), dtype=torch.int16, device="cuda")
+    B, L = w.hot_slots, w.hist_cap
+    bad = [
+        (lambda: lib.verify_step(0, 0, d["topk"], d["causal"], d["ring"], out), -1),       # null queries
+        (lambda: lib.verify_step(0, d["queries"], 0, d["causal"], d["ring"], out), -1),    # null list
+        (lambda: lib.verify_step(1, d["queries"], d["topk"], d["causal"], d["ring"], out), -4),   # no group 1
+        (lambda: lib.set_hot(0, w.n_req, [1], [0]), -1),                                    # no such request
+        (lambda: lib.set_hot(0, 0, list(range(B + 1)), [0] * (B + 1)), -1),                 # more rows than slots
+        (lambda: lib.set_hot(0, 0, [3, 3], [0, 0]), -1),                                    # repeated row
+        (lambda: lib.set_hot(0, 0, [L], [0]), -1),                                          # row outside the history
+        (lambda: lib.set_hot(0, 0, [3], [-1]), -1),                                         # negative stamp
+        (lambda: lib.ring_load(0, 0, int(pair.hist_len[0]) - 2, np.zeros((1, w.row_elems), np.uint16)), -1),
+        (lambda: lib.commit(np.full(w.n_req, w.q_max, np.int32)), -1),                      # A_r >= q_max
+        (lambda: lib.last_lists(0, w.n_req), -1),
+    ]
+    for i, (call, code) in enumerate(bad):
+        with pytest.raises(KVHierError) as ei:
+            call()
+        assert ei.value.code == code, (i, ei.value.code, str(ei.value))
+    torch.cuda.synchronize()
+    res = pair.orc.verify_step(0, si.topk, si.causal_pos, si.queries, si.block_rows)
+    lib.verify_step(0, d["queries"], d["topk"], d["causal"], d["ring"], out)
+    torch.cuda.synchronize()
+    compare_step(pair, 0, si, res, out.cpu().numpy().view(np.uint16))
+    compare_counts(pair, 0, res)
+    assert lib.hist_len().tolist() == pair.hist_len.tolist()
+    lib.close()
+
+
 def test_ring_block_only_reading():
     w = _tiny()
     pair = build_pair(w, block_only=True)
