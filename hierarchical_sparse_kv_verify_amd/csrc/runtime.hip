@@ -299,7 +299,7 @@ int sync_all(kv_hier* h) {
 
 int check_group(kv_hier* h, int g) {
   if (!h) return KV_EINVAL;
-  if (g < 0 || g >= h->cfg.n_groups) return fail(h, KV_ESTATE, "group %d outside [0, %d)", g, h->cfg.n_groups);
+  if (g < 0 || g >= h->cfg.n_groups) return fail(h, KV_EINVAL, "group %d outside [0, %d)", g, h->cfg.n_groups);
   return KV_OK;
 }
 

@@ -344,7 +344,7 @@ def test_invalid_calls_are_rejected_and_change_nothing():
     bad = [
         (lambda: lib.verify_step(0, 0, d["topk"], d["causal"], d["ring"], out), -1),       # null queries
         (lambda: lib.verify_step(0, d["queries"], 0, d["causal"], d["ring"], out), -1),    # null list
-        (lambda: lib.verify_step(1, d["queries"], d["topk"], d["causal"], d["ring"], out), -4),   # no group 1
+        (lambda: lib.verify_step(1, d["queries"], d["topk"], d["causal"], d["ring"], out), -1),   # no group 1
         (lambda: lib.set_hot(0, w.n_req, [1], [0]), -1),                                    # no such request
         (lambda: lib.set_hot(0, 0, list(range(B + 1)), [0] * (B + 1)), -1),                 # more rows than slots
         (lambda: lib.set_hot(0, 0, [3, 3], [0, 0]), -1),                                    # repeated row
