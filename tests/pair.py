@@ -1,8 +1,9 @@
 """Builds the library handle and the oracle from the same seeded workload.
 
 Both sides receive identical inputs from ``workloads``; they share nothing
-else.  Used by the GPU parity tests, the smoke check and the benchmark's
-CPU-baseline leg.
+else.  Used by the GPU parity tests and the smoke check.  The benchmark builds
+its handle here with ``with_oracle=False``, which never imports the oracle;
+only its CPU-baseline leg runs the oracle.
 """
 from __future__ import annotations
 
@@ -12,7 +13,6 @@ from typing import List, Optional
 
 import numpy as np
 
-import oracle
 from workloads import (History, Workload, f32_from_bf16_bits, make_history, make_hot_warm_set,
                        make_resident_bitmaps, make_step_inputs)
 from workloads.gen import make_hist_len
@@ -32,6 +32,7 @@ def lib_config(w: Workload, **kw) -> dict:
 
 
 def oracle_config(w: Workload, block_only: bool = False) -> "oracle.OracleConfig":
+    import oracle
     return oracle.OracleConfig(
         n_req=w.n_req, n_groups=w.n_groups, hist_cap=w.hist_cap, n_prefix=w.n_prefix,
         prefix_len=w.prefix_len, row_elems=w.row_elems, d_qk=w.d_qk, v_off=w.v_off, d_v=w.d_v,
@@ -77,6 +78,7 @@ def build_pair(w: Workload, *, warm: bool = True, rho: float = 0.0, with_oracle:
     lib.set_hist_len(hl)
     orc = None
     if with_oracle:
+        import oracle   # only here: the benchmark's timed path builds its handle without it
         ohists = [History(prefix=h.prefix, tails=h.tails.copy(), hist_len=h.hist_len.copy()) for h in hists]
         orc = oracle.HierOracle(oracle_config(w, block_only), ohists, hl, requests=oracle_requests)
     oreq = set(orc.requests) if orc else set()

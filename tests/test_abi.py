@@ -86,3 +86,15 @@ def test_null_handle_calls_are_rejected(lib):
     assert lib.kv_hier_opt_populate(None, 1, None) == -1
     assert lib.kv_hier_opt_query(None, -1, 0, None, None, None) == -1
     lib.kv_hier_destroy(None)
+
+
+def test_benchmark_timed_path_does_not_load_the_oracle():
+    """bench.py's GPU path builds its handle through tests/pair.py without an
+    oracle: importing what it imports must not load any module of oracle/."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r); import bench, tests.pair; "
+            "print(sorted(m for m in sys.modules if m == 'oracle' or m.startswith('oracle.')))" % ROOT)
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert res.returncode == 0, res.stderr
+    assert res.stdout.strip().splitlines()[-1] == "[]", res.stdout
