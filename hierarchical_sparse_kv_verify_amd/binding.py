@@ -15,11 +15,14 @@ from typing import Optional
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkvhier.so")
+# KVHIER_LIBRARY names another build of the same sources (the host-sanitizer
+# build that the CPU sanitizer run loads); by default the in-tree library
+LIB_PATH = os.environ.get("KVHIER_LIBRARY") or os.path.join(_HERE, "libkvhier.so")
 
 KV_OK, KV_EINVAL, KV_ENOMEM, KV_EHIP, KV_ESTATE, KV_EUNSUPPORTED, KV_EWAIT = 0, -1, -2, -3, -4, -5, -6
 KV_TIER_HOT, KV_TIER_STAGED, KV_TIER_RESIDENT, KV_TIER_RING = 0, 1, 2, 3
 KV_FLAG_TIMING, KV_FLAG_POISON, KV_FLAG_TIMING_ATTN, KV_FLAG_SERIAL, KV_FLAG_SYNC_BACKUP = 1, 2, 4, 8, 16
+KV_FLAG_TEST_FAIL_ATTN = 32
 TIER_SHIFT = 29
 
 _ERRNAMES = {KV_EINVAL: "KV_EINVAL", KV_ENOMEM: "KV_ENOMEM", KV_EHIP: "KV_EHIP",

@@ -111,6 +111,9 @@ __global__ __launch_bounds__(kThreads) void plan_resolve_kernel(PlanArgs a) {
 
   for (int w = tid; w < pwords; w += kThreads) protect[w] = 0;
   if (tid < 32) cnt[tid] = 0;
+  // the zeroing is complete in every wave before any wave adds to the
+  // counters or marks a slot (also when the row loop below runs no chunk)
+  __syncthreads();
 
   int c_sel = 0, c_pad = 0, c_bad = 0, c_sres = 0, c_shot = 0, c_smiss = 0, c_stail = 0;
   int c_ures = 0, c_uhot = 0, c_umiss = 0, c_utail = 0;

@@ -44,6 +44,8 @@ using namespace kvh;
 
 namespace {
 
+constexpr int kCommitBufs = 4;
+
 enum TimedKind { K_RING = 0, K_PLAN, K_GATHER, K_ATTN, K_COMBINE, K_PROMOTE, K_VICTIMS, K_NUM };
 
 struct Group {
@@ -64,6 +66,8 @@ struct Group {
   uint32_t* protect = nullptr;      // [N][ceil(B/32)] slots protected by this step's hits
   hipEvent_t ev_done = nullptr;     // copy-backs of the group's last step finished
   bool done_recorded = false;
+  hipEvent_t ev_sel = nullptr;      // the group's last step wrote its ring rows and ran its attention
+  bool sel_recorded = false;
   bool sel_valid = false;           // this step's selection may be reused (until commit)
   int m = 1;                        // positions per stored row (compressed source when > 1)
   int64_t* req_counts = nullptr;
@@ -157,11 +161,23 @@ struct kv_hier {
   std::vector<int> arena_step;      // that group's step counter when it was fetched
   std::vector<int32_t> hist_len;
   int32_t* d_commit = nullptr;
-  int32_t* h_commit = nullptr;
   const uint4** d_src = nullptr;    // per group: the caller's completed stored rows of a commit
-  const uint4** h_src = nullptr;    // pinned staging of those pointers
-  hipEvent_t ev_commit = nullptr;
-  bool commit_pending = false;
+  // pinned staging of a commit's frontiers, acceptances and row pointers: a
+  // ring of kCommitBufs buffers, each reused once the copy that read it is done
+  // (the host waits only when that many commits are still ahead of the GPU)
+  int32_t* h_commit[kCommitBufs] = {};
+  const uint4** h_src[kCommitBufs] = {};
+  hipEvent_t ev_commit[kCommitBufs] = {};
+  bool commit_pending[kCommitBufs] = {};
+  // split-key partials (part_o / part_ml) are one buffer for every launch of
+  // the handle: each launch that uses them waits for the previous one
+  hipEvent_t ev_part = nullptr;
+  bool part_recorded = false;
+  // a call failed after it had started to change device state: every later
+  // call that changes state is refused (KV_ESTATE)
+  bool began = false;
+  bool broken = false;
+  std::string broken_msg;
   // host backup of committed rows (eq. 7) on its own stream, after verification
   hipStream_t backup = nullptr;     // the copy-back stream, or null: backups run on the caller's stream
   hipEvent_t ev_verified = nullptr; // the step's ring rows are written (caller's stream)
@@ -308,6 +324,27 @@ int check_req(kv_hier* h, int r) {
   return KV_OK;
 }
 
+// A call that changes state marks the point where its checks end and its
+// device work (or bookkeeping that must match the device) begins; an error
+// after that point leaves the handle inconsistent, so the handle is latched
+// and every later state-changing call returns KV_ESTATE.
+void begin_work(kv_hier* h) { h->began = true; }
+
+int refuse_if_broken(kv_hier* h) {
+  if (h && h->broken) return fail(h, KV_ESTATE, "handle unusable after a failed call: %s", h->broken_msg.c_str());
+  return KV_OK;
+}
+
+int finish(kv_hier* h, int rc) {
+  if (!h) return rc;
+  if (rc != KV_OK && h->began && !h->broken) {
+    h->broken = true;
+    h->broken_msg = h->err;
+  }
+  h->began = false;
+  return rc;
+}
+
 
 int upload(kv_hier* h, void* dst, const void* src, size_t bytes) {
   if (bytes == 0) return KV_OK;
@@ -389,6 +426,7 @@ void free_all(kv_hier* h) {
     (void)hipFree(G.victims);
     (void)hipFree(G.protect);
     if (G.ev_done) (void)hipEventDestroy(G.ev_done);
+    if (G.ev_sel) (void)hipEventDestroy(G.ev_sel);
     (void)hipFree(G.loc);
     (void)hipFree(G.req_info);
     (void)hipFree(G.req_counts);
@@ -407,15 +445,18 @@ void free_all(kv_hier* h) {
   (void)hipFree(h->part_ml);
   (void)hipFree(h->d_commit);
   (void)hipFree(h->d_commit_groups);
-  if (h->h_commit) (void)hipHostFree(h->h_commit);
   (void)hipFree(const_cast<uint4**>(h->d_src));
-  if (h->h_src) (void)hipHostFree(const_cast<uint4**>(h->h_src));
+  for (int i = 0; i < kCommitBufs; ++i) {
+    if (h->h_commit[i]) (void)hipHostFree(h->h_commit[i]);
+    if (h->h_src[i]) (void)hipHostFree(const_cast<uint4**>(h->h_src[i]));
+    if (h->ev_commit[i]) (void)hipEventDestroy(h->ev_commit[i]);
+  }
+  if (h->ev_part) (void)hipEventDestroy(h->ev_part);
   for (auto& t : h->pending) { (void)hipEventDestroy(t.a); (void)hipEventDestroy(t.b); }
   for (hipEvent_t e : h->pool) (void)hipEventDestroy(e);
   if (h->ev_in) (void)hipEventDestroy(h->ev_in);
   if (h->ev_out) (void)hipEventDestroy(h->ev_out);
   if (h->work) (void)hipStreamDestroy(h->work);
-  if (h->ev_commit) (void)hipEventDestroy(h->ev_commit);
   if (h->ev_verified) (void)hipEventDestroy(h->ev_verified);
   for (hipEvent_t e : h->ev_backup)
     if (e) (void)hipEventDestroy(e);
@@ -596,6 +637,27 @@ int opt_drop(kv_hier* h, int r) {
   o.n_held[r] = 0;
   o.n_ready[r] = 0;
   return opt_map(h, wd, 0);
+}
+
+// Attention of one request range (+ the merge of its key splits) on stream
+// s.  Split partials live in one buffer of the handle: a launch that uses
+// them waits for the previous user, wherever that ran.
+int attend(kv_hier* h, int g, const AttnArgs& at, hipStream_t s) {
+  const kv_hier_config& c = h->cfg;
+  if (at.splits > 1 && h->part_recorded) HIPCHK(h, hipStreamWaitEvent(s, h->ev_part, 0));
+  int ti = time_begin(h, K_ATTN, g, s);
+  // test hook: the launch reports an error without launching anything
+  HIPCHK(h, (c.flags & KV_FLAG_TEST_FAIL_ATTN) ? hipErrorLaunchFailure
+                                                 : launch_attn(at, c.row_elems, c.d_qk, c.v_off, c.d_v, s));
+  time_end(h, ti, s);
+  if (at.splits > 1) {
+    ti = time_begin(h, K_COMBINE, g, s);
+    HIPCHK(h, launch_attn_combine(at, c.d_v, s));
+    time_end(h, ti, s);
+    HIPCHK(h, hipEventRecord(h->ev_part, s));
+    h->part_recorded = true;
+  }
+  return KV_OK;
 }
 
 }  // namespace
@@ -811,18 +873,24 @@ static int create_impl(kv_hier* h) {
     if ((rc = dev_alloc(h, &h->d_commit_groups, cg.size(), nullptr))) return rc;
     if ((rc = upload(h, h->d_commit_groups, cg.data(), cg.size() * sizeof(CommitGroup)))) return rc;
     if ((rc = dev_alloc(h, &h->d_commit, size_t(2) * N, nullptr))) return rc;
-    void* hc = nullptr;
-    if (hipHostMalloc(&hc, size_t(2) * N * 4, hipHostMallocDefault) != hipSuccess) {
-      return fail(h, KV_ENOMEM, "pinned commit buffer");
-    }
-    h->h_commit = static_cast<int32_t*>(hc);
     const uint4** ds = nullptr;
     if ((rc = dev_alloc(h, &ds, size_t(c.n_groups), nullptr))) return rc;
     h->d_src = ds;
-    void* hs = nullptr;
-    if (hipHostMalloc(&hs, size_t(c.n_groups) * sizeof(void*), hipHostMallocDefault) != hipSuccess)
-      return fail(h, KV_ENOMEM, "pinned commit buffer");
-    h->h_src = static_cast<const uint4**>(hs);
+    for (int i = 0; i < kCommitBufs; ++i) {
+      void* hc = nullptr;
+      if (hipHostMalloc(&hc, size_t(2) * N * 4, hipHostMallocDefault) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(h, KV_ENOMEM, "pinned commit buffer");
+      }
+      h->h_commit[i] = static_cast<int32_t*>(hc);
+      void* hs = nullptr;
+      if (hipHostMalloc(&hs, size_t(c.n_groups) * sizeof(void*), hipHostMallocDefault) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(h, KV_ENOMEM, "pinned commit buffer");
+      }
+      h->h_src[i] = static_cast<const uint4**>(hs);
+      HIPCHK(h, hipEventCreateWithFlags(&h->ev_commit[i], hipEventDisableTiming));
+    }
   }
   if (c.fetch_cus > 0) {
     // partition the CUs: a few for the PCIe-latency-bound fetch, the rest for the step
@@ -844,13 +912,16 @@ static int create_impl(kv_hier* h) {
     HIPCHK(h, hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking));
   }
   HIPCHK(h, hipStreamCreateWithFlags(&h->aux, hipStreamNonBlocking));
-  for (Group& G : h->grp) HIPCHK(h, hipEventCreateWithFlags(&G.ev_done, hipEventDisableTiming));
+  for (Group& G : h->grp) {
+    HIPCHK(h, hipEventCreateWithFlags(&G.ev_done, hipEventDisableTiming));
+    HIPCHK(h, hipEventCreateWithFlags(&G.ev_sel, hipEventDisableTiming));
+  }
   HIPCHK(h, hipEventCreateWithFlags(&h->ev_resolved, hipEventDisableTiming));
   h->ev_attn.assign(h->n_chunks, nullptr);
   for (auto& e : h->ev_attn) HIPCHK(h, hipEventCreateWithFlags(&e, hipEventDisableTiming));
   HIPCHK(h, hipEventCreateWithFlags(&h->ev_in, hipEventDisableTiming));
   HIPCHK(h, hipEventCreateWithFlags(&h->ev_out, hipEventDisableTiming));
-  HIPCHK(h, hipEventCreateWithFlags(&h->ev_commit, hipEventDisableTiming));
+  HIPCHK(h, hipEventCreateWithFlags(&h->ev_part, hipEventDisableTiming));
   // Asynchronous host backup needs every row of the last commit to stay in the
   // ring's tail through the next step (R_d >= 2 K_max); otherwise the backup
   // runs on the caller's stream, ahead of the next step.
@@ -933,8 +1004,7 @@ int kv_hier_host_rows(kv_hier_t* h, int g, int kind, int index, void** rows, int
   return KV_OK;
 }
 
-int kv_hier_set_hist_len(kv_hier_t* h, const int32_t* hist_len) {
-  DeviceGuard dg(h);
+static int set_hist_len_impl(kv_hier_t* h, const int32_t* hist_len) {
   if (!h || !hist_len) return KV_EINVAL;
   for (int r = 0; r < h->cfg.n_req; ++r)
     if (hist_len[r] < 0 || hist_len[r] > h->cfg.hist_cap)
@@ -943,12 +1013,19 @@ int kv_hier_set_hist_len(kv_hier_t* h, const int32_t* hist_len) {
     for (int r = 0; r < h->cfg.n_req; ++r)
       if (h->opt.admitted[r])
         return fail(h, KV_ESTATE, "request %d is admitted: its imported history is fixed until completion", r);
+  begin_work(h);
   int rc = sync_all(h);
   if (rc) return rc;
   h->hist_len.assign(hist_len, hist_len + h->cfg.n_req);
   for (Group& G : h->grp)
     if ((rc = upload(h, G.ring_lo, hist_len, size_t(h->cfg.n_req) * 4))) return rc;
   return KV_OK;
+}
+
+int kv_hier_set_hist_len(kv_hier_t* h, const int32_t* hist_len) {
+  DeviceGuard dg(h);
+  if (int rc = refuse_if_broken(h)) return rc;
+  return finish(h, set_hist_len_impl(h, hist_len));
 }
 
 int kv_hier_hist_len(kv_hier_t* h, int32_t* hist_len) {
@@ -958,8 +1035,7 @@ int kv_hier_hist_len(kv_hier_t* h, int32_t* hist_len) {
   return KV_OK;
 }
 
-int kv_hier_set_hot(kv_hier_t* h, int g, int r, const int32_t* rows, const int32_t* last_used, int n) {
-  DeviceGuard dg(h);
+static int set_hot_impl(kv_hier_t* h, int g, int r, const int32_t* rows, const int32_t* last_used, int n) {
   int rc = check_group(h, g);
   if (rc) return rc;
   if ((rc = check_req(h, r))) return rc;
@@ -979,6 +1055,7 @@ int kv_hier_set_hot(kv_hier_t* h, int g, int r, const int32_t* rows, const int32
     nlu[s] = last_used[s];
     maxlu = std::max(maxlu, last_used[s]);
   }
+  begin_work(h);
   if ((rc = sync_all(h))) return rc;
   Group& G = h->grp[g];
   std::vector<int32_t> old(B);
@@ -1008,8 +1085,13 @@ int kv_hier_set_hot(kv_hier_t* h, int g, int r, const int32_t* rows, const int32
   return KV_OK;
 }
 
-int kv_hier_set_resident(kv_hier_t* h, int g, int r, const uint8_t* bitmap) {
+int kv_hier_set_hot(kv_hier_t* h, int g, int r, const int32_t* rows, const int32_t* last_used, int n) {
   DeviceGuard dg(h);
+  if (int rc = refuse_if_broken(h)) return rc;
+  return finish(h, set_hot_impl(h, g, r, rows, last_used, n));
+}
+
+static int set_resident_impl(kv_hier_t* h, int g, int r, const uint8_t* bitmap) {
   int rc = check_group(h, g);
   if (rc) return rc;
   if ((rc = check_req(h, r))) return rc;
@@ -1031,6 +1113,7 @@ int kv_hier_set_resident(kv_hier_t* h, int g, int r, const uint8_t* bitmap) {
   if (G.res_cursor + int64_t(val.size()) > h->cfg.resident_cap)
     return fail(h, KV_ENOMEM, "resident pool full (%lld of %lld rows)", (long long)(G.res_cursor + val.size()),
                 (long long)h->cfg.resident_cap);
+  begin_work(h);
   if ((rc = sync_all(h))) return rc;
   if ((rc = scatter32(h, G.res_map, idx, val))) return rc;
   if ((rc = rows_from_host(h, G, req, src, dst, G.resident))) return rc;
@@ -1039,11 +1122,17 @@ int kv_hier_set_resident(kv_hier_t* h, int g, int r, const uint8_t* bitmap) {
   return KV_OK;
 }
 
-int kv_hier_clear_resident(kv_hier_t* h, int g) {
+int kv_hier_set_resident(kv_hier_t* h, int g, int r, const uint8_t* bitmap) {
   DeviceGuard dg(h);
+  if (int rc = refuse_if_broken(h)) return rc;
+  return finish(h, set_resident_impl(h, g, r, bitmap));
+}
+
+static int clear_resident_impl(kv_hier_t* h, int g) {
   int rc = check_group(h, g);
   if (rc) return rc;
   if (h->opt.on) return fail(h, KV_ESTATE, "static resident sets are not used with dynamic residency");
+  begin_work(h);
   if ((rc = sync_all(h))) return rc;
   Group& G = h->grp[g];
   HIPCHK(h, launch_fill32(reinterpret_cast<uint32_t*>(G.res_map), 0xffffffffu, size_t(h->cfg.n_req) * h->L, nullptr));
@@ -1053,13 +1142,19 @@ int kv_hier_clear_resident(kv_hier_t* h, int g) {
   return KV_OK;
 }
 
-int kv_hier_ring_load(kv_hier_t* h, int g, int r, int32_t first_pos, const void* rows, int n) {
+int kv_hier_clear_resident(kv_hier_t* h, int g) {
   DeviceGuard dg(h);
+  if (int rc = refuse_if_broken(h)) return rc;
+  return finish(h, clear_resident_impl(h, g));
+}
+
+static int ring_load_impl(kv_hier_t* h, int g, int r, int32_t first_pos, const void* rows, int n) {
   int rc = check_group(h, g);
   if (rc) return rc;
   if ((rc = check_req(h, r))) return rc;
   if (n < 0 || first_pos < 0 || n > h->Rd || (n > 0 && !rows) || int64_t(first_pos) + n != h->hist_len[r])
     return fail(h, KV_EINVAL, "ring_load must cover [first_pos, n_r) with at most R_d=%d rows", h->Rd);
+  begin_work(h);
   if ((rc = sync_all(h))) return rc;
   Group& G = h->grp[g];
   const char* src = static_cast<const char*>(rows);
@@ -1076,9 +1171,14 @@ int kv_hier_ring_load(kv_hier_t* h, int g, int r, int32_t first_pos, const void*
   return upload(h, G.ring_lo + r, &lo, 4);
 }
 
-int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t* topk_idx,
-                        const int32_t* causal_pos, const void* ring_rows, void* out, void* stream) {
+int kv_hier_ring_load(kv_hier_t* h, int g, int r, int32_t first_pos, const void* rows, int n) {
   DeviceGuard dg(h);
+  if (int rc = refuse_if_broken(h)) return rc;
+  return finish(h, ring_load_impl(h, g, r, first_pos, rows, n));
+}
+
+static int verify_step_impl(kv_hier_t* h, int g, const void* queries, const int32_t* topk_idx,
+                        const int32_t* causal_pos, const void* ring_rows, void* out, void* stream) {
   int rc = check_group(h, g);
   if (rc) return rc;
   if (!queries || !causal_pos || !out) return fail(h, KV_EINVAL, "null device pointer");
@@ -1089,6 +1189,7 @@ int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t*
       return fail(h, KV_ESTATE, "group %d uses the plan of group %d: call that group's step first, once per step",
                   g, G0.leader);
   }
+  begin_work(h);
   const kv_hier_config& c = h->cfg;
   hipStream_t caller = static_cast<hipStream_t>(stream);
   hipStream_t s = caller;
@@ -1128,6 +1229,12 @@ int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t*
     // resolution plan and host fetch on the side stream (no event hop between
     // them), after the caller's prior work; the ring write runs beside the plan
     HIPCHK(h, hipStreamWaitEvent(h->side, h->ev_in, 0));
+    // the plan rewrites the set's lists, counts and (through the victims) its
+    // slot tables: every group of the set must have finished reading the
+    // previous ones (its attention, copy-back and counters, all before its
+    // ev_done), whatever stream its step was issued on
+    for (int m = 0; m < h->share; ++m)
+      if (h->grp[g + m].done_recorded) HIPCHK(h, hipStreamWaitEvent(h->side, h->grp[g + m].ev_done, 0));
     // optional-history pages whose copies have completed become ready for
     // this step's resolution (the first group's step is the step boundary)
     if (g == 0 && h->opt.on && (rc = opt_publish_impl(h, false))) return rc;
@@ -1235,14 +1342,7 @@ int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t*
     at.r1 = h->chunk_lo[ch + 1];
     at.splits = h->chunk_splits[ch];
     HIPCHK(h, hipStreamWaitEvent(s, h->ev_fetched[G.member][ch], 0));
-    ti = time_begin(h, K_ATTN, g, s);
-    HIPCHK(h, launch_attn(at, c.row_elems, c.d_qk, c.v_off, c.d_v, s));
-    time_end(h, ti, s);
-    if (at.splits > 1) {
-      ti = time_begin(h, K_COMBINE, g, s);
-      HIPCHK(h, launch_attn_combine(at, c.d_v, s));
-      time_end(h, ti, s);
-    }
+    if ((rc = attend(h, g, at, s))) return rc;
     // copy-back on the aux stream once the victims are chosen, concurrent
     // with the attention (victim slots are not read by the step)
     HIPCHK(h, hipEventRecord(h->ev_attn[ch], s));
@@ -1265,6 +1365,8 @@ int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t*
   // attention waits for this
   HIPCHK(h, hipEventRecord(G.ev_done, h->aux));
   G.done_recorded = true;
+  HIPCHK(h, hipEventRecord(G.ev_sel, s));
+  G.sel_recorded = true;
   G.sel_valid = true;
   if (h->work) {
     HIPCHK(h, hipEventRecord(h->ev_out, s));
@@ -1273,9 +1375,15 @@ int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t*
   return KV_OK;
 }
 
-int kv_hier_verify_reuse(kv_hier_t* h, int g, const void* queries, const int32_t* causal_pos, void* out,
-                         void* stream) {
+int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t* topk_idx,
+                        const int32_t* causal_pos, const void* ring_rows, void* out, void* stream) {
   DeviceGuard dg(h);
+  if (int rc = refuse_if_broken(h)) return rc;
+  return finish(h, verify_step_impl(h, g, queries, topk_idx, causal_pos, ring_rows, out, stream));
+}
+
+static int verify_reuse_impl(kv_hier_t* h, int g, const void* queries, const int32_t* causal_pos, void* out,
+                         void* stream) {
   int rc = check_group(h, g);
   if (rc) return rc;
   if (!queries || !causal_pos || !out) return fail(h, KV_EINVAL, "null device pointer");
@@ -1286,6 +1394,7 @@ int kv_hier_verify_reuse(kv_hier_t* h, int g, const void* queries, const int32_t
   if (!G.sel_valid) return fail(h, KV_ESTATE, "group %d has no selection of this step to reuse", g);
   if (h->arena_owner[a] != g || h->arena_step[a] != G.t)
     return fail(h, KV_ESTATE, "the staged payload of group %d was replaced by a later fetch into arena %d", g, a);
+  begin_work(h);
   hipStream_t caller = static_cast<hipStream_t>(stream);
   hipStream_t s = caller;
   if (h->work) {
@@ -1317,19 +1426,14 @@ int kv_hier_verify_reuse(kv_hier_t* h, int g, const void* queries, const int32_t
   at.head_groups = h->head_groups;
   const float scale = c.softmax_scale > 0.f ? c.softmax_scale : 1.0f / std::sqrt(float(c.d_qk));
   at.scale_log2 = scale * 1.4426950408889634f;
-  {
-    at.r0 = 0;
-    at.r1 = c.n_req;
-    at.splits = h->all_splits;
-    int ti = time_begin(h, K_ATTN, g, s);
-    HIPCHK(h, launch_attn(at, c.row_elems, c.d_qk, c.v_off, c.d_v, s));
-    time_end(h, ti, s);
-    if (at.splits > 1) {
-      ti = time_begin(h, K_COMBINE, g, s);
-      HIPCHK(h, launch_attn_combine(at, c.d_v, s));
-      time_end(h, ti, s);
-    }
-  }
+  // the selection's ring rows, staged rows and lists are complete once its
+  // step's attention ran (that step waited for every fetch chunk)
+  if (G.sel_recorded) HIPCHK(h, hipStreamWaitEvent(s, G.ev_sel, 0));
+  at.r0 = 0;
+  at.r1 = c.n_req;
+  at.splits = h->all_splits;
+  int rc2 = attend(h, g, at, s);
+  if (rc2) return rc2;
   // the arena is released once this reader and the step's own readers and
   // copy-backs are done: the release events now follow all of them
   for (int ch = 0; ch < h->n_chunks; ++ch) {
@@ -1344,8 +1448,14 @@ int kv_hier_verify_reuse(kv_hier_t* h, int g, const void* queries, const int32_t
   return KV_OK;
 }
 
-int kv_hier_commit_src(kv_hier_t* h, const int32_t* accepted, const void* const* src_rows, void* stream) {
+int kv_hier_verify_reuse(kv_hier_t* h, int g, const void* queries, const int32_t* causal_pos, void* out,
+                         void* stream) {
   DeviceGuard dg(h);
+  if (int rc = refuse_if_broken(h)) return rc;
+  return finish(h, verify_reuse_impl(h, g, queries, causal_pos, out, stream));
+}
+
+static int commit_src_impl(kv_hier_t* h, const int32_t* accepted, const void* const* src_rows, void* stream) {
   if (!h || !accepted) return KV_EINVAL;
   const kv_hier_config& c = h->cfg;
   const int N = c.n_req, G = c.n_groups;
@@ -1367,21 +1477,29 @@ int kv_hier_commit_src(kv_hier_t* h, const int32_t* accepted, const void* const*
           return fail(h, KV_EINVAL, "request %d: stored rows of group %d inside the shared prefix", r, g);
     }
   }
+  begin_work(h);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (h->commit_pending) HIPCHK(h, hipEventSynchronize(h->ev_commit));
+  // staging buffer of this commit: the one whose copy was issued kCommitBufs
+  // commits ago (the host waits only if that copy has not run yet)
+  const int cb = int(h->n_commits % kCommitBufs);
+  if (h->commit_pending[cb]) {
+    HIPCHK(h, hipEventSynchronize(h->ev_commit[cb]));
+    h->commit_pending[cb] = false;
+  }
+  int32_t* hc = h->h_commit[cb];
+  const uint4** hs = h->h_src[cb];
   for (int r = 0; r < N; ++r) {
-    h->h_commit[r] = h->hist_len[r];
-    h->h_commit[N + r] = accepted[r];
+    hc[r] = h->hist_len[r];
+    hc[N + r] = accepted[r];
   }
   for (int g = 0; g < G; ++g)
-    h->h_src[g] = (src_rows && h->grp[g].m > 1) ? static_cast<const uint4*>(src_rows[g]) : nullptr;
-  // the previous backup still reads the commit buffers until it ends
+    hs[g] = (src_rows && h->grp[g].m > 1) ? static_cast<const uint4*>(src_rows[g]) : nullptr;
+  // the previous backup still reads the device commit buffers until it ends
   if (h->backup && h->n_commits >= 1) HIPCHK(h, hipStreamWaitEvent(s, h->ev_backup[(h->n_commits - 1) % 2], 0));
-  HIPCHK(h, hipMemcpyAsync(h->d_commit, h->h_commit, size_t(2) * N * 4, hipMemcpyHostToDevice, s));
-  HIPCHK(h, hipMemcpyAsync(const_cast<uint4**>(h->d_src), h->h_src, size_t(G) * sizeof(void*),
-                           hipMemcpyHostToDevice, s));
-  HIPCHK(h, hipEventRecord(h->ev_commit, s));
-  h->commit_pending = true;
+  HIPCHK(h, hipMemcpyAsync(h->d_commit, hc, size_t(2) * N * 4, hipMemcpyHostToDevice, s));
+  HIPCHK(h, hipMemcpyAsync(const_cast<uint4**>(h->d_src), hs, size_t(G) * sizeof(void*), hipMemcpyHostToDevice, s));
+  HIPCHK(h, hipEventRecord(h->ev_commit[cb], s));
+  h->commit_pending[cb] = true;
   // compressed sources: the caller's rows are consumed in its stream order, so
   // their host copy exists before the next step fetches (they have no tail)
   if (any_compressed)
@@ -1406,13 +1524,18 @@ int kv_hier_commit_src(kv_hier_t* h, const int32_t* accepted, const void* const*
   return KV_OK;
 }
 
+int kv_hier_commit_src(kv_hier_t* h, const int32_t* accepted, const void* const* src_rows, void* stream) {
+  DeviceGuard dg(h);
+  if (int rc = refuse_if_broken(h)) return rc;
+  return finish(h, commit_src_impl(h, accepted, src_rows, stream));
+}
+
 int kv_hier_commit(kv_hier_t* h, const int32_t* accepted, void* stream) {
   DeviceGuard dg(h);
   return kv_hier_commit_src(h, accepted, nullptr, stream);
 }
 
-int kv_hier_set_compression(kv_hier_t* h, int g, int32_t m) {
-  DeviceGuard dg(h);
+static int set_compression_impl(kv_hier_t* h, int g, int32_t m) {
   int rc = check_group(h, g);
   if (rc) return rc;
   Group& G = h->grp[g];
@@ -1420,6 +1543,7 @@ int kv_hier_set_compression(kv_hier_t* h, int g, int32_t m) {
   if (G.calls > 0) return fail(h, KV_ESTATE, "group %d has already run a step", g);
   if (m > 1 && h->opt.on) return fail(h, KV_ESTATE, "dynamic residency pages assume uncompressed sources");
   if (m > 1 && h->share > 1) return fail(h, KV_ESTATE, "plan-sharing sets assume uncompressed sources");
+  begin_work(h);
   if ((rc = sync_all(h))) return rc;
   G.m = m;
   CommitGroup cg;
@@ -1428,6 +1552,12 @@ int kv_hier_set_compression(kv_hier_t* h, int g, int32_t m) {
   cg.m = m;
   cg.cmax = (h->cfg.q_max + m - 1) / m;
   return upload(h, h->d_commit_groups + g, &cg, sizeof cg);
+}
+
+int kv_hier_set_compression(kv_hier_t* h, int g, int32_t m) {
+  DeviceGuard dg(h);
+  if (int rc = refuse_if_broken(h)) return rc;
+  return finish(h, set_compression_impl(h, g, m));
 }
 
 int kv_hier_stats(kv_hier_t* h, int g, kv_hier_counters* cum, kv_hier_counters* last) {
@@ -1592,7 +1722,8 @@ int kv_hier_sync(kv_hier_t* h) {
 int kv_hier_set_flags(kv_hier_t* h, int32_t flags) {
   DeviceGuard dg(h);
   if (!h) return KV_EINVAL;
-  if (flags & ~(KV_FLAG_TIMING | KV_FLAG_POISON | KV_FLAG_TIMING_ATTN | KV_FLAG_SERIAL | KV_FLAG_SYNC_BACKUP))
+  if (flags & ~(KV_FLAG_TIMING | KV_FLAG_POISON | KV_FLAG_TIMING_ATTN | KV_FLAG_SERIAL | KV_FLAG_SYNC_BACKUP |
+                KV_FLAG_TEST_FAIL_ATTN))
     return fail(h, KV_EINVAL, "unknown flags %d", flags);
   int rc = sync_all(h);
   if (rc) return rc;
@@ -1600,11 +1731,12 @@ int kv_hier_set_flags(kv_hier_t* h, int32_t flags) {
   return KV_OK;
 }
 
-int kv_hier_cache_snapshot(kv_hier_t* h, int g, int op) {
-  DeviceGuard dg(h);
+static int cache_snapshot_impl(kv_hier_t* h, int g, int op) {
   int rc = check_group(h, g);
   if (rc) return rc;
   if (op != 0 && op != 1) return fail(h, KV_EINVAL, "snapshot op %d", op);
+  if (op == 1 && h->grp[g].snap_t < 0) return fail(h, KV_ESTATE, "no snapshot of group %d", g);
+  begin_work(h);
   if ((rc = sync_all(h))) return rc;
   Group& G = h->grp[g];
   const size_t NB = size_t(h->cfg.n_req) * h->cfg.hot_slots, NL = size_t(h->cfg.n_req) * h->L;
@@ -1633,11 +1765,16 @@ int kv_hier_cache_snapshot(kv_hier_t* h, int g, int op) {
   return KV_OK;
 }
 
+int kv_hier_cache_snapshot(kv_hier_t* h, int g, int op) {
+  DeviceGuard dg(h);
+  if (int rc = refuse_if_broken(h)) return rc;
+  return finish(h, cache_snapshot_impl(h, g, op));
+}
+
 // ---------------------------------------------------------------- dynamic optional residency
 
-int kv_hier_opt_admit(kv_hier_t* h, int r, int32_t required_pages, const int32_t* order, int n_order,
+static int opt_admit_impl(kv_hier_t* h, int r, int32_t required_pages, const int32_t* order, int n_order,
                       int32_t* n_reclaimed) {
-  DeviceGuard dg(h);
   if (!h) return KV_EINVAL;
   Opt& o = h->opt;
   if (!o.on) return fail(h, KV_ESTATE, "dynamic residency is off (opt_page_rows = 0)");
@@ -1666,6 +1803,7 @@ int kv_hier_opt_admit(kv_hier_t* h, int r, int32_t required_pages, const int32_t
                   (long long)deficit, (long long)covered);
     }
   }
+  begin_work(h);
   for (int i = 0; i < q; ++i)
     if ((rc = opt_drop(h, order[i]))) return rc;
   o.requests_reclaimed += q;
@@ -1680,14 +1818,21 @@ int kv_hier_opt_admit(kv_hier_t* h, int r, int32_t required_pages, const int32_t
   return KV_OK;
 }
 
-int kv_hier_opt_complete(kv_hier_t* h, int r) {
+int kv_hier_opt_admit(kv_hier_t* h, int r, int32_t required_pages, const int32_t* order, int n_order,
+                      int32_t* n_reclaimed) {
   DeviceGuard dg(h);
+  if (int rc = refuse_if_broken(h)) return rc;
+  return finish(h, opt_admit_impl(h, r, required_pages, order, n_order, n_reclaimed));
+}
+
+static int opt_complete_impl(kv_hier_t* h, int r) {
   if (!h) return KV_EINVAL;
   Opt& o = h->opt;
   if (!o.on) return fail(h, KV_ESTATE, "dynamic residency is off (opt_page_rows = 0)");
   int rc = check_req(h, r);
   if (rc) return rc;
   if (!o.admitted[r]) return fail(h, KV_ESTATE, "request %d is not admitted", r);
+  begin_work(h);
   if ((rc = opt_drop(h, r))) return rc;
   o.admitted[r] = 0;
   o.sum_req -= o.required[r];
@@ -1697,12 +1842,18 @@ int kv_hier_opt_complete(kv_hier_t* h, int r) {
   return KV_OK;
 }
 
-int kv_hier_opt_populate(kv_hier_t* h, int32_t max_pages, int32_t* n_assigned) {
+int kv_hier_opt_complete(kv_hier_t* h, int r) {
   DeviceGuard dg(h);
+  if (int rc = refuse_if_broken(h)) return rc;
+  return finish(h, opt_complete_impl(h, r));
+}
+
+static int opt_populate_impl(kv_hier_t* h, int32_t max_pages, int32_t* n_assigned) {
   if (!h) return KV_EINVAL;
   Opt& o = h->opt;
   if (!o.on) return fail(h, KV_ESTATE, "dynamic residency is off (opt_page_rows = 0)");
   if (max_pages < 0) return fail(h, KV_EINVAL, "negative page bound");
+  begin_work(h);
   const int N = h->cfg.n_req;
   const int64_t budget = int64_t(o.M) - o.sum_req - o.reserve - o.sum_held;
   const int64_t limit = std::min<int64_t>(max_pages, std::max<int64_t>(0, budget));
@@ -1758,12 +1909,24 @@ int kv_hier_opt_populate(kv_hier_t* h, int32_t max_pages, int32_t* n_assigned) {
   return KV_OK;
 }
 
-int kv_hier_opt_publish(kv_hier_t* h, int wait) {
+int kv_hier_opt_populate(kv_hier_t* h, int32_t max_pages, int32_t* n_assigned) {
   DeviceGuard dg(h);
+  if (int rc = refuse_if_broken(h)) return rc;
+  return finish(h, opt_populate_impl(h, max_pages, n_assigned));
+}
+
+static int opt_publish_entry(kv_hier_t* h, int wait) {
   if (!h) return KV_EINVAL;
   if (!h->opt.on) return fail(h, KV_ESTATE, "dynamic residency is off (opt_page_rows = 0)");
   if (wait != 0 && wait != 1) return fail(h, KV_EINVAL, "wait must be 0 or 1");
+  begin_work(h);
   return opt_publish_impl(h, wait == 1);
+}
+
+int kv_hier_opt_publish(kv_hier_t* h, int wait) {
+  DeviceGuard dg(h);
+  if (int rc = refuse_if_broken(h)) return rc;
+  return finish(h, opt_publish_entry(h, wait));
 }
 
 int kv_hier_opt_query(kv_hier_t* h, int r, int32_t n_pages, int32_t* held, uint8_t* ready,

@@ -33,6 +33,20 @@
  * Conventions
  *   - Every call returns KV_OK (0) or a negative KV_E* code; no exception
  *     crosses the ABI.  kv_hier_last_error() gives a message for the handle.
+ *   - Every argument is checked before a call changes anything: a call that
+ *     returns KV_EINVAL, KV_ESTATE, KV_EUNSUPPORTED or KV_EWAIT has changed
+ *     nothing.  If a call that changes state fails after its checks (a HIP
+ *     runtime error, a failed pinned allocation), the handle's device state
+ *     may be partly updated: the handle is then latched, and every later call
+ *     that changes state or enqueues device work returns KV_ESTATE (its
+ *     message names the first failure).  Calls that only read (stats, lists,
+ *     info, hist_len, sync, last_error) and kv_hier_destroy still work.
+ *   - Streams: steps, Reuse layers and commits may be issued on different
+ *     caller streams of the handle's device; the library orders its own work
+ *     between them with events (each layer's plan after every earlier reader
+ *     of the plan state it rewrites, a Reuse after the step whose selection it
+ *     reads, every launch using the shared split-key partials after the
+ *     previous one).  The caller orders its own buffers.
  *   - "device" pointers are HIP device allocations owned by the caller that
  *     must stay valid until the stream passes the step; "host" pointers are
  *     ordinary host memory read or written before the call returns.
@@ -74,8 +88,10 @@ enum {
                               events then sit on no stream that gates the host fetch   */
   KV_FLAG_SERIAL = 8,     /* measurement: the step's attention starts only after its whole
                              host fetch, so it runs alone on the GPU (slower steps)     */
-  KV_FLAG_SYNC_BACKUP = 16 /* measurement: commit's host backup runs on the caller's stream,
+  KV_FLAG_SYNC_BACKUP = 16, /* measurement: commit's host backup runs on the caller's stream,
                              ahead of the next step, instead of beside it             */
+  KV_FLAG_TEST_FAIL_ATTN = 32 /* test hook: every attention launch reports a HIP error without
+                             launching anything (exercises the failure latch below)   */
 };
 
 typedef struct kv_hier kv_hier_t;  /* opaque, owned by the library */
@@ -185,7 +201,10 @@ typedef struct {
                                bitmap's LDS)                                             */
 } kv_hier_info;
 
-/* Creates a handle: allocates hot caches, slot tables, maps, rings, staging
+/* Creates a handle ("Adaptive DHiSparse" §2.2 fixed-cache offloading and
+ * §3.4: per request and source a bounded hot cache of B rows, the draft ring
+ * of eq. (9), chi staging arenas shared by the layer groups, host copies of the
+ * history): allocates hot caches, slot tables, maps, rings, staging
  * arenas, plan buffers, a side stream and events on the current HIP device,
  * and pinned host history for every group.  Every later call on the handle
  * runs on that device whatever device is current when it is made (the
@@ -215,7 +234,9 @@ int kv_hier_host_rows(kv_hier_t *h, int g, int kind, int index, void **rows, int
  * ring of every group empty below n_r.  Eq. (5): query j sits at n_r + j. */
 int kv_hier_set_hist_len(kv_hier_t *h, const int32_t *hist_len);
 
-/* Hot-cache contents of (g, r): n <= B host rows (-1 = empty slot) with their
+/* Hot-cache contents of (g, r) ("Adaptive DHiSparse" §2.2: the bounded GPU
+ * cache of one request and source, whose LRU stamps order the victims): n <= B
+ * host rows (-1 = empty slot) with their
  * last-used stamps (>= 0); rows must be distinct and < hist_cap.  Row bytes
  * are copied from the host backing.  Synchronous. */
 int kv_hier_set_hot(kv_hier_t *h, int g, int r, const int32_t *rows, const int32_t *last_used, int n);
@@ -229,7 +250,8 @@ int kv_hier_set_resident(kv_hier_t *h, int g, int r, const uint8_t *bitmap);
 int kv_hier_clear_resident(kv_hier_t *h, int g);
 
 /* Loads committed positions first_pos .. n_r-1 (n rows, host bf16
- * [n][row_elems]) into the ring of (g, r); first_pos + n must equal n_r and
+ * [n][row_elems]) into the ring of (g, r) at the addresses of
+ * "Adaptive DHiSparse" §3.4 eq. (10), phi(r, t) = r*R_d + (t mod R_d); first_pos + n must equal n_r and
  * n <= R_d.  Synchronous. */
 int kv_hier_ring_load(kv_hier_t *h, int g, int r, int32_t first_pos, const void *rows, int n);
 
@@ -314,12 +336,18 @@ int kv_hier_set_compression(kv_hier_t *h, int g, int32_t m);
 int kv_hier_commit_src(kv_hier_t *h, const int32_t *accepted, const void *const *src_rows, void *stream);
 
 /* Waits for all work of the handle, then returns group g's counters:
- * cumulative over all steps and of the last step.  Either pointer may be NULL. */
+ * cumulative over all steps and of the last step.  Either pointer may be NULL.
+ * They are the quantities "Adaptive DHiSparse" §4.3.1-4.3.2 measures: the
+ * share of selected rows fetched from the host (sel_miss / selections, Table
+ * A1), distinct fetched rows and bytes (the resolver's unique host-miss
+ * payload, Figure 8a), and missing selections per fetched row. */
 int kv_hier_stats(kv_hier_t *h, int g, kv_hier_counters *cumulative, kv_hier_counters *last);
 int kv_hier_reset_stats(kv_hier_t *h);
 
 /* Waits, then copies request r's lists of the last step of group g (a
- * follower's are its leader's). */
+ * follower's are its leader's): the union U_r of eq. (6), the host-recovery
+ * set D_r of eq. (2) in staging order, and the location of every list entry
+ * in selection order, eq. (12). */
 int kv_hier_last_lists(kv_hier_t *h, int g, int r, kv_hier_lists *out);
 
 /* Waits, then copies the slot table of (g, r): host int32[B] rows and stamps
