@@ -28,6 +28,7 @@ if ROOT not in sys.path:
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_PCIE_GBS = 64.0           # PCIe 5.0 x16, one direction (host link of the MI355X)
+CPU_SHARE_THREADS = 16         # host threads per GPU on the GPU host (worker pools are sized to it)
 
 
 def log(*a):
@@ -94,7 +95,7 @@ def resolver_sweep(args):
     import torch
 
     from hierarchical_sparse_kv_verify_amd import KV_FLAG_TIMING
-    from tests.pair import build_pair, to_device
+    from workloads.load import device_inputs as to_device, load_library
     from workloads import WORKLOADS, make_step_inputs, shrink
 
     torch.cuda.set_device(0)
@@ -103,9 +104,9 @@ def resolver_sweep(args):
     points = []
     for name, kw in patterns:
         w = shrink(base, **kw)
-        pair = build_pair(w, warm=False, with_oracle=False, lib_kw=dict(n_chunks=1))
-        lib = pair.lib
-        si = make_step_inputs(w, 0, 0, pair.hist_len)
+        ld = load_library(w, warm=False, lib_kw=dict(n_chunks=1))
+        lib = ld.lib
+        si = make_step_inputs(w, 0, 0, ld.hist_len)
         d = to_device(si)
         out = torch.zeros((w.n_req, w.q_max, w.n_heads, w.d_v), dtype=torch.int16, device="cuda")
         lib.set_flags(KV_FLAG_TIMING)
@@ -142,7 +143,7 @@ def resolver_sweep(args):
                                    pm[0], pm[1], pm[2]))
         lib.set_flags(0)
         lib.close()
-        del pair, lib
+        del ld, lib
     x = np.array([p["miss_mb"] for p in points])
     y = np.array([p["resolver_ms"]["median"] for p in points])
     A = np.stack([x, np.ones_like(x)], axis=1)
@@ -197,7 +198,7 @@ def main():
     import torch
 
     from hierarchical_sparse_kv_verify_amd import KV_FLAG_SERIAL, KV_FLAG_TIMING, KV_FLAG_TIMING_ATTN
-    from tests.pair import build_pair, to_device
+    from workloads.load import device_inputs as to_device, load_library
     from workloads import WORKLOADS, make_history, make_step_inputs, shrink
     from workloads.gen import make_hist_len
 
@@ -210,9 +211,9 @@ def main():
     hl = make_hist_len(w)
     hists = [make_history(w, g, hl, progress=log if w.n_prefix > 4 else None) for g in range(w.n_groups)]
     log("bench: host rows ready (%.1fs); creating the library state" % (time.perf_counter() - t_setup))
-    pair = build_pair(w, rho=args.rho, with_oracle=False, histories=hists,
+    ld = load_library(w, rho=args.rho, histories=hists,
                       lib_kw=dict(n_chunks=args.n_chunks, fetch_cus=args.fetch_cus, fetch_wgs=args.fetch_wgs))
-    lib = pair.lib
+    lib = ld.lib
     G = w.n_groups
     sis = [make_step_inputs(w, g, 0, hl) for g in range(G)]
     dev = [to_device(si) for si in sis]
@@ -351,7 +352,15 @@ def main():
     roofline["traffic"] = attn_traffic(attn_bytes / n_attn_live) if same_launch else None
     roofline["timing"] = "HIP events around every attention launch during the timed steps"
     rooflines["sparse_attn"]["traffic"] = roofline["traffic"]
-    roofline_host = dict(rooflines["miss_gather"])
+    # host-link bytes from the IO read counter: rows of the shared prefix that
+    # two requests of a chunk both miss can be served on the GPU side
+    mg = rooflines["miss_gather"]
+    mg["traffic"] = link_traffic(mg["work_per_launch"]) if same_launch else None
+    if mg["traffic"] is not None:
+        link_gbs = mg["traffic"] / (mg["avg_launch_ms"] / 1000.0) / 1e9
+        mg["link_achieved_GBs"] = round(link_gbs, 3)
+        mg["link_frac_of_measured_h2d"] = round(link_gbs / h2d, 4)
+    roofline_host = dict(mg)
     roofline_host["kernel"] = "miss_gather"
 
     cpu = None
@@ -410,7 +419,7 @@ def load_step(args):
     import numpy as np
     import torch
 
-    from tests.pair import build_pair, to_device
+    from workloads.load import device_inputs as to_device, load_library
     from workloads import WORKLOADS, make_history, make_step_inputs
     from workloads.gen import make_hist_len
 
@@ -434,8 +443,8 @@ def load_step(args):
         kw = dict(resident_cap=M * P, opt_page_rows=P, opt_reserve=args.reserve_pages) if arm == "on" else {}
         log("load step: arm %s, pool %d pages of %d rows (%.2f GB per group)" %
             (arm, M if arm == "on" else 0, P, M * P * 2 * w.row_elems / 1e9 if arm == "on" else 0.0))
-        pair = build_pair(w, with_oracle=False, histories=hists, lib_kw=kw)
-        lib = pair.lib
+        ld = load_library(w, histories=hists, lib_kw=kw)
+        lib = ld.lib
         assert lib.info["ring_rows"] == ring_rows
         dev = [to_device(si) for si in sis]
         causal = {}
@@ -520,7 +529,7 @@ def load_step(args):
                        pages_reclaimed=inf["pages_reclaimed"], bytes_populated=inf["bytes_populated"])
         report[arm] = res
         lib.close()
-        del pair, lib, dev, causal, out
+        del ld, lib, dev, causal, out
         torch.cuda.empty_cache()
     line = {"metric": "host-fetched share of selections under a load step, optional residency on/off",
             "unit": "fraction", "n_gpus": 1, "data": "synthetic",
@@ -543,7 +552,7 @@ def shared_source(args):
     import numpy as np
     import torch
 
-    from tests.pair import build_pair, to_device
+    from workloads.load import device_inputs as to_device, load_library
     from workloads import WORKLOADS, make_history, make_step_inputs, shrink
     from workloads.gen import make_hist_len
 
@@ -552,8 +561,8 @@ def shared_source(args):
     G, R = w.n_groups, args.reuse_per_selection
     hl = make_hist_len(w)
     hists = [make_history(w, g, hl) for g in range(G)]
-    pair = build_pair(w, with_oracle=False, histories=hists)
-    lib = pair.lib
+    ld = load_library(w, histories=hists)
+    lib = ld.lib
     dev = torch.device("cuda")
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     layers = []          # per source: (selection A inputs, reindex topk, consumer query sets)
@@ -658,7 +667,7 @@ def rounds(args):
     import torch
 
     from hierarchical_sparse_kv_verify_amd import KV_FLAG_SYNC_BACKUP
-    from tests.pair import build_pair, to_device
+    from workloads.load import device_inputs as to_device, load_library
     from workloads import WORKLOADS, make_accepted, make_history, make_step_inputs, shrink
     from workloads.gen import make_hist_len
 
@@ -681,9 +690,9 @@ def rounds(args):
         n = n + 1 + acc
     report = {}
     for arm in ("async", "sync"):
-        pair = build_pair(w, with_oracle=False, histories=hists,
+        ld = load_library(w, histories=hists,
                           lib_kw=dict(flags=KV_FLAG_SYNC_BACKUP if arm == "sync" else 0))
-        lib = pair.lib
+        lib = ld.lib
         out = torch.zeros((w.n_req, w.q_max, w.n_heads, w.d_v), dtype=torch.int16, device="cuda")
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         tails = sels = fetched = 0
@@ -710,7 +719,7 @@ def rounds(args):
                                                       / R / 1e6, 2))
         log("rounds: arm %s: %s" % (arm, report[arm]))
         lib.close()
-        del pair, lib
+        del ld, lib
         torch.cuda.empty_cache()
     print(json.dumps({"metric": "decode rounds with commits: host backup beside vs ahead of the next round",
                       "unit": "ms per round", "n_gpus": 1, "data": "synthetic", "rounds": R,
@@ -735,14 +744,13 @@ def measure_h2d(torch, mib=512, reps=3):
     return best
 
 
-def attn_traffic(algo_bytes_per_launch):
-    """HBM bytes per attention launch of the default mla128 step from the
-    committed rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, scaled by a
-    plain copy's reading), or None when the kernel source changed since the
-    counters were taken."""
+def _counter_ratio(profile, key, source):
+    """A counter-measured bytes-per-algorithmic-byte ratio from a committed
+    rocprofv3 summary (its ``traffic:`` line), or None when the kernel's source
+    file changed since the counters were taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "sparse_attn_mla128_traffic.md")
-    src = os.path.join(ROOT, "hierarchical_sparse_kv_verify_amd", "csrc", "attn.hip")
+    path = os.path.join(ROOT, "profiles", profile)
+    src = os.path.join(ROOT, "hierarchical_sparse_kv_verify_amd", "csrc", source)
     try:
         text = open(path).read()
         digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
@@ -754,9 +762,24 @@ def attn_traffic(algo_bytes_per_launch):
             for kv in ln[len("traffic:"):].split():
                 k, _, v = kv.partition("=")
                 vals[k] = v
-    if vals.get("attn_sha256") != digest or "bytes_per_algo_byte" not in vals:
+    tag = os.path.splitext(source)[0] + "_sha256"
+    if vals.get(tag) != digest or key not in vals:
         return None
-    return round(float(vals["bytes_per_algo_byte"]) * algo_bytes_per_launch, 1)
+    return float(vals[key])
+
+
+def attn_traffic(algo_bytes_per_launch):
+    """HBM bytes per attention launch of the default mla128 step: DRAM reads +
+    writes from the TCC counters (profiles/sparse_attn_mla128_traffic.md)."""
+    r = _counter_ratio("sparse_attn_mla128_traffic.md", "bytes_per_algo_byte", "attn.hip")
+    return None if r is None else round(r * algo_bytes_per_launch, 1)
+
+
+def link_traffic(algo_bytes_per_launch):
+    """Host-link bytes per fetch launch of the default mla128 step: the TCC IO
+    read counter (profiles/miss_gather_mla128_host_link.md)."""
+    r = _counter_ratio("miss_gather_mla128_host_link.md", "io_bytes_per_algo_byte", "copy.hip")
+    return None if r is None else round(r * algo_bytes_per_launch, 1)
 
 
 def _cpu_model():
@@ -773,14 +796,21 @@ def cpu_baseline(w, hists, hl, sis, n_req_sample, n_groups_sample):
     """The oracle, as it stands, on the host cores over the first requests of
     the first layer groups (resolution + attention of all their queries)."""
     import oracle
-    from tests.pair import oracle_config, prefill_rows
     from workloads import make_hot_warm_set
+    from workloads.load import prefill_rows
 
-    cores = min(len(os.sched_getaffinity(0)), 16)
+    # the GPU box gives each GPU a share of 16 host threads, whatever the
+    # affinity mask shows: the oracle's worker pool is sized to that share
+    online = len(os.sched_getaffinity(0))
+    cores = min(online, CPU_SHARE_THREADS)
     reqs = list(range(min(n_req_sample, w.n_req)))
     groups = list(range(max(1, min(n_groups_sample, w.n_groups))))
     # no commit happens here, so the oracle may read the generator's rows in place
-    orc = oracle.HierOracle(oracle_config(w), hists, hl, requests=reqs)
+    ocfg = oracle.OracleConfig(
+        n_req=w.n_req, n_groups=w.n_groups, hist_cap=w.hist_cap, n_prefix=w.n_prefix, prefix_len=w.prefix_len,
+        row_elems=w.row_elems, d_qk=w.d_qk, v_off=w.v_off, d_v=w.d_v, n_heads=w.n_heads, q_max=w.q_max,
+        topk=w.topk, hot_slots=w.hot_slots, ring_window=w.ring_window, ring_page=w.ring_page)
+    orc = oracle.HierOracle(ocfg, hists, hl, requests=reqs)
     for g in groups:
         for r, hs in enumerate(make_hot_warm_set(w, g, hl, sis[g])):
             orc.set_hot(g, r, hs[0], hs[1])
@@ -800,7 +830,9 @@ def cpu_baseline(w, hists, hl, sis, n_req_sample, n_groups_sample):
     value = nq / (dt * w.n_groups / len(groups))
     log("bench: oracle %.2fs for %d query tokens of %d layer groups" % (dt, nq, len(groups)))
     return {"value": round(value, 3), "unit": "query-tokens/s", "cores": cores, "kind": "oracle",
-            "cpu_model": _cpu_model(),
+            "online_cores": online, "cpu_model": _cpu_model(),
+            "threads_note": "oracle threads = min(online cores, %d): the GPU host's CPU share per GPU"
+                            % CPU_SHARE_THREADS,
             "sample": "%d requests x %d queries of layer groups 0..%d of %s (resolution + attention), "
                       "scaled to %d layer groups per step; %.2f s" % (len(reqs), w.q_max, len(groups) - 1,
                                                                       w.name, w.n_groups, dt)}

@@ -89,12 +89,37 @@ def test_null_handle_calls_are_rejected(lib):
 
 
 def test_benchmark_timed_path_does_not_load_the_oracle():
-    """bench.py's GPU path builds its handle through tests/pair.py without an
-    oracle: importing what it imports must not load any module of oracle/."""
+    """bench.py's GPU path builds its handle with workloads.load, never through
+    test code: importing what it imports must load no module of oracle/ and no
+    module of tests/."""
     import subprocess
     import sys
-    code = ("import sys; sys.path.insert(0, %r); import bench, tests.pair; "
-            "print(sorted(m for m in sys.modules if m == 'oracle' or m.startswith('oracle.')))" % ROOT)
+    code = ("import sys; sys.path.insert(0, %r); import bench, workloads.load; "
+            "print(sorted(m for m in sys.modules if m.split('.')[0] in ('oracle', 'tests')))" % ROOT)
     res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120, cwd=ROOT)
     assert res.returncode == 0, res.stderr
     assert res.stdout.strip().splitlines()[-1] == "[]", res.stdout
+
+
+def test_sanitized_build_is_the_one_loaded(lib):
+    """Under the sanitizer run (KVHIER_EXPECT_SANITIZED set) the library in the
+    process is the host-sanitized build, and the sanitizer runtime is loaded."""
+    if not os.environ.get("KVHIER_EXPECT_SANITIZED"):
+        pytest.skip("only in the sanitizer run")
+    maps = open("/proc/self/maps").read()
+    assert os.environ["KVHIER_LIBRARY"] in maps
+    assert "asan" in maps
+
+
+def test_create_that_fails_after_its_checks_cleans_up(lib):
+    """A valid configuration on a host without a GPU: creation passes its
+    checks, fails at its first device call with KV_EHIP and a message, and
+    frees what it had allocated (the sanitizer run checks the frees)."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("needs a host without a GPU")
+    from hierarchical_sparse_kv_verify_amd import KVHier, KVHierError
+    for _ in range(2):
+        with pytest.raises(KVHierError) as ei:
+            KVHier(**_cfg())
+        assert ei.value.code == -3 and "kv_hier_create: " in str(ei.value)

@@ -19,7 +19,9 @@ drew.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
+import os
 from dataclasses import dataclass, field
 from typing import Optional
 
@@ -183,6 +185,29 @@ def _normal_bf16(rng: np.random.Generator, shape) -> np.ndarray:
     return bf16_bits_from_f32(rng.standard_normal(shape, dtype=np.float32))
 
 
+def _fill_normal_bf16(rng: np.random.Generator, out: np.ndarray, block_rows: int = 8192) -> None:
+    """out[:] = N(0, 1) rounded to bf16, drawn in blocks of rows: the same
+    values as one draw of the whole array (the generator fills sequentially),
+    without a full-size float32 temporary."""
+    for i in range(0, out.shape[0], block_rows):
+        n = min(block_rows, out.shape[0] - i)
+        out[i:i + n] = _normal_bf16(rng, (n,) + out.shape[1:])
+
+
+def _pool_map(fn, items) -> None:
+    """Runs fn over independent items (each with its own generator and its own
+    output slice) on up to 16 threads; the results do not depend on the order."""
+    items = list(items)
+    workers = max(1, min(16, os.cpu_count() or 1, len(items)))
+    if workers == 1:
+        for x in items:
+            fn(x)
+        return
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        for _ in ex.map(fn, items):
+            pass
+
+
 def _seeds(w: Workload, group: int, purpose: int, *extra: int, n: int):
     ss = np.random.SeedSequence([SEED, w.config_id, group, purpose, *extra])
     return [np.random.default_rng(s) for s in ss.spawn(n)]
@@ -226,14 +251,20 @@ def make_history(w: Workload, group: int, hist_len: Optional[np.ndarray] = None,
     npfx = w.n_prefix if w.n_prefix > 0 else 0
     rngs = _seeds(w, group, _P_HISTORY, n=npfx + w.n_req)
     prefix = np.empty((max(npfx, 1), plen, w.row_elems), dtype=np.uint16)
-    for p in range(npfx):
-        prefix[p] = _normal_bf16(rngs[p], (plen, w.row_elems))
+
+    def one_prefix(p):
+        _fill_normal_bf16(rngs[p], prefix[p])
         if progress is not None:
             progress("history of group %d: prefix %d of %d ready" % (group, p + 1, npfx))
+
+    _pool_map(one_prefix, range(npfx))
     tails = np.zeros((w.n_req, w.hist_cap - plen, w.row_elems), dtype=np.uint16)
-    for r in range(w.n_req):
+
+    def one_tail(r):
         n_own = int(hist_len[r]) - plen
-        tails[r, :n_own] = _normal_bf16(rngs[npfx + r], (n_own, w.row_elems))
+        _fill_normal_bf16(rngs[npfx + r], tails[r, :n_own])
+
+    _pool_map(one_tail, range(w.n_req))
     return History(prefix=prefix, tails=tails, hist_len=hist_len.astype(np.int32).copy())
 
 
@@ -312,7 +343,8 @@ def make_step_inputs(w: Workload, group: int, step: int, hist_len: np.ndarray,
     drawn = [None] * N
     req_iter = range(N) if requests is None else [int(x) for x in requests]
     m = positions_per_row(w, group)
-    for r in req_iter:
+
+    def one_request(r):
         rng = rngs[r]
         n_pos = int(hist_len[r])
         n_r = n_pos // m                  # stored rows the selections draw from
@@ -359,6 +391,8 @@ def make_step_inputs(w: Workload, group: int, step: int, hist_len: np.ndarray,
             queries[r, j] = _normal_bf16(rng, (w.n_heads, w.d_qk))
             block[r, j] = _normal_bf16(rng, (w.row_elems,))
         drawn[r] = (core, privs)
+
+    _pool_map(one_request, req_iter)
     return StepInputs(topk=topk, causal_pos=causal, queries=queries, block_rows=block,
                       k_active=k_active.astype(np.int32), drawn=drawn)
 
