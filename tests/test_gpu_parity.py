@@ -450,10 +450,11 @@ def test_full_size_mla128_sampled():
     default chunked launch): sampled requests bit-exact, sampled queries within
     tolerance; whole-step counters consistent."""
     w = WORKLOADS["mla128"]
-    reqs = [0, 37, 126, 127]
+    reqs = [0, 37, 70, 126, 127]          # every chunk of (0, 32, 64, 96, 128)
     pair = build_pair(w, oracle_requests=reqs)
     assert pair.lib.info["n_chunks"] > 1
     attend = {(r, j) for r in reqs for j in (0, 3, 7)}
+    assert pair.lib.info["n_chunks"] == 4
     for g in range(w.n_groups):
         si = make_step_inputs(w, g, 0, pair.hist_len)
         res = pair.orc.verify_step(g, si.topk, si.causal_pos, si.queries, si.block_rows,
@@ -598,4 +599,191 @@ def test_compressed_source_rounds():
     with pytest.raises(KVHierError) as ei:                      # only before the group's first step
         pair.lib.set_compression(1, 2)
     assert ei.value.code == -4
+    pair.lib.close()
+
+
+@pytest.mark.parametrize("layout", ["tiny", "mla"])
+def test_repeated_entries_within_a_list(layout):
+    """Reading R2: a row selected twice by one query is two terms of its
+    softmax (eq. 12 gives every entry a location), while the union holds it
+    once and the host fetch copies it once.  Repeats are planted in the
+    generated lists (the generator draws distinct entries): within a query,
+    across the two halves of one list and at both ends."""
+    w = _tiny(n_req=2) if layout == "tiny" else _mla_small(n_groups=1, n_req=3)
+    pair = build_pair(w)
+    si = make_step_inputs(w, 0, 0, pair.hist_len)
+    rng = np.random.default_rng(7)
+    planted = 0
+    for r in range(w.n_req):
+        for j in range(int(si.k_active[r])):
+            lst = si.topk[r, j]
+            valid = np.flatnonzero((lst >= 0) & (lst < int(pair.hist_len[r])))
+            src = rng.choice(valid, size=min(12, valid.size // 2), replace=False)
+            dst = rng.choice(np.setdiff1d(np.arange(w.topk), src), size=src.size, replace=False)
+            lst[dst] = lst[src]
+            lst[-1] = lst[0] if lst[0] >= 0 else lst[-1]
+            planted += src.size
+    assert planted > 0
+    res = pair.orc.verify_step(0, si.topk, si.causal_pos, si.queries, si.block_rows, n_threads=8)
+    out = run_lib_step(pair, 0, si)
+    compare_step(pair, 0, si, res, out)
+    compare_counts(pair, 0, res)
+    for r in range(w.n_req):
+        L = pair.lib.last_lists(0, r)
+        assert len(set(L["union_rows"].tolist())) == L["n_union"]        # the union holds each row once
+        assert len(set(L["miss_rows"].tolist())) == L["n_miss"]          # each missing row fetched once
+        _exact_vs_topk(pair, 0, r, si.topk[r])
+    pair.lib.close()
+
+
+def test_request_with_no_history():
+    """A request whose committed history is empty (n_r = 0, a fresh request
+    before any commit): every list entry is a pad or invalid (R1: valid iff
+    0 <= e < n_r), its union is empty, nothing is fetched or evicted, and its
+    queries attend over their ring window only (this step's block rows).  The
+    other requests of the step are unaffected."""
+    w = _mla_small(n_groups=1, n_req=4, var_k=False, n_prefix=0, prefix_len=0)
+    from workloads.gen import make_hist_len
+    hl = make_hist_len(w)
+    hl[1] = 0
+    pair = build_pair(w, hist_len=hl)
+    si = make_step_inputs(w, 0, 0, hl)                 # request 1: nothing to draw from, p_j = j
+    assert (si.causal_pos[1] == np.arange(w.q_max)).all()
+    rng = np.random.default_rng(3)
+    si.topk[1] = rng.integers(-1, 40, size=si.topk[1].shape).astype(np.int32)   # pads and invalid entries
+    res = pair.orc.verify_step(0, si.topk, si.causal_pos, si.queries, si.block_rows, n_threads=8)
+    assert res.req[1].union == [] and res.req[1].miss == []
+    out = run_lib_step(pair, 0, si)
+    compare_step(pair, 0, si, res, out)
+    compare_counts(pair, 0, res)
+    L = pair.lib.last_lists(0, 1)
+    assert L["n_union"] == 0 and L["n_miss"] == 0 and (L["loc"] == -1).all()
+    pair.lib.close()
+
+
+def test_failed_launch_latches_the_handle():
+    """A HIP error after a step has started its device work leaves the handle
+    latched: that call returns KV_EHIP, every later call that changes state or
+    enqueues work returns KV_ESTATE naming the first failure, reads still
+    work.  The failure is forced from the host (the attention launch reports an
+    error without launching anything), so no kernel faults."""
+    import torch
+    from hierarchical_sparse_kv_verify_amd import KV_FLAG_TEST_FAIL_ATTN, KVHierError
+    from tests.pair import to_device
+    w = _tiny(n_req=2)
+    pair = build_pair(w)
+    lib = pair.lib
+    si = make_step_inputs(w, 0, 0, pair.hist_len)
+    d = to_device(si)
+    out = torch.zeros((w.n_req, w.q_max, w.n_heads, w.d_v), dtype=torch.int16, device="cuda")
+    res = pair.orc.verify_step(0, si.topk, si.causal_pos, si.queries, si.block_rows)
+    lib.verify_step(0, d["queries"], d["topk"], d["causal"], d["ring"], out)
+    torch.cuda.synchronize()
+    compare_step(pair, 0, si, res, out.cpu().numpy().view(np.uint16))
+    lib.set_flags(KV_FLAG_TEST_FAIL_ATTN)
+    with pytest.raises(KVHierError) as ei:
+        lib.verify_step(0, d["queries"], d["topk"], d["causal"], d["ring"], out)
+    assert ei.value.code == -3, str(ei.value)
+    lib.set_flags(0)
+    later = [
+        lambda: lib.verify_step(0, d["queries"], d["topk"], d["causal"], d["ring"], out),
+        lambda: lib.commit(np.zeros(w.n_req, np.int32)),
+        lambda: lib.set_hot(0, 0, [1], [0]),
+        lambda: lib.save_cache(0),
+        lambda: lib.set_hist_len(pair.hist_len),
+    ]
+    for call in later:
+        with pytest.raises(KVHierError) as ei:
+            call()
+        assert ei.value.code == -4 and "unusable" in str(ei.value), str(ei.value)
+    lib.sync()
+    _, last = lib.stats(0)                     # reads still work
+    assert last["calls"] >= 1
+    assert lib.hist_len().tolist() == pair.hist_len.tolist()
+    lib.close()
+
+
+def test_reuse_on_another_stream_without_host_sync():
+    """A Reuse layer issued on a second caller stream right after the selecting
+    step (no host synchronisation in between) reads that step's ring rows,
+    staged rows and locations: the library orders it after the step.  Two
+    rounds with commits; outputs match the oracle."""
+    import torch
+    from tests.pair import to_device
+    w = _mla_small(n_groups=1, n_req=4, var_k=False)
+    pair = build_pair(w, lib_kw=dict(n_chunks=2))
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    n = pair.hist_len.copy()
+    for step in range(2):
+        si = make_step_inputs(w, 0, step, n)
+        q2 = make_step_inputs(w, 0, 100 + step, n).queries
+        with torch.cuda.stream(s1):
+            d = to_device(si)
+            out1 = torch.zeros((w.n_req, w.q_max, w.n_heads, w.d_v), dtype=torch.int16, device="cuda")
+        with torch.cuda.stream(s2):
+            dq2 = torch.from_numpy(np.ascontiguousarray(q2.view(np.int16))).cuda()
+            dc2 = torch.from_numpy(np.ascontiguousarray(si.causal_pos)).cuda()
+            out2 = torch.zeros_like(out1)
+        torch.cuda.synchronize()
+        pair.lib.verify_step(0, d["queries"], d["topk"], d["causal"], d["ring"], out1, stream=s1)
+        pair.lib.verify_reuse(0, dq2, dc2, out2, stream=s2)
+        torch.cuda.synchronize()
+        res = pair.orc.verify_step(0, si.topk, si.causal_pos, si.queries, si.block_rows, n_threads=8)
+        compare_step(pair, 0, si, res, out1.cpu().numpy().view(np.uint16))
+        ref2 = pair.orc.verify_reuse(0, q2, n_threads=8)
+        got2 = out2.cpu().numpy().view(np.uint16)
+        for (r, j), v in ref2.items():
+            assert_close(got2[r, j], v, "reuse r=%d j=%d" % (r, j))
+        acc = make_accepted(w, step, si.k_active)
+        pair.orc.commit(acc)
+        pair.lib.commit(acc, stream=s1)
+        n = n + 1 + acc
+    pair.lib.close()
+
+
+def test_follower_sets_over_rounds_without_host_sync():
+    """Plan-sharing sets (two sets of two layers) over four rounds with
+    commits, every call issued without host synchronisation and the two layers
+    of each set on two different caller streams: the leader's next plan waits
+    for the follower's previous readers, so the final slot tables of every
+    layer and every round's outputs match the oracle."""
+    import torch
+    from tests.pair import to_device
+    w = _mla_small(n_groups=4, plan_share=2, n_arenas=2, var_k=True)
+    pair = build_pair(w)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    n = pair.hist_len.copy()
+    rounds = []
+    for step in range(4):
+        sis, outs = [], []
+        for g in range(w.n_groups):
+            si = make_step_inputs(w, g, step, n)
+            s = streams[g % 2]
+            with torch.cuda.stream(s):
+                d = to_device(si)
+                out = torch.zeros((w.n_req, w.q_max, w.n_heads, w.d_v), dtype=torch.int16, device="cuda")
+            # the inputs were copied on the stream the step is issued on
+            pair.lib.verify_step(g, d["queries"], d["topk"], d["causal"], d["ring"], out, stream=s)
+            sis.append((si, d))
+            outs.append(out)
+        acc = make_accepted(w, step, sis[0][0].k_active)
+        pair.lib.commit(acc, stream=streams[0])
+        rounds.append((sis, outs, acc))
+        n = n + 1 + acc
+    torch.cuda.synchronize()
+    for step, (sis, outs, acc) in enumerate(rounds):
+        for g in range(w.n_groups):
+            si = sis[g][0]
+            res = pair.orc.verify_step(g, si.topk, si.causal_pos, si.queries, si.block_rows, n_threads=8)
+            got = outs[g].cpu().numpy().view(np.uint16)
+            for (r, j), ref in res.out.items():
+                assert_close(got[r, j], ref, "round %d group %d r=%d j=%d" % (step, g, r, j))
+        pair.orc.commit(acc)
+    for g in range(w.n_groups):
+        for r in range(w.n_req):
+            rows, lu = pair.lib.slot_table(g, r)
+            orows, olu = pair.orc.slot_table(g, r)
+            np.testing.assert_array_equal(rows, orows, err_msg="slot rows g=%d r=%d" % (g, r))
+            np.testing.assert_array_equal(lu, olu, err_msg="slot stamps g=%d r=%d" % (g, r))
+    assert pair.lib.hist_len().tolist() == n.tolist()
     pair.lib.close()
