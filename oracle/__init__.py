@@ -7,7 +7,6 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 from .model import (  # noqa: F401
     CLS_HOT, CLS_MISS, CLS_RESIDENT, CLS_TAIL, HOT, RESIDENT, RING, STAGED,
     HierOracle, OracleConfig, StepResult, completed_rows, loc_code, ring_addr, ring_rows, staging_bytes,
-    to_bf16_bits,
 )
 from .residency import OptResidency  # noqa: F401
 from . import native  # noqa: F401

@@ -24,37 +24,47 @@ Hierarchy" (arXiv 2610.13708), referred to below as "the paper":
 Everything is plain Python containers (sets, dicts, sorted lists) walked in
 the paper's order; attention is the C reference in ``attn_ref.c``.
 
-Readings where the pages leave a step open (each marked READING below):
+Readings where the pages leave a step open.  One numbering R1-R26 covers
+every reading of this build; the ones the oracle follows are listed here and
+in ``residency.py`` (R17-R21, dynamic residency):
   R1 a list entry e of query j is a valid history selection iff 0 <= e < n_r
      (n_r = causal position of the anchor); -1 is a pad; anything else is
      counted invalid and skipped.  Rows of the current block reach attention
      through the ring branch, not through the list.
-  R2 the ring is a separate local branch joined in one softmax: query j also
+  R2 Attn of eq. (1) is per-head scaled dot-product softmax; every list entry
+     is one term (a repeated entry counts twice: eq. 12 gives every entry a
+     location).
+  R3 absorbed-MLA rows of 576 elements: K = all 576, V = the first 512;
+     256-element rows: K = row[0:128], V = row[128:256].
+  R4 the ring is a separate local branch joined in one softmax: query j also
      attends positions max(ring_lo, p_j - W + 1) .. p_j of its ring (and, with
      ring_block_only, only those >= n_r); no positional dedup against the list.
-  R3 a row that is both resident and in the hot cache resolves as resident
+  R5 a row that is both resident and in the hot cache resolves as resident
      (probe order of Figure 2).
-  R4 LRU: per-step timestamps; hits are stamped with the step counter t;
-     victims are slots whose row is not in U_r, ordered by (last_used, slot)
-     with empty slots first; the i-th missing row (ascending) takes the i-th
-     victim; missing rows beyond the victims overflow (staged only).
-  R5 staging order: missing rows ascending, dense, in the request's segment
+  R6 LRU: per-step timestamps; the step counter of a group starts above every
+     age given to set_hot; hits are stamped with the step counter t; victims
+     are slots whose row is not in U_r, ordered by (last_used, slot) with
+     empty slots first.
+  R7 the i-th missing row (ascending) takes the i-th victim; missing rows
+     beyond the victims overflow (staged only).
+  R8 staging order: missing rows ascending, dense, in the request's segment
      of K_max*k rows of the arena.
-  R6 location codes: tier in bits 30..29 (0 hot slot r*B+slot, 1 staged
-     r*K_max*k+i, 2 resident pool index), index in bits 28..0, -1 for pads and
-     invalid entries; every valid code is a non-negative int32.
-  R7 resident pool indices are handed out per layer group in call order of
+  R9 location codes: tier in bits 30..29 (0 hot slot r*B+slot, 1 staged
+     r*K_max*k+i, 2 resident pool index, 3 ring row r*R_d + (u mod R_d) of a
+     tail row, R24), index in bits 28..0, -1 for pads and invalid entries;
+     every valid code is a non-negative int32.
+  R10 resident pool indices are handed out per layer group in call order of
      set_resident, ascending row order within a call.
-  R8 the step counter of a group starts above every age given to set_hot.
-  R9 the tail (Figure 2 callout 1; §3.1 "mutable tail"; Figure 3 callout 4):
+  R24 the tail (Figure 2 callout 1; §3.1 "mutable tail"; Figure 3 callout 4):
      a selected history row still held by the request's ring resolves there
      directly, before the optional map and the hot cache.  The ring holds
      position u while u >= ring_lo and u >= n_r + K_max - R_d (slots of
      older positions may already carry this step's new rows, eq. 10);
      location tier 3, index r*R_d + (u mod R_d).  Tail rows are never
      inserted in the hot cache.
+  R26 compressed sources, below.
 
-Compressed sources (§3.3 eq. 8): a group whose stored rows each pack m
+Compressed sources (§3.3 eq. 8, R26): a group whose stored rows each pack m
 consecutive token positions.  Its history rows are source rows; a list entry
 s is valid iff 0 <= s < floor(n_r / m) (complete rows only: the incomplete
 group stays in the tail as positions, reached by the ring branch); a commit
@@ -77,7 +87,7 @@ import numpy as np
 
 from . import native
 
-HOT, STAGED, RESIDENT, RING = 0, 1, 2, 3  # tiers of a location code (R6)
+HOT, STAGED, RESIDENT, RING = 0, 1, 2, 3  # tiers of a location code (R9)
 CLS_RESIDENT, CLS_HOT, CLS_MISS, CLS_TAIL = 0, 1, 2, 3  # class of a union row
 
 
@@ -204,7 +214,7 @@ class HierOracle:
                 or any(x < -1 for x in rows) or any(a < 0 for a in ages):
             raise ValueError("bad hot set")
         if ages:
-            self.t[g] = max(self.t[g], max(ages))          # R8 (every request counts)
+            self.t[g] = max(self.t[g], max(ages))          # R6 (every request counts)
         if r not in self.st[g]:
             return                                        # request not modelled here
         st = self.st[g][r]
@@ -217,13 +227,13 @@ class HierOracle:
         rows = [s for s in range(min(bm.size, self.n[r])) if bm[s]]
         if self.opt is not None:
             raise RuntimeError("static resident sets and dynamic residency do not mix")
-        if r not in self.st[g]:                           # not modelled: only the cursor moves (R7)
+        if r not in self.st[g]:                           # not modelled: only the cursor moves (R10)
             self.res_cursor[g] += len(rows)
             return
         st = self.st[g][r]
         if st.resident_set:
             raise RuntimeError("resident set already given for this request and group")
-        for s in rows:                                    # R7
+        for s in rows:                                    # R10
             st.res_idx[s] = self.res_cursor[g]
             self.res_cursor[g] += 1
         st.resident_set = True
@@ -273,7 +283,7 @@ class HierOracle:
 
     def window(self, g: int, r: int, n_r: int, p_j: int) -> range:
         st = self.st[g][r]
-        lo = max(st.ring_lo, p_j - self.cfg.ring_window + 1, 0)   # R2
+        lo = max(st.ring_lo, p_j - self.cfg.ring_window + 1, 0)   # R4
         if self.cfg.ring_block_only:
             lo = max(lo, n_r)
         return range(lo, p_j + 1)
@@ -319,10 +329,10 @@ class HierOracle:
                         n_bad += 1
             U = sorted(valid)
 
-            # Figure 2 / §3.2: (1) direct map, (2) hot cache, (3) host; R3
+            # Figure 2 / §3.2: (1) direct map, (2) hot cache, (3) host; R5
             cls = {}
             res_at = {}
-            tail_lo = max(st.ring_lo, n_r + Q - self.r_d) if m == 1 else n_r   # R9
+            tail_lo = max(st.ring_lo, n_r + Q - self.r_d) if m == 1 else n_r   # R24
             for u in U:
                 ri = self._resident(g, r, u)
                 if u >= tail_lo:
@@ -337,9 +347,9 @@ class HierOracle:
                 else:
                     cls[u] = CLS_MISS
             D = [u for u in U if cls[u] == CLS_MISS]          # eq. (6): D_r = U_r \ R_r
-            stage = {u: i for i, u in enumerate(D)}          # R5
+            stage = {u: i for i, u in enumerate(D)}          # R8
 
-            # §3.5 eq. (12): one location per list entry, in selection order (R6)
+            # §3.5 eq. (12): one location per list entry, in selection order (R9)
             seg = r * Q * k
             loc = np.full((Q, k), -1, dtype=np.int32)
             sel_cls = [0, 0, 0, 0]
@@ -359,7 +369,7 @@ class HierOracle:
                     else:
                         loc[j, i] = loc_code(STAGED, seg + stage[e])
 
-            # §2.2: hits refresh recency, selected rows are protected, LRU victims (R4)
+            # §2.2: hits refresh recency, selected rows are protected, LRU victims (R6, R7)
             in_u = set(U)
             for u in U:
                 if cls[u] == CLS_HOT:
@@ -407,7 +417,7 @@ class HierOracle:
 
     def _attend(self, g, topk, causal_pos, queries, res, attend, n_threads):
         """Eq. (1) over each query's own list (read from the original rows,
-        eqs. 11-12) plus its ring window (R2)."""
+        eqs. 11-12) plus its ring window (R4)."""
         cfg = self.cfg
         pairs = []
         for r in self.requests:
@@ -485,9 +495,3 @@ class HierOracle:
         st = self.st[g][r]
         return np.array(st.slot_row, dtype=np.int32), np.array(st.slot_lu, dtype=np.int32)
 
-
-def to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """double -> bf16 bit pattern by round-to-nearest-even of the float32 value."""
-    f = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    r = (f + np.uint32(0x7FFF) + ((f >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
-    return r.astype(np.uint16)

@@ -23,25 +23,29 @@ Hierarchy" (arXiv 2610.13708):
     capacity.
   - Figure 2 / §3.2: resolution consults the ready optional map first.
 
-Readings where the pages leave a step open (numbered after the readings of
-``model.py``):
-  R9  the pool holds M pages of P rows; an admitted request's required
+Readings where the pages leave a step open (one numbering R1-R26 covers
+every reading of this build; R1-R10, R24 and R26 are in ``model.py``):
+  R17 the pool holds M pages of P rows; an admitted request's required
       allocations (hot cache, tail, staging) are charged against M in pages
       but occupy no pool page; optional pages occupy pool pages.  Eq. (3)
       is the invariant  sum(required) + sum(held) + reserve <= M.
-  R10 the reclaim order is the caller's policy and is passed with the
-      admission; reclaiming a request drops all of its optional pages (pending
-      or ready) and leaves it admitted and eligible for later repopulation.
-  R11 one population attempt visits request slots cyclically from a cursor
+  R18 eligible pages of a request are floor(n_r / P) for its frontier n_r
+      at admission (complete pages of the imported history).
+  R19 a_r of eq. (4) counts every page the request holds, pending or ready;
+      the reclaim order is the caller's policy and is passed with the
+      admission; reclaiming a request drops all of its optional pages
+      (pending or ready) and leaves it admitted and eligible for later
+      repopulation; if the whole order cannot cover the deficit the admission
+      waits and nothing changes.
+  R20 one population attempt visits request slots cyclically from a cursor
       that persists between attempts; a visit to an admitted request that
       holds fewer than its eligible pages assigns its lowest page index not
       held to the lowest free pool page; the attempt ends after max_pages
       assignments, when the budget M - sum(required) - reserve - sum(held) is
       used up, or after a whole cycle with no assignment; the cursor then
       points past the last visited slot.
-  R12 eligible pages of a request are floor(n_r / P) for its frontier n_r
-      at admission.
-  R13 a_r of eq. (4) counts every page the request holds, pending or ready.
+  R21 a page becomes ready (visible to resolution) only when it is published
+      after its copy has completed.
 """
 from __future__ import annotations
 
@@ -110,7 +114,7 @@ class OptResidency:
             self._drop(x)
         self.admitted[r] = True
         self.required[r] = required_pages
-        self.eligible[r] = max(0, n_r) // self.P  # R12
+        self.eligible[r] = max(0, n_r) // self.P  # R18
         return taken
 
     def complete(self, r: int):
@@ -123,7 +127,7 @@ class OptResidency:
         self.eligible[r] = 0
 
     def populate(self, max_pages: int) -> List[Tuple[int, int, int]]:
-        """One bounded round-robin attempt (R11).  Returns the new pending
+        """One bounded round-robin attempt (R20).  Returns the new pending
         pages as (request, page index, pool page), in assignment order."""
         if max_pages < 0:
             raise ValueError("negative page bound")
