@@ -64,5 +64,48 @@ def build(force: bool = True, verbose: bool = False) -> str:
     return LIB
 
 
+SAN_DIR = os.path.join(OBJDIR, "san")
+SAN_LIB = os.path.join(SAN_DIR, "libkvhier.so")
+# host-side sanitizers only: each flag applies to the host compilation of the
+# HIP sources (device code is built as usual)
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build_sanitized() -> str:
+    """libkvhier.so with AddressSanitizer and UBSan in its host code, for the
+    CPU-reachable paths (argument checks, failed creation, null handles); run
+    it with the clang sanitizer runtime preloaded.  Returns its path."""
+    os.makedirs(SAN_DIR, exist_ok=True)
+
+    def comp(src):
+        obj = os.path.join(SAN_DIR, os.path.splitext(src)[0] + ".o")
+        cmd = [_hipcc(), *HIPCC_FLAGS, *SAN_FLAGS, "-g", "-I", INCLUDE, "-I", CSRC, "-c",
+               os.path.join(CSRC, src), "-o", obj]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("compile of %s failed:\n%s\n%s" % (src, " ".join(cmd), res.stderr))
+        return obj
+
+    with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
+        objs = list(ex.map(comp, SOURCES))
+    cmd = [_hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, *SAN_FLAGS, "-shared-libsan", *objs,
+           "-o", SAN_LIB]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), res.stderr))
+    return SAN_LIB
+
+
+def sanitizer_runtime() -> str:
+    """The clang AddressSanitizer runtime the sanitized build links against."""
+    res = subprocess.run([_hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True,
+                         text=True)
+    path = res.stdout.strip()
+    if not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("clang sanitizer runtime not found (%r)" % path)
+    return path
+
+
 if __name__ == "__main__":
     build(force="--no-force" not in sys.argv, verbose=True)

@@ -13,17 +13,34 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "attn_ref.c")
-_LIB = os.path.join(_HERE, "liboracle_attn.so")
+# ORACLE_ATTN_LIBRARY names a prebuilt copy instead (the sanitizer run builds
+# one with AddressSanitizer and UBSan and runs the oracle's pins on it)
+_LIB = os.environ.get("ORACLE_ATTN_LIBRARY") or os.path.join(_HERE, "liboracle_attn.so")
+_SAN_LIB = os.path.join(_HERE, "_san", "liboracle_attn.so")
 _lib = None
 
 
 def build(force: bool = False) -> str:
+    if os.environ.get("ORACLE_ATTN_LIBRARY"):
+        return _LIB
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
                                "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
+
+
+def build_sanitized() -> str:
+    """The same C reference built with AddressSanitizer and UBSan (host only),
+    for a run of the oracle's pins under the gcc sanitizer runtime."""
+    os.makedirs(os.path.dirname(_SAN_LIB), exist_ok=True)
+    tmp = _SAN_LIB + ".tmp%d" % os.getpid()
+    subprocess.check_call(["gcc", "-O1", "-g", "-std=c11", "-fPIC", "-shared", "-pthread",
+                           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+                           "-fno-omit-frame-pointer", "-o", tmp, _SRC, "-lm"])
+    os.replace(tmp, _SAN_LIB)
+    return _SAN_LIB
 
 
 def lib():
