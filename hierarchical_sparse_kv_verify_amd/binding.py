@@ -36,7 +36,7 @@ EXPORTED = [
     "kv_hier_last_lists", "kv_hier_slot_table", "kv_hier_read_rows", "kv_hier_sync",
     "kv_hier_set_flags", "kv_hier_cache_snapshot", "kv_hier_opt_admit", "kv_hier_opt_complete",
     "kv_hier_opt_populate", "kv_hier_opt_publish", "kv_hier_opt_query", "kv_hier_verify_reuse",
-    "kv_hier_set_compression", "kv_hier_commit_src",
+    "kv_hier_set_compression", "kv_hier_commit_src", "kv_hier_verify_step_static",
 ]
 
 
@@ -144,6 +144,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "kv_hier_clear_resident": ([vp, i32], i32),
         "kv_hier_ring_load": ([vp, i32, i32, ctypes.c_int32, vp, i32], i32),
         "kv_hier_verify_step": ([vp, i32, vp, vp, vp, vp, vp, vp], i32),
+        "kv_hier_verify_step_static": ([vp, i32, vp, vp, vp, vp, vp, vp], i32),
         "kv_hier_verify_reuse": ([vp, i32, vp, vp, vp, vp], i32),
         "kv_hier_commit": ([vp, vp, vp], i32),
         "kv_hier_commit_src": ([vp, vp, vp, vp], i32),
@@ -291,6 +292,14 @@ class KVHier:
         """ring_rows None: a Reindex consumer of a shared source (the ring already
         holds this step's rows); topk_idx None only for a follower layer."""
         self._check(self._lib.kv_hier_verify_step(
+            self._h, g, _dev_ptr(queries), None if topk_idx is None else _dev_ptr(topk_idx),
+            _dev_ptr(causal_pos), None if ring_rows is None else _dev_ptr(ring_rows), _dev_ptr(out),
+            _stream_handle(stream)))
+
+    def verify_step_static(self, g: int, queries, topk_idx, causal_pos, ring_rows, out, stream=None):
+        """kv_hier_verify_step_static: the same step, allocating nothing during
+        the call (split-key partials in the library's static device array)."""
+        self._check(self._lib.kv_hier_verify_step_static(
             self._h, g, _dev_ptr(queries), None if topk_idx is None else _dev_ptr(topk_idx),
             _dev_ptr(causal_pos), None if ring_rows is None else _dev_ptr(ring_rows), _dev_ptr(out),
             _stream_handle(stream)))

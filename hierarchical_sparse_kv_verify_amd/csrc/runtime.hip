@@ -32,6 +32,7 @@
 #include <cstdio>
 #include <cstring>
 #include <deque>
+#include <mutex>
 #include <set>
 #include <string>
 #include <new>
@@ -45,6 +46,37 @@ using namespace kvh;
 namespace {
 
 constexpr int kCommitBufs = 4;
+
+// Scratch of kv_hier_verify_step_static: the split-key partial numerators and
+// (max, sum) pairs of its attention launches, in a file-scope device array
+// instead of memory the handle allocated, for callers that cannot allocate.
+// Every GPU the library runs on holds its own copy until the process ends; in
+// host code the array's name is not a device address, so every use goes
+// through the address hipGetSymbolAddress returns on that device
+// (scratch_on_device).
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+// Device address of `scratch` on the current device, looked up once per device
+// (at handle creation) and kept; nullptr on failure.
+unsigned char* scratch_on_device(int device, hipError_t* err) {
+  static std::mutex mu;
+  static std::vector<unsigned char*> addr;
+  std::lock_guard<std::mutex> lock(mu);
+  *err = hipSuccess;
+  if (device < 0) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  if (size_t(device) >= addr.size()) addr.resize(size_t(device) + 1, nullptr);
+  if (!addr[device]) {
+    void* p = nullptr;
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess) return nullptr;
+    addr[device] = static_cast<unsigned char*>(p);
+  }
+  return addr[device];
+}
 
 enum TimedKind { K_RING = 0, K_PLAN, K_GATHER, K_ATTN, K_COMBINE, K_PROMOTE, K_VICTIMS, K_NUM };
 
@@ -142,6 +174,9 @@ struct kv_hier {
   float* part_o = nullptr;
   uint16_t* zero_row = nullptr;   // one all-zero row: target of masked attention reads
   float* part_ml = nullptr;
+  size_t step_part_blocks = 0;      // split-key partial blocks of the largest chunk launch of a step
+  unsigned char* scratch_dev = nullptr;   // this device's copy of the static scratch array
+  bool no_alloc_call = false;       // inside kv_hier_verify_step_static: take no events, allocate nothing
   int splits = 1, head_groups = 1, n_chunks = 1;   // splits: the largest of chunk_splits
   int all_splits = 1;               // key splits of one launch over every request (Reuse layers)
   std::vector<int> chunk_lo, chunk_splits;
@@ -278,6 +313,7 @@ hipEvent_t take_event(kv_hier* h) {
 
 // Records a start event when timing is on; returns the pending index or -1.
 int time_begin(kv_hier* h, int kind, int g, hipStream_t s) {
+  if (h->no_alloc_call) return -1;   // the pool may have to create events
   const bool on = (h->cfg.flags & KV_FLAG_TIMING) ||
                   ((h->cfg.flags & KV_FLAG_TIMING_ATTN) && (kind == K_ATTN || kind == K_COMBINE));
   if (!on) return -1;
@@ -711,6 +747,11 @@ static int create_impl(kv_hier* h) {
   // per device: every handle sets it on its own)
   HIPCHK(h, plan_init_attributes());
   HIPCHK(h, attn_init_attributes());
+  {
+    hipError_t e = hipSuccess;
+    h->scratch_dev = scratch_on_device(h->device, &e);
+    if (!h->scratch_dev) return fail(h, KV_EHIP, "static scratch address: %s", hipGetErrorString(e));
+  }
   // request chunks for the fetch/attention pipeline
   // Automatic layout for N >= 64: four quarters, the last one halved when each
   // half still fills the GPU with attention workgroups (N/8 x Q x head groups
@@ -746,6 +787,7 @@ static int create_impl(kv_hier* h) {
       h->splits = std::max(h->splits, s);
       if (s > 1) blocks = std::max(blocks, size_t(wgs) * s);
     }
+    h->step_part_blocks = blocks;
     {
       // a Reuse layer has no fetch to overlap: one launch over every request
       const int64_t wgs = int64_t(N) * c.q_max * h->head_groups;
@@ -1237,7 +1279,7 @@ static int verify_step_impl(kv_hier_t* h, int g, const void* queries, const int3
       if (h->grp[g + m].done_recorded) HIPCHK(h, hipStreamWaitEvent(h->side, h->grp[g + m].ev_done, 0));
     // optional-history pages whose copies have completed become ready for
     // this step's resolution (the first group's step is the step boundary)
-    if (g == 0 && h->opt.on && (rc = opt_publish_impl(h, false))) return rc;
+    if (g == 0 && h->opt.on && !h->no_alloc_call && (rc = opt_publish_impl(h, false))) return rc;
 
     PlanArgs pa;
     pa.topk = topk_idx;
@@ -1324,6 +1366,11 @@ static int verify_step_impl(kv_hier_t* h, int g, const void* queries, const int3
   at.out = static_cast<uint16_t*>(out);
   at.part_o = h->part_o;
   at.part_ml = h->part_ml;
+  if (h->no_alloc_call) {
+    // the same partials, in this device's static scratch (size checked before any work)
+    at.part_o = reinterpret_cast<float*>(h->scratch_dev);
+    at.part_ml = at.part_o + h->step_part_blocks * size_t(attn_heads_per_wg(c.n_heads)) * c.d_v;
+  }
   at.N = N;
   at.Q = c.q_max;
   at.k = c.topk;
@@ -1380,6 +1427,23 @@ int kv_hier_verify_step(kv_hier_t* h, int g, const void* queries, const int32_t*
   DeviceGuard dg(h);
   if (int rc = refuse_if_broken(h)) return rc;
   return finish(h, verify_step_impl(h, g, queries, topk_idx, causal_pos, ring_rows, out, stream));
+}
+
+int kv_hier_verify_step_static(kv_hier_t* h, int g, const void* queries, const int32_t* topk_idx,
+                               const int32_t* causal_pos, const void* ring_rows, void* out, void* stream) {
+  DeviceGuard dg(h);
+  if (!h) return KV_EINVAL;
+  if (int rc = refuse_if_broken(h)) return rc;
+  const size_t need = h->step_part_blocks * size_t(attn_heads_per_wg(h->cfg.n_heads)) *
+                      (size_t(h->cfg.d_v) + 2) * sizeof(float);
+  if (need > kStaticScratchBytes)
+    return fail(h, KV_EINVAL,
+                "split-key partials of this handle's steps take %zu bytes, over the %zu-byte static scratch", need,
+                kStaticScratchBytes);
+  h->no_alloc_call = true;
+  const int rc = finish(h, verify_step_impl(h, g, queries, topk_idx, causal_pos, ring_rows, out, stream));
+  h->no_alloc_call = false;
+  return rc;
 }
 
 static int verify_reuse_impl(kv_hier_t* h, int g, const void* queries, const int32_t* causal_pos, void* out,

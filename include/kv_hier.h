@@ -290,6 +290,22 @@ int kv_hier_verify_step(kv_hier_t *h, int g, const void *queries, const int32_t 
                         const int32_t *causal_pos, const void *ring_rows, void *out,
                         void *stream);
 
+/* kv_hier_verify_step for callers that cannot allocate device memory during
+ * a call (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same step, same arguments and same results, but the
+ * attention's split-key partials live in a file-scope device array of the
+ * library (32 MiB, one copy per GPU, held until the process ends) instead of
+ * the handle's buffer, and the call allocates nothing: no device or host
+ * memory, no events (KV_FLAG_TIMING and KV_FLAG_TIMING_ATTN are not honoured
+ * here), and optional-history pages are not published here (kv_hier_opt_publish
+ * and kv_hier_verify_step publish them).  The caller still passes every input
+ * and output.  Returns KV_EINVAL, before any device work, when the handle's
+ * split-key partials (blocks x heads per workgroup x (d_v + 2) floats) exceed
+ * the array.  Calls on one handle are ordered by the library; calls of two
+ * handles on one GPU that overlap in time share the array and race. */
+int kv_hier_verify_step_static(kv_hier_t *h, int g, const void *queries, const int32_t *topk_idx,
+                               const int32_t *causal_pos, const void *ring_rows, void *out, void *stream);
+
 /* A Reuse consumer of source g ("Adaptive DHiSparse" §2, §3.2): new queries
  * (device bf16 [N][q_max][n_heads][d_qk]) attend, exactly as in verify_step,
  * over the latest selection of g through its location vector and the payload
