@@ -189,12 +189,14 @@ def test_plan_shared_by_follower_layers():
     pair.lib.close()
 
 
-def test_mla_128_heads_split_keys():
-    """Two head groups of 64 and key splits merged by the combine pass."""
-    w = _mla_small(n_req=2, n_groups=1, n_heads=128, q_max=4, topk=1024, ring_window=64,
+@pytest.mark.parametrize("n_heads,groups", [(128, 2), (256, 4), (96, 2)])
+def test_mla_many_heads_split_keys(n_heads, groups):
+    """Head groups of 64 (the last one partly masked at 96 heads) and key
+    splits merged by the combine pass."""
+    w = _mla_small(n_req=2, n_groups=1, n_heads=n_heads, q_max=4, topk=1024, ring_window=64,
                    n_prefix=2, hot_slots=2048, var_k=False)
     pair = build_pair(w)
-    assert pair.lib.info["attn_head_groups"] == 2 and pair.lib.info["attn_splits"] > 1
+    assert pair.lib.info["attn_head_groups"] == groups and pair.lib.info["attn_splits"] > 1, pair.lib.info
     si = make_step_inputs(w, 0, 0, pair.hist_len)
     res = pair.orc.verify_step(0, si.topk, si.causal_pos, si.queries, si.block_rows, n_threads=8)
     out = run_lib_step(pair, 0, si)
@@ -202,11 +204,12 @@ def test_mla_128_heads_split_keys():
     pair.lib.close()
 
 
-@pytest.mark.parametrize("n_heads", [32, 16])
+@pytest.mark.parametrize("n_heads", [32, 16, 8, 48])
 def test_mla_one_head_block_split_keys(n_heads):
-    """Absorbed-MLA rows with at most 32 heads: one 32-head block per
-    workgroup (four waves, eight rows of every tile per wave), heads past H
-    masked, key splits merged by the combine pass."""
+    """Absorbed-MLA rows with few heads: at most 32 heads take one 32-head
+    block per workgroup (four waves, eight rows of every tile per wave), 48
+    heads two blocks; heads past H masked, key splits merged by the combine
+    pass."""
     w = _mla_small(n_req=2, n_groups=1, n_heads=n_heads, q_max=4, topk=1024, ring_window=64,
                    n_prefix=2, hot_slots=2048, var_k=True)
     pair = build_pair(w)
@@ -238,6 +241,7 @@ def test_mla_short_lists(topk, window):
 @pytest.mark.parametrize("n_req,n_heads,q_max,chunks,splits", [
     (128, 64, 8, [0, 32, 64, 96, 128], 1),            # quarters of one GPU wave each
     (128, 128, 8, [0, 32, 64, 96, 112, 128], 1),      # halves of the last quarter still fill the GPU
+    (256, 64, 8, [0, 64, 128, 192, 224, 256], 1),     # the same with 64 heads and twice the requests
     (64, 64, 4, [0, 16, 32, 48, 64], 4),              # quarters under a wave: key splits (17 tiles)
     (32, 64, 8, [0, 16, 32], 2),                      # fewer than 64 requests: two chunks
 ])
