@@ -185,7 +185,6 @@ struct kv_hier {
   hipStream_t side = nullptr;       // host fetch
   hipStream_t work = nullptr;       // the rest of the step when CUs are partitioned (else null)
   hipStream_t aux = nullptr;        // copy-back of promoted rows
-  std::vector<hipEvent_t> ev_attn;  // per chunk: attention done
   hipEvent_t ev_resolved = nullptr; // LRU victims chosen (the copy-backs follow)
   hipEvent_t ev_in = nullptr, ev_out = nullptr;
   int share = 1;                    // groups per plan-sharing set (leader + followers)
@@ -498,7 +497,6 @@ void free_all(kv_hier* h) {
     if (e) (void)hipEventDestroy(e);
   for (auto& v : h->ev_fetched) for (hipEvent_t e : v) (void)hipEventDestroy(e);
   for (auto& v : h->ev_free) for (hipEvent_t e : v) (void)hipEventDestroy(e);
-  for (hipEvent_t e : h->ev_attn) (void)hipEventDestroy(e);
   if (h->ev_resolved) (void)hipEventDestroy(h->ev_resolved);
   if (h->side) (void)hipStreamDestroy(h->side);
   if (h->aux) (void)hipStreamDestroy(h->aux);
@@ -959,8 +957,6 @@ static int create_impl(kv_hier* h) {
     HIPCHK(h, hipEventCreateWithFlags(&G.ev_sel, hipEventDisableTiming));
   }
   HIPCHK(h, hipEventCreateWithFlags(&h->ev_resolved, hipEventDisableTiming));
-  h->ev_attn.assign(h->n_chunks, nullptr);
-  for (auto& e : h->ev_attn) HIPCHK(h, hipEventCreateWithFlags(&e, hipEventDisableTiming));
   HIPCHK(h, hipEventCreateWithFlags(&h->ev_in, hipEventDisableTiming));
   HIPCHK(h, hipEventCreateWithFlags(&h->ev_out, hipEventDisableTiming));
   HIPCHK(h, hipEventCreateWithFlags(&h->ev_part, hipEventDisableTiming));
@@ -1392,7 +1388,6 @@ static int verify_step_impl(kv_hier_t* h, int g, const void* queries, const int3
     if ((rc = attend(h, g, at, s))) return rc;
     // copy-back on the aux stream once the victims are chosen, concurrent
     // with the attention (victim slots are not read by the step)
-    HIPCHK(h, hipEventRecord(h->ev_attn[ch], s));
     if (ch == 0) {
       HIPCHK(h, hipStreamWaitEvent(h->aux, h->ev_resolved, 0));
       // a follower's counters are its plan's: copy the leader's last-step counts
@@ -1404,7 +1399,17 @@ static int verify_step_impl(kv_hier_t* h, int g, const void* queries, const int3
     HIPCHK(h, launch_promote(reinterpret_cast<const uint4*>(h->arena[a]), P.victims, P.req_info,
                              reinterpret_cast<uint4*>(G.hot), h->QK, c.hot_slots, h->row16, at.r0, at.r1, h->aux));
     time_end(h, ti, h->aux);
-    HIPCHK(h, hipStreamWaitEvent(h->aux, h->ev_attn[ch], 0));
+  }
+  // One event after the group's last attention chunk (an event record costs
+  // the stream a few microseconds, so there is none per chunk): a Reuse of
+  // this selection waits for it, and the arena chunks are released after it
+  // (a later fetch into a chunk then waits for every chunk's readers, which
+  // it does anyway when it belongs to a later step of the caller's stream).
+  HIPCHK(h, hipEventRecord(G.ev_sel, s));
+  G.sel_recorded = true;
+  G.sel_valid = true;
+  HIPCHK(h, hipStreamWaitEvent(h->aux, G.ev_sel, 0));
+  for (int ch = 0; ch < h->n_chunks; ++ch) {
     HIPCHK(h, hipEventRecord(h->ev_free[a][ch], h->aux));
     h->free_recorded[a][ch] = 1;
   }
@@ -1412,9 +1417,6 @@ static int verify_step_impl(kv_hier_t* h, int g, const void* queries, const int3
   // attention waits for this
   HIPCHK(h, hipEventRecord(G.ev_done, h->aux));
   G.done_recorded = true;
-  HIPCHK(h, hipEventRecord(G.ev_sel, s));
-  G.sel_recorded = true;
-  G.sel_valid = true;
   if (h->work) {
     HIPCHK(h, hipEventRecord(h->ev_out, s));
     HIPCHK(h, hipStreamWaitEvent(caller, h->ev_out, 0));
