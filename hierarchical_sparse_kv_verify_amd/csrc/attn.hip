@@ -82,7 +82,12 @@ struct Cfg {
   static constexpr int NDP = 4;              // waves per 32-head block: key / value width split
   static constexpr int NW = NDP * HB;
   static constexpr int NT = NW * 64;
-  static constexpr int KS = D_QK / NDP / 16; // 16-wide k-steps over this wave's key part
+  static constexpr int KST = D_QK / 16;      // 16-wide k-steps over the key width
+  // k-steps of one wave's key part (wave dq takes k-steps dq*KS .. dq*KS+KS-1
+  // that exist: with a key width that is no multiple of 64 the last waves
+  // take fewer, or none)
+  static constexpr int KS = (KST + NDP - 1) / NDP;
+  static constexpr bool KS_EVEN = KST % NDP == 0;
   static constexpr int DVB = D_V / NDP / 32; // 32-dim value blocks of this wave's value part
   static constexpr int RCH = ROW / 8;        // 16-byte chunks per row
   static constexpr int RPW = TILE / NW;      // rows of a tile gathered by one wave
@@ -90,7 +95,8 @@ struct Cfg {
   // instruction per row for chunks 0..63 plus shared ones for the rest
   static constexpr bool WIDE = RCH >= 64;
   static constexpr int REST = WIDE ? RCH - 64 : 0;
-  static constexpr int NU = WIDE ? RPW + (RPW * REST + 63) / 64 : (RPW * RCH) / 64;
+  static constexpr int NU = WIDE ? RPW + (RPW * REST + 63) / 64 : (RPW * RCH + 63) / 64;
+  static constexpr bool GATHER_EXACT = WIDE || (RPW * RCH) % 64 == 0;   // no idle lanes
   // row stride: 36 banks (dwords mod 64) apart
   static constexpr int ROW_DW = ROW / 2;
   static constexpr int KSTR = ROW + 2 * ((36 - ROW_DW % 64 + 64) % 64);
@@ -113,9 +119,9 @@ struct Cfg {
   static constexpr size_t LDS_M = size_t(NW) * 32 * 4;
   static constexpr size_t LDS_C = DMA ? size_t(3) * NW * 64 * 4 : 0;
   static constexpr size_t LDS = LDS_K + LDS_S + LDS_P + LDS_M + LDS_C + 16;
-  static_assert(D_QK % (NDP * 16) == 0 && D_V % (NDP * 32) == 0 && ROW % 8 == 0, "shape");
+  static_assert(D_QK % 16 == 0 && D_V % (NDP * 32) == 0 && ROW % 8 == 0, "shape");
   static_assert(V_OFF % 8 == 0 && V_OFF + D_V <= ROW && D_QK <= ROW, "row layout");
-  static_assert(WIDE ? (REST <= 64 && 64 % REST == 0) : (64 % RCH == 0 && (RPW * RCH) % 64 == 0), "gather");
+  static_assert(WIDE ? (REST <= 64 && 64 % REST == 0) : RCH <= 64, "gather");
   static_assert(LDS <= 160 * 1024, "LDS");
   static_assert(!DMA || (RPW * 8 <= 64 && NVM <= 15), "DMA tile");
 };
@@ -167,10 +173,13 @@ __device__ __forceinline__ void task_of(int u, int lane, int& rr, int& ch, bool&
     rr = st ? x : 0;
     ch = 64 + lane % C::REST;
   } else {
+    // rows whose chunk count does not divide the wave: the last
+    // instruction's idle lanes load a chunk of the wave's first row and store
+    // nothing
     const int x = u * 64 + lane;
-    rr = x / C::RCH;
-    ch = x % C::RCH;
-    st = true;
+    st = C::GATHER_EXACT || x < C::RPW * C::RCH;
+    rr = st ? x / C::RCH : 0;
+    ch = st ? x % C::RCH : 0;
   }
 }
 
@@ -359,11 +368,11 @@ __global__ __launch_bounds__(C::NT, 1) void attn_kernel(AttnArgs a) {
   // Q fragment: B operand of S^T = K Q^T, head = lane%32, 8 dims per k-step
   bf16x8 qreg[C::KS];
   {
-    const uint16_t* qp = a.q + (size_t(qi) * a.H + head) * C::D_QK + dq * (C::D_QK / C::NDP) + hi_half * 8;
+    const uint16_t* qp = a.q + (size_t(qi) * a.H + head) * C::D_QK + dq * (C::KS * 16) + hi_half * 8;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (head < a.H) v = gload16(reinterpret_cast<uintptr_t>(qp + ks * 16));
+      if (head < a.H && (C::KS_EVEN || dq * C::KS + ks < C::KST)) v = gload16(reinterpret_cast<uintptr_t>(qp + ks * 16));
       qreg[ks] = __builtin_bit_cast(bf16x8, v);
     }
   }
@@ -412,7 +421,7 @@ __global__ __launch_bounds__(C::NT, 1) void attn_kernel(AttnArgs a) {
   int koff[C::KS];
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks) {
-    const int c = (dq * (C::D_QK / C::NDP) + ks * 16 + hi_half * 8) / 8;
+    const int c = (dq * (C::KS * 16) + ks * 16 + hi_half * 8) / 8;
     koff[ks] = !C::DMA || c < 64 ? crow * C::RSTR + c * 8
                                  : C::TAILO + crow * 64 + (((c - 64) ^ tail_swz(crow)) * 8);
   }
@@ -450,7 +459,9 @@ __global__ __launch_bounds__(C::NT, 1) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[ks], qreg[ks], acc, 0, 0, 0);
+    for (int ks = 0; ks < C::KS; ++ks)
+      if (C::KS_EVEN || dq * C::KS + ks < C::KST)     // wave-uniform: k-steps past the key width are skipped
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[ks], qreg[ks], acc, 0, 0, 0);
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4)
       sx_own[i4 * 64] = make_float4(acc[4 * i4], acc[4 * i4 + 1], acc[4 * i4 + 2], acc[4 * i4 + 3]);
@@ -719,12 +730,15 @@ hipError_t attn_init_attributes() {
   if (e == hipSuccess) e = set_lds_limit<Cfg<576, 0, 512, 576, 2>>();
   if (e == hipSuccess) e = set_lds_limit<Cfg<128, 128, 128, 256, 1>>();
   if (e == hipSuccess) e = set_lds_limit<Cfg<128, 128, 128, 256, 2>>();
+  if (e == hipSuccess) e = set_lds_limit<Cfg<144, 0, 128, 144, 1>>();
+  if (e == hipSuccess) e = set_lds_limit<Cfg<144, 0, 128, 144, 2>>();
   return e;
 }
 
 bool attn_layout_supported(int row_elems, int d_qk, int v_off, int d_v) {
   return (row_elems == 576 && d_qk == 576 && v_off == 0 && d_v == 512) ||
-         (row_elems == 256 && d_qk == 128 && v_off == 128 && d_v == 128);
+         (row_elems == 256 && d_qk == 128 && v_off == 128 && d_v == 128) ||
+         (row_elems == 144 && d_qk == 144 && v_off == 0 && d_v == 128);
 }
 
 int attn_heads_per_wg(int H) { return H <= 32 ? 32 : 64; }
@@ -738,6 +752,10 @@ hipError_t launch_attn(const AttnArgs& a, int row_elems, int d_qk, int v_off, in
   if (row_elems == 256 && d_qk == 128 && v_off == 128 && d_v == 128) {
     if (hpw == 32) return launch_cfg<Cfg<128, 128, 128, 256, 1>>(a, s);
     return launch_cfg<Cfg<128, 128, 128, 256, 2>>(a, s);
+  }
+  if (row_elems == 144 && d_qk == 144 && v_off == 0 && d_v == 128) {
+    if (hpw == 32) return launch_cfg<Cfg<144, 0, 128, 144, 1>>(a, s);
+    return launch_cfg<Cfg<144, 0, 128, 144, 2>>(a, s);
   }
   return hipErrorInvalidValue;
 }

@@ -106,7 +106,11 @@ typedef struct {
   int32_t row_elems;        /* bf16 elements per row (d_KV = 2*row_elems bytes)          */
   int32_t d_qk;             /* key: K = row[0 : d_qk]                                    */
   int32_t v_off;            /* value: V = row[v_off : v_off + d_v]                       */
-  int32_t d_v;
+  int32_t d_v;              /* layouts with kernels (row_elems, d_qk, v_off, d_v):
+                               (576, 576, 0, 512) absorbed MLA (512 latent + 64 rope);
+                               (144, 144, 0, 128) the 288-B rows of Table 3
+                               (128 latent + 16 rope); (256, 128, 128, 128) K || V.
+                               Others: KV_EUNSUPPORTED                                   */
   int32_t n_heads;          /* query heads sharing each row                              */
   int32_t q_max;            /* K_max verification queries per request (<= 32)           */
   int32_t topk;             /* k >= 1 selections per query (a query with nothing selected

@@ -35,7 +35,10 @@ in ``residency.py`` (R17-R21, dynamic residency):
      is one term (a repeated entry counts twice: eq. 12 gives every entry a
      location).
   R3 absorbed-MLA rows of 576 elements: K = all 576, V = the first 512;
-     256-element rows: K = row[0:128], V = row[128:256].
+     256-element rows: K = row[0:128], V = row[128:256].  (R27: the 288-B
+     rows of Table 3 are 144 elements, K = all 144, V = the first 128; the
+     attention here reads K = row[0:d_qk], V = row[v_off:v_off+d_v] for any
+     layout the configuration names.)
   R4 the ring is a separate local branch joined in one softmax: query j also
      attends positions max(ring_lo, p_j - W + 1) .. p_j of its ring (and, with
      ring_block_only, only those >= n_r); no positional dedup against the list.

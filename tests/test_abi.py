@@ -55,6 +55,7 @@ def _cfg(**kw):
     (dict(q_max=32, topk=2047), -5),                        # 65,504 codes: over the plan's LDS
     (dict(q_max=32, topk=1272), -5),                        # 40,704 codes: just over it at B = 128
     (dict(row_elems=300, d_qk=256, d_v=256), -5),
+    (dict(row_elems=144, d_qk=128, d_v=128), -5),           # 288-B rows take K = all 144 elements
     (dict(d_qk=600), -1),
     (dict(n_prefix=0, prefix_len=10), -1),
     (dict(n_prefix=2, prefix_len=0), -1),

@@ -158,6 +158,33 @@ def test_mla_two_groups_two_steps(n_chunks, fetch_cus):
     pair.lib.close()
 
 
+@pytest.mark.parametrize("n_heads,n_chunks", [(128, 2), (16, 1), (64, 3)])
+def test_288_byte_rows_two_groups_two_steps(n_heads, n_chunks):
+    """Rows of 144 bf16 (288 B, the bytes per missed selection of the pages'
+    DeepSeek configuration, Table 3): K = all 144 elements, V = the first 128.
+    The key width is no multiple of the four waves' 16-dim k-steps (the last
+    wave of a head block takes none) and a row's 18 chunks leave gather lanes
+    idle.  Two groups, two steps with a commit, key splits at this size."""
+    w = _mla_small(row_elems=144, d_qk=144, v_off=0, d_v=128, n_heads=n_heads)
+    pair = build_pair(w, lib_kw=dict(n_chunks=n_chunks))
+    assert pair.lib.info["attn_splits"] > 1
+    n = pair.hist_len.copy()
+    for step in range(2):
+        sis = []
+        for g in range(w.n_groups):
+            si = make_step_inputs(w, g, step, n)
+            res = pair.orc.verify_step(g, si.topk, si.causal_pos, si.queries, si.block_rows, n_threads=8)
+            out = run_lib_step(pair, g, si)
+            compare_step(pair, g, si, res, out)
+            compare_counts(pair, g, res)
+            sis.append(si)
+        acc = make_accepted(w, step, sis[0].k_active)
+        pair.orc.commit(acc)
+        pair.lib.commit(acc)
+        n = n + 1 + acc
+    pair.lib.close()
+
+
 def test_plan_shared_by_follower_layers():
     """Follower-layer reuse of one plan: groups 0-1 and 2-3 each form a set fed
     by one selection.  The leader resolves once and fetches for both layers;

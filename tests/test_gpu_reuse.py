@@ -66,9 +66,13 @@ def _check_reuse(pair, g, q, causal, what):
                 assert (got[r, j] == 0).all()
 
 
-def test_shared_source_full_reuse_reindex_reuse():
+@pytest.mark.parametrize("rows", ["mla576", "rows288"])
+def test_shared_source_full_reuse_reindex_reuse(rows):
     from hierarchical_sparse_kv_verify_amd import KVHierError
-    w = _mla_small(n_groups=1)
+    if rows == "mla576":
+        w = _mla_small(n_groups=1)
+    else:  # the 288-B rows of the shared-source measurement, 128 heads
+        w = _mla_small(n_groups=1, row_elems=144, d_qk=144, v_off=0, d_v=128, n_heads=128)
     pair = build_pair(w, lib_kw=dict(flags=2, n_chunks=2))
     orc, lib = pair.orc, pair.lib
     with pytest.raises(KVHierError) as ei:            # nothing to reuse yet

@@ -140,13 +140,13 @@ def _ds_shared() -> Workload:
     return Workload(
         name="ds_shared", config_id=6, n_req=128, n_groups=4, n_arenas=4,
         hist_lo=99_000, hist_hi=100_000, hist_cap=100_512, n_prefix=1, prefix_len=98_304,
-        row_elems=576, d_qk=576, v_off=0, d_v=512, n_heads=128,
+        row_elems=144, d_qk=144, v_off=0, d_v=128, n_heads=128,
         q_max=4, topk=512, hot_slots=2048, ring_window=64, ring_page=64,
         f_sh=0.85, zipf_s=1.0, hit_rate=0.82,
         note="4 shared KV sources (one staging arena each) read by several layers: per source "
              "a selecting layer, a re-selecting layer and layers reusing the latest selection; "
-             "128 requests x ~100K rows, MLA 576 bf16, 128 heads, Q=4, k=512, B=2048, W=64, "
-             "~18% distinct-row misses")
+             "128 requests x ~100K rows of 144 bf16 (288 B: K = all 144, V = the first 128), "
+             "128 heads, Q=4, k=512, B=2048, W=64, ~18% distinct-row misses")
 
 
 WORKLOADS = {w.name: w for w in (_tiny(), _mla32(), _mla128(), _mla128_res(), _mla512(), _mla128_shared(),
