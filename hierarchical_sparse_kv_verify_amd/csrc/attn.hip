@@ -48,6 +48,8 @@
 //    rows shared by a request's queries are re-read from that XCD's L2.
 #include "common.h"
 
+#include <hip/hip_ext.h>
+
 #include <type_traits>
 
 namespace kvh {
@@ -713,14 +715,32 @@ hipError_t set_lds_limit() {
                              hipFuncAttributeMaxDynamicSharedMemorySize, int(C::LDS));
 }
 
+// Events, when given, are bound to the launch (they complete with it and time
+// its own start and end); with nothing to launch they are recorded in place.
+hipError_t no_launch(hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
+  if (ev_start) (void)hipEventRecord(ev_start, s);
+  if (ev_stop) return hipEventRecord(ev_stop, s);
+  return hipSuccess;
+}
+
+template <class K, class... Args>
+hipError_t launch_with(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, hipEvent_t ev_start,
+                       hipEvent_t ev_stop, Args... args) {
+  if (ev_start || ev_stop) {
+    hipExtLaunchKernelGGL(kernel, grid, block, uint32_t(lds), s, ev_start, ev_stop, 0, args...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+  }
+  return hipGetLastError();
+}
+
 template <class C>
-hipError_t launch_cfg(const AttnArgs& a, hipStream_t s) {
+hipError_t launch_cfg(const AttnArgs& a, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
   const int nreq = a.r1 - a.r0;
-  if (nreq <= 0) return hipSuccess;
+  if (nreq <= 0) return no_launch(s, ev_start, ev_stop);
   const int per_req = a.Q * a.head_groups * a.splits;
   const long long blocks = (long long)((nreq + 7) / 8) * 8 * per_req;
-  hipLaunchKernelGGL(attn_kernel<C>, dim3(unsigned(blocks)), dim3(C::NT), C::LDS, s, a);
-  return hipGetLastError();
+  return launch_with(attn_kernel<C>, dim3(unsigned(blocks)), dim3(C::NT), C::LDS, s, ev_start, ev_stop, a);
 }
 
 }  // namespace
@@ -743,38 +763,38 @@ bool attn_layout_supported(int row_elems, int d_qk, int v_off, int d_v) {
 
 int attn_heads_per_wg(int H) { return H <= 32 ? 32 : 64; }
 
-hipError_t launch_attn(const AttnArgs& a, int row_elems, int d_qk, int v_off, int d_v, hipStream_t s) {
+hipError_t launch_attn(const AttnArgs& a, int row_elems, int d_qk, int v_off, int d_v, hipStream_t s,
+                       hipEvent_t ev_start, hipEvent_t ev_stop) {
   const int hpw = attn_heads_per_wg(a.H);
   if (row_elems == 576 && d_qk == 576 && v_off == 0 && d_v == 512) {
-    if (hpw == 32) return launch_cfg<Cfg<576, 0, 512, 576, 1>>(a, s);
-    return launch_cfg<Cfg<576, 0, 512, 576, 2>>(a, s);
+    if (hpw == 32) return launch_cfg<Cfg<576, 0, 512, 576, 1>>(a, s, ev_start, ev_stop);
+    return launch_cfg<Cfg<576, 0, 512, 576, 2>>(a, s, ev_start, ev_stop);
   }
   if (row_elems == 256 && d_qk == 128 && v_off == 128 && d_v == 128) {
-    if (hpw == 32) return launch_cfg<Cfg<128, 128, 128, 256, 1>>(a, s);
-    return launch_cfg<Cfg<128, 128, 128, 256, 2>>(a, s);
+    if (hpw == 32) return launch_cfg<Cfg<128, 128, 128, 256, 1>>(a, s, ev_start, ev_stop);
+    return launch_cfg<Cfg<128, 128, 128, 256, 2>>(a, s, ev_start, ev_stop);
   }
   if (row_elems == 144 && d_qk == 144 && v_off == 0 && d_v == 128) {
-    if (hpw == 32) return launch_cfg<Cfg<144, 0, 128, 144, 1>>(a, s);
-    return launch_cfg<Cfg<144, 0, 128, 144, 2>>(a, s);
+    if (hpw == 32) return launch_cfg<Cfg<144, 0, 128, 144, 1>>(a, s, ev_start, ev_stop);
+    return launch_cfg<Cfg<144, 0, 128, 144, 2>>(a, s, ev_start, ev_stop);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_attn_combine(const AttnArgs& a, int d_v, hipStream_t s) {
+hipError_t launch_attn_combine(const AttnArgs& a, int d_v, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
   const int nreq = a.r1 - a.r0;
-  if (nreq <= 0 || a.splits <= 1) return hipSuccess;
+  if (nreq <= 0 || a.splits <= 1) return no_launch(s, ev_start, ev_stop);
   const int hpw = attn_heads_per_wg(a.H);
   const dim3 grid(unsigned(((nreq + 7) / 8) * 8 * a.Q * a.head_groups * (hpw / 8)));
   if (d_v == 512) {
-    if (hpw == 32) hipLaunchKernelGGL((combine_kernel<512, 1>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((combine_kernel<512, 2>), grid, dim3(256), 0, s, a);
-  } else if (d_v == 128) {
-    if (hpw == 32) hipLaunchKernelGGL((combine_kernel<128, 1>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((combine_kernel<128, 2>), grid, dim3(256), 0, s, a);
-  } else {
-    return hipErrorInvalidValue;
+    if (hpw == 32) return launch_with(combine_kernel<512, 1>, grid, dim3(256), 0, s, ev_start, ev_stop, a);
+    return launch_with(combine_kernel<512, 2>, grid, dim3(256), 0, s, ev_start, ev_stop, a);
   }
-  return hipGetLastError();
+  if (d_v == 128) {
+    if (hpw == 32) return launch_with(combine_kernel<128, 1>, grid, dim3(256), 0, s, ev_start, ev_stop, a);
+    return launch_with(combine_kernel<128, 2>, grid, dim3(256), 0, s, ev_start, ev_stop, a);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace kvh

@@ -52,8 +52,10 @@ struct PlanArgs {
   int sort_cap;              // power of two >= B
 };
 size_t plan_lds_bytes(int Q, int k, int B, int chunk_words, int sort_cap);
-// union, probe, staging positions, locations (everything the fetch needs)
-hipError_t launch_plan(const PlanArgs& a, size_t lds, hipStream_t s);
+// union, probe, staging positions, locations (everything the fetch needs);
+// ev_start / ev_stop as for launch_miss_gather
+hipError_t launch_plan(const PlanArgs& a, size_t lds, hipStream_t s, hipEvent_t ev_start = nullptr,
+                       hipEvent_t ev_stop = nullptr);
 // dynamic-LDS limits of the plan and attention kernels, on the current device
 hipError_t plan_init_attributes();
 hipError_t attn_init_attributes();
@@ -69,8 +71,11 @@ struct HostRowSrc {
 
 // miss gather: for r in [r0, r1), i < req_info[r][I_NMISS]:
 //   staging[(r*QK + i)] = host row miss_rows[r][i]
+// (ev_start / ev_stop, when given, are bound to the launch itself: they complete
+// with it and time its own start and end, with no marker of their own)
 hipError_t launch_miss_gather(const HostRowSrc& src, const int32_t* miss_rows, const int32_t* req_info,
-                              uint4* staging, int QK, int r0, int r1, int wg_per_req, hipStream_t s);
+                              uint4* staging, int QK, int r0, int r1, int wg_per_req, hipStream_t s,
+                              hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 // promote: hot[(r*B + victims[r][i])] = staging[r*QK + i], i < req_info[r][I_NPROMOTE]
 hipError_t launch_promote(const uint4* staging, const int32_t* victims, const int32_t* req_info,
                           uint4* hot, int QK, int B, int row16, int r0, int r1, hipStream_t s);
@@ -128,7 +133,10 @@ struct AttnArgs {
 // supported layouts; returns hipErrorInvalidValue for others
 bool attn_layout_supported(int row_elems, int d_qk, int v_off, int d_v);
 int attn_heads_per_wg(int H);
-hipError_t launch_attn(const AttnArgs& a, int row_elems, int d_qk, int v_off, int d_v, hipStream_t s);
-hipError_t launch_attn_combine(const AttnArgs& a, int d_v, hipStream_t s);
+// ev_start / ev_stop as for launch_miss_gather
+hipError_t launch_attn(const AttnArgs& a, int row_elems, int d_qk, int v_off, int d_v, hipStream_t s,
+                       hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+hipError_t launch_attn_combine(const AttnArgs& a, int d_v, hipStream_t s, hipEvent_t ev_start = nullptr,
+                               hipEvent_t ev_stop = nullptr);
 
 }  // namespace kvh

@@ -19,6 +19,8 @@
 // between resolution and movement.
 #include "common.h"
 
+#include <hip/hip_ext.h>
+
 namespace kvh {
 namespace {
 
@@ -217,10 +219,21 @@ inline unsigned grid_for(size_t work, unsigned cap) {
 }  // namespace
 
 hipError_t launch_miss_gather(const HostRowSrc& src, const int32_t* miss_rows, const int32_t* req_info,
-                              uint4* staging, int QK, int r0, int r1, int wg_per_req, hipStream_t s) {
-  if (r1 <= r0) return hipSuccess;
-  hipLaunchKernelGGL(miss_gather_kernel, dim3(wg_per_req, r1 - r0), dim3(64), 0, s, src, miss_rows,
-                     req_info, staging, QK, r0);
+                              uint4* staging, int QK, int r0, int r1, int wg_per_req, hipStream_t s,
+                              hipEvent_t ev_start, hipEvent_t ev_stop) {
+  if (r1 <= r0) {
+    // nothing to launch: the events still mark this point of the stream
+    if (ev_start) (void)hipEventRecord(ev_start, s);
+    if (ev_stop) return hipEventRecord(ev_stop, s);
+    return hipSuccess;
+  }
+  if (ev_start || ev_stop) {
+    hipExtLaunchKernelGGL(miss_gather_kernel, dim3(wg_per_req, r1 - r0), dim3(64), 0, s, ev_start, ev_stop, 0, src,
+                          miss_rows, req_info, staging, QK, r0);
+  } else {
+    hipLaunchKernelGGL(miss_gather_kernel, dim3(wg_per_req, r1 - r0), dim3(64), 0, s, src, miss_rows, req_info,
+                       staging, QK, r0);
+  }
   return hipGetLastError();
 }
 

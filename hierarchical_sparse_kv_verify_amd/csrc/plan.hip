@@ -24,6 +24,8 @@
 // is deterministic.
 #include "common.h"
 
+#include <hip/hip_ext.h>
+
 namespace kvh {
 namespace {
 
@@ -409,8 +411,12 @@ hipError_t plan_init_attributes() {
   return e;
 }
 
-hipError_t launch_plan(const PlanArgs& a, size_t lds, hipStream_t s) {
-  hipLaunchKernelGGL(plan_resolve_kernel, dim3(a.N), dim3(kThreads), lds, s, a);
+hipError_t launch_plan(const PlanArgs& a, size_t lds, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
+  if (ev_start || ev_stop) {
+    hipExtLaunchKernelGGL(plan_resolve_kernel, dim3(a.N), dim3(kThreads), uint32_t(lds), s, ev_start, ev_stop, 0, a);
+  } else {
+    hipLaunchKernelGGL(plan_resolve_kernel, dim3(a.N), dim3(kThreads), lds, s, a);
+  }
   return hipGetLastError();
 }
 

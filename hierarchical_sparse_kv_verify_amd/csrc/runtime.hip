@@ -101,6 +101,7 @@ struct Group {
   hipEvent_t ev_sel = nullptr;      // the group's last step wrote its ring rows and ran its attention
   bool sel_recorded = false;
   bool sel_valid = false;           // this step's selection may be reused (until commit)
+  bool map_wait = false;            // the resident maps changed on the side stream since its last plan
   int m = 1;                        // positions per stored row (compressed source when > 1)
   int64_t* req_counts = nullptr;
   unsigned long long* cum = nullptr;
@@ -185,12 +186,13 @@ struct kv_hier {
   hipStream_t side = nullptr;       // host fetch
   hipStream_t work = nullptr;       // the rest of the step when CUs are partitioned (else null)
   hipStream_t aux = nullptr;        // copy-back of promoted rows
-  hipEvent_t ev_resolved = nullptr; // LRU victims chosen (the copy-backs follow)
+  hipEvent_t ev_planned = nullptr;  // the last plan is complete (its launch's own end)
+  hipEvent_t ev_map = nullptr;      // last resident-map update on the side stream
   hipEvent_t ev_in = nullptr, ev_out = nullptr;
   int share = 1;                    // groups per plan-sharing set (leader + followers)
   std::vector<std::vector<hipEvent_t>> ev_fetched;   // [set member][chunk]
-  std::vector<std::vector<hipEvent_t>> ev_free;
-  std::vector<std::vector<char>> free_recorded;
+  std::vector<hipEvent_t> ev_free;  // [arena]: the arena's last readers are done (every chunk at once)
+  std::vector<char> free_recorded;
   std::vector<int> arena_owner;     // group whose payload the arena holds (-1 none)
   std::vector<int> arena_step;      // that group's step counter when it was fetched
   std::vector<int32_t> hist_len;
@@ -325,6 +327,32 @@ int time_begin(kv_hier* h, int kind, int g, hipStream_t s) {
 void time_end(kv_hier* h, int idx, hipStream_t s) {
   if (idx < 0) return;
   (void)hipEventRecord(h->pending[idx].b, s);
+}
+
+// Events bound to one launch (hipExtLaunchKernel): with timing on, the pair
+// that times the launch itself (no markers around it) and `done` to be
+// recorded after it; else `done` itself is the launch's end event.
+struct LaunchEv {
+  hipEvent_t start = nullptr, stop = nullptr, after = nullptr;
+};
+LaunchEv launch_events(kv_hier* h, int kind, int g, hipEvent_t done) {
+  LaunchEv le;
+  le.stop = done;
+  const bool on = !h->no_alloc_call &&
+                  ((h->cfg.flags & KV_FLAG_TIMING) ||
+                   ((h->cfg.flags & KV_FLAG_TIMING_ATTN) && (kind == K_ATTN || kind == K_COMBINE)));
+  if (!on) return le;
+  Timed t{kind, g, take_event(h), take_event(h)};
+  if (!t.a || !t.b) {
+    if (t.a) h->pool.push_back(t.a);
+    if (t.b) h->pool.push_back(t.b);
+    return le;
+  }
+  h->pending.push_back(t);
+  le.start = t.a;
+  le.stop = t.b;
+  le.after = done;
+  return le;
 }
 
 int drain_timing(kv_hier* h) {
@@ -496,8 +524,9 @@ void free_all(kv_hier* h) {
   for (hipEvent_t e : h->ev_backup)
     if (e) (void)hipEventDestroy(e);
   for (auto& v : h->ev_fetched) for (hipEvent_t e : v) (void)hipEventDestroy(e);
-  for (auto& v : h->ev_free) for (hipEvent_t e : v) (void)hipEventDestroy(e);
-  if (h->ev_resolved) (void)hipEventDestroy(h->ev_resolved);
+  for (hipEvent_t e : h->ev_free) (void)hipEventDestroy(e);
+  if (h->ev_map) (void)hipEventDestroy(h->ev_map);
+  if (h->ev_planned) (void)hipEventDestroy(h->ev_planned);
   if (h->side) (void)hipStreamDestroy(h->side);
   if (h->aux) (void)hipStreamDestroy(h->aux);
   Opt& o = h->opt;
@@ -598,14 +627,20 @@ int stage_list(kv_hier* h, const std::vector<int32_t>& ent, int32_t* dev, hipStr
 }
 
 // Publication (publish = 1) or withdrawal of pages in every group's resident
-// map, on the side stream: ordered before every later plan.
+// map, on the side stream, between the plans issued before it and those
+// issued after it: it waits for every group's last step (its plan ran before
+// its attention), and every group's next plan waits for it (map_wait).
 int opt_map(kv_hier* h, const std::vector<int32_t>& ent, int publish) {
   if (ent.empty()) return KV_OK;
   Opt& o = h->opt;
+  for (const Group& G : h->grp)
+    if (G.member == 0 && G.sel_recorded) HIPCHK(h, hipStreamWaitEvent(h->side, G.ev_sel, 0));
   int rc = stage_list(h, ent, o.d_list_side, h->side);
   if (rc) return rc;
   HIPCHK(h, launch_opt_map(o.d_groups, h->cfg.n_groups, o.d_list_side, int(ent.size() / 3), o.P, h->L, publish,
                            h->side));
+  HIPCHK(h, hipEventRecord(h->ev_map, h->side));
+  for (Group& G : h->grp) G.map_wait = true;
   if (!publish) {
     HIPCHK(h, hipEventRecord(o.ev_unpub, h->side));
     o.unpub_recorded = true;
@@ -679,16 +714,16 @@ int opt_drop(kv_hier* h, int r) {
 int attend(kv_hier* h, int g, const AttnArgs& at, hipStream_t s) {
   const kv_hier_config& c = h->cfg;
   if (at.splits > 1 && h->part_recorded) HIPCHK(h, hipStreamWaitEvent(s, h->ev_part, 0));
-  int ti = time_begin(h, K_ATTN, g, s);
+  LaunchEv le = launch_events(h, K_ATTN, g, nullptr);
   // test hook: the launch reports an error without launching anything
-  HIPCHK(h, (c.flags & KV_FLAG_TEST_FAIL_ATTN) ? hipErrorLaunchFailure
-                                                 : launch_attn(at, c.row_elems, c.d_qk, c.v_off, c.d_v, s));
-  time_end(h, ti, s);
+  HIPCHK(h, (c.flags & KV_FLAG_TEST_FAIL_ATTN)
+                ? hipErrorLaunchFailure
+                : launch_attn(at, c.row_elems, c.d_qk, c.v_off, c.d_v, s, le.start, le.stop));
   if (at.splits > 1) {
-    ti = time_begin(h, K_COMBINE, g, s);
-    HIPCHK(h, launch_attn_combine(at, c.d_v, s));
-    time_end(h, ti, s);
-    HIPCHK(h, hipEventRecord(h->ev_part, s));
+    // the partials' release is the merge's own end event unless timing holds it
+    le = launch_events(h, K_COMBINE, g, h->ev_part);
+    HIPCHK(h, launch_attn_combine(at, c.d_v, s, le.start, le.stop));
+    if (le.after) HIPCHK(h, hipEventRecord(le.after, s));
     h->part_recorded = true;
   }
   return KV_OK;
@@ -956,7 +991,7 @@ static int create_impl(kv_hier* h) {
     HIPCHK(h, hipEventCreateWithFlags(&G.ev_done, hipEventDisableTiming));
     HIPCHK(h, hipEventCreateWithFlags(&G.ev_sel, hipEventDisableTiming));
   }
-  HIPCHK(h, hipEventCreateWithFlags(&h->ev_resolved, hipEventDisableTiming));
+  HIPCHK(h, hipEventCreateWithFlags(&h->ev_planned, hipEventDisableTiming));
   HIPCHK(h, hipEventCreateWithFlags(&h->ev_in, hipEventDisableTiming));
   HIPCHK(h, hipEventCreateWithFlags(&h->ev_out, hipEventDisableTiming));
   HIPCHK(h, hipEventCreateWithFlags(&h->ev_part, hipEventDisableTiming));
@@ -973,12 +1008,12 @@ static int create_impl(kv_hier* h) {
   h->ev_fetched.assign(h->share, std::vector<hipEvent_t>(h->n_chunks, nullptr));
   for (auto& v : h->ev_fetched)
     for (auto& e : v) HIPCHK(h, hipEventCreateWithFlags(&e, hipEventDisableTiming));
-  h->ev_free.assign(c.n_arenas, std::vector<hipEvent_t>(h->n_chunks, nullptr));
-  h->free_recorded.assign(c.n_arenas, std::vector<char>(h->n_chunks, 0));
+  h->ev_free.assign(c.n_arenas, nullptr);
+  h->free_recorded.assign(c.n_arenas, 0);
   h->arena_owner.assign(c.n_arenas, -1);
   h->arena_step.assign(c.n_arenas, 0);
-  for (auto& v : h->ev_free)
-    for (auto& e : v) HIPCHK(h, hipEventCreateWithFlags(&e, hipEventDisableTiming));
+  for (auto& e : h->ev_free) HIPCHK(h, hipEventCreateWithFlags(&e, hipEventDisableTiming));
+  HIPCHK(h, hipEventCreateWithFlags(&h->ev_map, hipEventDisableTiming));
   HIPCHK(h, hipDeviceSynchronize());
   return rc;
 }
@@ -1231,8 +1266,8 @@ static int verify_step_impl(kv_hier_t* h, int g, const void* queries, const int3
   const kv_hier_config& c = h->cfg;
   hipStream_t caller = static_cast<hipStream_t>(stream);
   hipStream_t s = caller;
-  HIPCHK(h, hipEventRecord(h->ev_in, caller));
   if (h->work) {           // the step runs on the partitioned stream, ordered after the caller's work
+    HIPCHK(h, hipEventRecord(h->ev_in, caller));
     HIPCHK(h, hipStreamWaitEvent(h->work, h->ev_in, 0));
     s = h->work;
   }
@@ -1241,12 +1276,9 @@ static int verify_step_impl(kv_hier_t* h, int g, const void* queries, const int3
   const bool lead = G.member == 0;
   // rows of the last commit are still in the tail (resolved from the ring);
   // those of the commit before may be fetched from the host or have their ring
-  // slots rewritten by this step: its backup must be complete
-  if (h->backup && h->n_commits >= 2) {
-    hipEvent_t eb = h->ev_backup[h->n_commits % 2];
-    HIPCHK(h, hipStreamWaitEvent(s, eb, 0));
-    if (lead) HIPCHK(h, hipStreamWaitEvent(h->side, eb, 0));
-  }
+  // slots rewritten by this step: its backup must be complete (the side
+  // stream's fetches of this step follow the first fetch on this stream)
+  if (h->backup && h->n_commits >= 2) HIPCHK(h, hipStreamWaitEvent(s, h->ev_backup[h->n_commits % 2], 0));
   const int N = c.n_req;
   const int a = g % c.n_arenas;
   if (lead) {
@@ -1264,18 +1296,25 @@ static int verify_step_impl(kv_hier_t* h, int g, const void* queries, const int3
     time_end(h, ti, s);
   }
   if (lead) {
-    // resolution plan and host fetch on the side stream (no event hop between
-    // them), after the caller's prior work; the ring write runs beside the plan
-    HIPCHK(h, hipStreamWaitEvent(h->side, h->ev_in, 0));
-    // the plan rewrites the set's lists, counts and (through the victims) its
+    // The resolution plan and the first chunk's host fetch run on this stream,
+    // after the caller's prior work: no hop between streams lies between the
+    // caller's work, the plan, the first fetch and the first attention (each
+    // hop costs about as much as a short kernel).  The side stream fetches the
+    // other chunks once the first fetch is done, so after the plan.
+    // The plan rewrites the set's lists, counts and (through the victims) its
     // slot tables: every group of the set must have finished reading the
     // previous ones (its attention, copy-back and counters, all before its
-    // ev_done), whatever stream its step was issued on
+    // ev_done), whatever stream its step was issued on.
     for (int m = 0; m < h->share; ++m)
-      if (h->grp[g + m].done_recorded) HIPCHK(h, hipStreamWaitEvent(h->side, h->grp[g + m].ev_done, 0));
+      if (h->grp[g + m].done_recorded) HIPCHK(h, hipStreamWaitEvent(s, h->grp[g + m].ev_done, 0));
     // optional-history pages whose copies have completed become ready for
     // this step's resolution (the first group's step is the step boundary)
     if (g == 0 && h->opt.on && !h->no_alloc_call && (rc = opt_publish_impl(h, false))) return rc;
+    // resident-map updates issued since this group's last plan
+    if (G.map_wait) {
+      HIPCHK(h, hipStreamWaitEvent(s, h->ev_map, 0));
+      G.map_wait = false;
+    }
 
     PlanArgs pa;
     pa.topk = topk_idx;
@@ -1305,47 +1344,55 @@ static int verify_step_impl(kv_hier_t* h, int g, const void* queries, const int3
     pa.t = G.t;
     pa.chunk_words = h->chunk_words;
     pa.sort_cap = h->sort_cap;
-    ti = time_begin(h, K_PLAN, g, h->side);
-    HIPCHK(h, launch_plan(pa, h->plan_lds, h->side));
-    time_end(h, ti, h->side);
+    {
+      const LaunchEv le = launch_events(h, K_PLAN, g, h->ev_planned);
+      HIPCHK(h, launch_plan(pa, h->plan_lds, s, le.start, le.stop));
+      if (le.after) HIPCHK(h, hipEventRecord(le.after, s));
+    }
+    // LRU victims on the copy-back stream right after the plan: they run
+    // while the first chunk is fetched, when few other kernels hold CUs (each
+    // of their workgroups excludes an attention workgroup from its CU), and
+    // the copy-backs that need them follow on the same stream.  The group's
+    // next plan sees the updated slot tables through its ev_done.
+    HIPCHK(h, hipStreamWaitEvent(h->aux, h->ev_planned, 0));
+    ti = time_begin(h, K_VICTIMS, g, h->aux);
+    HIPCHK(h, launch_plan_victims(pa, h->plan_lds, h->aux));
+    time_end(h, ti, h->aux);
 
     // host fetch of every chunk, for this group and then for every follower
     // layer of its plan (one selection starts the transfers of all of them;
-    // each layer fetches its own bytes into its own arena).  The LRU victims
-    // follow this group's own fetch, on the same stream: off the path to its
-    // fetch, before the followers' fetches (their copy-backs need them), and
-    // the group's next plan (same stream) sees the updated slot tables.
+    // each layer fetches its own bytes into its own arena)
     for (int m = 0; m < h->share; ++m) {
       const int gm = g + m, am = gm % c.n_arenas;
       const HostRowSrc src = host_src(h, h->grp[gm]);
       for (int ch = 0; ch < h->n_chunks; ++ch) {
         const int r0 = h->chunk_lo[ch], r1 = h->chunk_lo[ch + 1];
-        if (h->free_recorded[am][ch]) HIPCHK(h, hipStreamWaitEvent(h->side, h->ev_free[am][ch], 0));
+        const bool here = m == 0 && ch == 0;      // the leader's first chunk: this stream
+        hipStream_t fs = here ? s : h->side;
+        // every chunk of an arena is released at once (after the arena's last
+        // readers); later chunks follow this wait on the same stream or, for
+        // the leader's arena, the first fetch
+        if (ch == 0 && h->free_recorded[am]) HIPCHK(h, hipStreamWaitEvent(fs, h->ev_free[am], 0));
         if (c.flags & KV_FLAG_POISON) {
           // debug: between the chunk's last readers and its next fetch the arena
           // holds NaN, so a read outside that order shows in the outputs
           const size_t words = size_t(r1 - r0) * h->QK * c.row_elems / 2;
           HIPCHK(h, launch_fill32(reinterpret_cast<uint32_t*>(h->arena[am] + size_t(r0) * h->QK * c.row_elems),
-                                  0x7fc07fc0u, words, h->side));
+                                  0x7fc07fc0u, words, fs));
         }
         // 128 one-wave workgroups: enough host reads in flight to fill the link;
         // more only queue in the memory system and slow the attention beside them
         const int wgs = c.fetch_wgs > 0 ? c.fetch_wgs : 128;
         const int wpr = std::max(1, wgs / std::max(1, r1 - r0));
-        ti = time_begin(h, K_GATHER, gm, h->side);
+        // the chunk's fetched event is the launch's own end (no marker) unless timing holds it
+        const LaunchEv le = launch_events(h, K_GATHER, gm, h->ev_fetched[m][ch]);
         HIPCHK(h, launch_miss_gather(src, G.miss_rows, G.req_info, reinterpret_cast<uint4*>(h->arena[am]), h->QK,
-                                     r0, r1, wpr, h->side));
-        time_end(h, ti, h->side);
-        HIPCHK(h, hipEventRecord(h->ev_fetched[m][ch], h->side));
+                                     r0, r1, wpr, fs, le.start, le.stop));
+        if (le.after) HIPCHK(h, hipEventRecord(le.after, fs));
+        if (here) HIPCHK(h, hipStreamWaitEvent(h->side, h->ev_fetched[0][0], 0));
       }
       h->arena_owner[am] = gm;
       h->arena_step[am] = G.t;
-      if (m == 0) {
-        ti = time_begin(h, K_VICTIMS, g, h->side);
-        HIPCHK(h, launch_plan_victims(pa, h->plan_lds, h->side));
-        time_end(h, ti, h->side);
-        HIPCHK(h, hipEventRecord(h->ev_resolved, h->side));
-      }
     }
   }
   // attention per chunk on the caller's stream, copy-back on the copy-back stream
@@ -1377,24 +1424,24 @@ static int verify_step_impl(kv_hier_t* h, int g, const void* queries, const int3
   at.head_groups = h->head_groups;
   const float scale = c.softmax_scale > 0.f ? c.softmax_scale : 1.0f / std::sqrt(float(c.d_qk));
   at.scale_log2 = scale * 1.4426950408889634f;
-  // hot slots promoted by this group's previous step
-  if (G.done_recorded) HIPCHK(h, hipStreamWaitEvent(s, G.ev_done, 0));
+  // The hot slots promoted by this group's previous step are complete before
+  // any chunk's attention: the leader's plan (this stream, or the leader's
+  // for a follower) waited for every set member's ev_done before the first
+  // fetch, and every chunk's attention follows a fetch of this step.
   if (c.flags & KV_FLAG_SERIAL) HIPCHK(h, hipStreamWaitEvent(s, h->ev_fetched[G.member][h->n_chunks - 1], 0));
   for (int ch = 0; ch < h->n_chunks; ++ch) {
     at.r0 = h->chunk_lo[ch];
     at.r1 = h->chunk_lo[ch + 1];
     at.splits = h->chunk_splits[ch];
-    HIPCHK(h, hipStreamWaitEvent(s, h->ev_fetched[G.member][ch], 0));
+    // the leader's first chunk was fetched on this stream
+    if (!(lead && ch == 0)) HIPCHK(h, hipStreamWaitEvent(s, h->ev_fetched[G.member][ch], 0));
     if ((rc = attend(h, g, at, s))) return rc;
-    // copy-back on the aux stream once the victims are chosen, concurrent
-    // with the attention (victim slots are not read by the step)
-    if (ch == 0) {
-      HIPCHK(h, hipStreamWaitEvent(h->aux, h->ev_resolved, 0));
-      // a follower's counters are its plan's: copy the leader's last-step counts
-      if (!lead) HIPCHK(h, launch_counts_follow(P.req_counts, G.req_counts, G.cum, N, h->aux));
-    }
-    // a follower's chunk is fetched after its leader's victims are chosen
-    if (!lead) HIPCHK(h, hipStreamWaitEvent(h->aux, h->ev_fetched[G.member][ch], 0));
+    // copy-back on the aux stream, after the victims (issued there by the
+    // leader's step) and the chunk's fetch, concurrent with the attention
+    // (victim slots are not read by the step)
+    // a follower's counters are its plan's: copy the leader's last-step counts
+    if (ch == 0 && !lead) HIPCHK(h, launch_counts_follow(P.req_counts, G.req_counts, G.cum, N, h->aux));
+    HIPCHK(h, hipStreamWaitEvent(h->aux, h->ev_fetched[G.member][ch], 0));
     ti = time_begin(h, K_PROMOTE, g, h->aux);
     HIPCHK(h, launch_promote(reinterpret_cast<const uint4*>(h->arena[a]), P.victims, P.req_info,
                              reinterpret_cast<uint4*>(G.hot), h->QK, c.hot_slots, h->row16, at.r0, at.r1, h->aux));
@@ -1402,17 +1449,16 @@ static int verify_step_impl(kv_hier_t* h, int g, const void* queries, const int3
   }
   // One event after the group's last attention chunk (an event record costs
   // the stream a few microseconds, so there is none per chunk): a Reuse of
-  // this selection waits for it, and the arena chunks are released after it
-  // (a later fetch into a chunk then waits for every chunk's readers, which
-  // it does anyway when it belongs to a later step of the caller's stream).
+  // this selection waits for it, and the arena is released after it and the
+  // copy-backs (a later fetch into any chunk then waits for every chunk's
+  // readers, which it does anyway when it belongs to a later step of the
+  // caller's stream).
   HIPCHK(h, hipEventRecord(G.ev_sel, s));
   G.sel_recorded = true;
   G.sel_valid = true;
   HIPCHK(h, hipStreamWaitEvent(h->aux, G.ev_sel, 0));
-  for (int ch = 0; ch < h->n_chunks; ++ch) {
-    HIPCHK(h, hipEventRecord(h->ev_free[a][ch], h->aux));
-    h->free_recorded[a][ch] = 1;
-  }
+  HIPCHK(h, hipEventRecord(h->ev_free[a], h->aux));
+  h->free_recorded[a] = 1;
   // the group's hot cache is complete after its copy-backs: the group's next
   // attention waits for this
   HIPCHK(h, hipEventRecord(G.ev_done, h->aux));
@@ -1502,11 +1548,9 @@ static int verify_reuse_impl(kv_hier_t* h, int g, const void* queries, const int
   if (rc2) return rc2;
   // the arena is released once this reader and the step's own readers and
   // copy-backs are done: the release events now follow all of them
-  for (int ch = 0; ch < h->n_chunks; ++ch) {
-    if (h->free_recorded[a][ch]) HIPCHK(h, hipStreamWaitEvent(s, h->ev_free[a][ch], 0));
-    HIPCHK(h, hipEventRecord(h->ev_free[a][ch], s));
-    h->free_recorded[a][ch] = 1;
-  }
+  if (h->free_recorded[a]) HIPCHK(h, hipStreamWaitEvent(s, h->ev_free[a], 0));
+  HIPCHK(h, hipEventRecord(h->ev_free[a], s));
+  h->free_recorded[a] = 1;
   if (h->work) {
     HIPCHK(h, hipEventRecord(h->ev_out, s));
     HIPCHK(h, hipStreamWaitEvent(caller, h->ev_out, 0));

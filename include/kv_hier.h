@@ -274,8 +274,9 @@ int kv_hier_ring_load(kv_hier_t *h, int g, int r, int32_t first_pos, const void 
  * request's ring still holds: positions >= max(first ring position,
  * n_r + q_max - R_d)) and the resident map, then the hot cache, fetches every
  * distinct missing row once from pinned host memory
- * into the group's staging arena (on a side stream, overlapped with attention
- * of earlier request chunks), runs exact sparse attention of every query over
+ * into the group's staging arena (the first request chunk on `stream` after
+ * the resolution, the others on a side stream, overlapped with attention of
+ * earlier request chunks), runs exact sparse attention of every query over
  * its own list plus its ring window, and copies promoted rows into their
  * victim slots.  Caller contract (not checked on the device): causal_pos[r][0]
  * equals the frontier set by kv_hier_set_hist_len / kv_hier_commit.
