@@ -31,7 +31,9 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
-constexpr int kMissMark = -2;
+// a union row found nowhere on the device is held as -2 - row until it gets
+// its staging position (every other code is >= 0)
+__device__ __forceinline__ int32_t miss_mark(int row) { return -2 - row; }
 constexpr int kBatch = 16;         // independent loads issued together
 
 __host__ __device__ inline size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
@@ -111,10 +113,24 @@ __global__ __launch_bounds__(kThreads) void plan_resolve_kernel(PlanArgs a) {
   uint32_t amask = 0;
   for (int j = 0; j < Q; ++j) amask |= (cp[j] >= 0 ? 1u : 0u) << j;
 
+  // When a thread's entries fit one batch (QK <= kBatch * kThreads, the usual
+  // case) they are loaded once and held in registers through the marking and
+  // location passes of every row chunk.
+  const bool held = QK <= kBatch * kThreads;
+  int hv[kBatch];
+  if (held) {
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int i = tid + b * kThreads;
+      hv[b] = i < QK ? tk[i] : -1;
+    }
+  }
   for (int w = tid; w < pwords; w += kThreads) protect[w] = 0;
   if (tid < 32) cnt[tid] = 0;
+  for (int w = tid; w < CW; w += kThreads) bitmap[w] = 0;   // the first row chunk's bitmap
   // the zeroing is complete in every wave before any wave adds to the
-  // counters or marks a slot (also when the row loop below runs no chunk)
+  // counters, marks a slot or marks a row (also when the row loop below runs
+  // no chunk)
   __syncthreads();
 
   int c_sel = 0, c_pad = 0, c_bad = 0, c_sres = 0, c_shot = 0, c_smiss = 0, c_stail = 0;
@@ -124,8 +140,10 @@ __global__ __launch_bounds__(kThreads) void plan_resolve_kernel(PlanArgs a) {
 
   for (int c0 = 0; c0 < n_r; c0 += CB) {
     const int c1 = min(c0 + CB, n_r);
-    for (int w = tid; w < CW; w += kThreads) bitmap[w] = 0;
-    __syncthreads();
+    if (c0 > 0) {
+      for (int w = tid; w < CW; w += kThreads) bitmap[w] = 0;
+      __syncthreads();
+    }
     // mark the selections of this row chunk (loads issued kBatch at a time)
     for (int i0 = tid; i0 < QK; i0 += kBatch * kThreads) {
       int ev[kBatch];
@@ -134,7 +152,7 @@ __global__ __launch_bounds__(kThreads) void plan_resolve_kernel(PlanArgs a) {
       for (int b = 0; b < kBatch; ++b) {
         const int i = i0 + b * kThreads;
         on[b] = i < QK && ((amask >> (i / k)) & 1u);
-        ev[b] = on[b] ? tk[i] : -1;
+        ev[b] = on[b] ? (held ? hv[b] : tk[i]) : -1;
       }
 #pragma unroll
       for (int b = 0; b < kBatch; ++b) {
@@ -158,7 +176,9 @@ __global__ __launch_bounds__(kThreads) void plan_resolve_kernel(PlanArgs a) {
     for (int w = wb; w < we; ++w) mine += __popc(bitmap[w]);
     int chunk_union;
     const int ubase = block_exclusive_scan(mine, scratch, &chunk_union);
-    // union rows of the chunk in ascending order, with the per-word rank table
+    // union rows of the chunk in ascending order, with the per-word rank table;
+    // the rows also go to uloc, which the probe below reads and overwrites
+    // with their codes
     int run = ubase;
     for (int w = wb; w < we; ++w) {
       wpre[w] = static_cast<uint16_t>(run);
@@ -166,7 +186,9 @@ __global__ __launch_bounds__(kThreads) void plan_resolve_kernel(PlanArgs a) {
       while (bits) {
         const int b = __ffs(bits) - 1;
         bits &= bits - 1;
-        a.union_rows[size_t(r) * QK + union_base + run] = c0 + w * 32 + b;
+        const int row = c0 + w * 32 + b;
+        a.union_rows[size_t(r) * QK + union_base + run] = row;
+        uloc[run] = row;
         ++run;
       }
     }
@@ -179,7 +201,7 @@ __global__ __launch_bounds__(kThreads) void plan_resolve_kernel(PlanArgs a) {
 #pragma unroll
       for (int b = 0; b < kBatch; ++b) {
         const int x = x0 + b * kThreads;
-        uv[b] = x < chunk_union ? a.union_rows[size_t(r) * QK + union_base + x] : -1;
+        uv[b] = x < chunk_union ? uloc[x] : -1;
       }
 #pragma unroll
       for (int b = 0; b < kBatch; ++b) {
@@ -204,7 +226,7 @@ __global__ __launch_bounds__(kThreads) void plan_resolve_kernel(PlanArgs a) {
           a.slot_lu[size_t(r) * B + sm] = a.t;
           ++c_uhot;
         } else {
-          code = kMissMark;
+          code = miss_mark(uv[b]);
           ++c_umiss;
         }
         uloc[x] = code;
@@ -215,14 +237,14 @@ __global__ __launch_bounds__(kThreads) void plan_resolve_kernel(PlanArgs a) {
     const int upt = (chunk_union + kThreads - 1) / kThreads;
     const int xb = min(tid * upt, chunk_union), xe = min(xb + upt, chunk_union);
     int my_miss = 0;
-    for (int x = xb; x < xe; ++x) my_miss += uloc[x] == kMissMark;
+    for (int x = xb; x < xe; ++x) my_miss += uloc[x] < 0;
     int chunk_miss;
     const int mbase = block_exclusive_scan(my_miss, scratch, &chunk_miss);
     int mi = miss_base + mbase;
     for (int x = xb; x < xe; ++x) {
       int code = uloc[x];
-      if (code == kMissMark) {
-        a.miss_rows[size_t(r) * QK + mi] = a.union_rows[size_t(r) * QK + union_base + x];
+      if (code < 0) {
+        a.miss_rows[size_t(r) * QK + mi] = -2 - code;
         code = make_loc(kTierStaged, r * QK + mi);
         uloc[x] = code;
         ++mi;
@@ -234,7 +256,7 @@ __global__ __launch_bounds__(kThreads) void plan_resolve_kernel(PlanArgs a) {
     for (int i0 = tid; i0 < QK; i0 += kBatch * kThreads) {
       int ev[kBatch];
 #pragma unroll
-      for (int q = 0; q < kBatch; ++q) ev[q] = i0 + q * kThreads < QK ? tk[i0 + q * kThreads] : -1;
+      for (int q = 0; q < kBatch; ++q) ev[q] = i0 + q * kThreads < QK ? (held ? hv[q] : tk[i0 + q * kThreads]) : -1;
 #pragma unroll
       for (int q = 0; q < kBatch; ++q) {
         const int i = i0 + q * kThreads;
