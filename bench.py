@@ -233,11 +233,11 @@ def main():
             d = dev[g]
             lib.verify_step(g, d["queries"], d["topk"], d["causal"], d["ring"], out)
 
-    # The attention (the roofline's kernel) is timed with HIP events recorded
-    # around its launches, on its stream, during the timed steps themselves;
-    # those events sit on no stream that gates the host fetch.  Every other
-    # kernel is timed in a separate pass, whose events on the fetch stream
-    # would otherwise lengthen the timed steps.
+    # The attention (the roofline's kernel) is timed with HIP events bound to
+    # its launches (the launch's own start and end, no marker on its stream)
+    # during the timed steps themselves.  Every other kernel is timed in a
+    # separate pass, whose events on the fetch stream would otherwise
+    # lengthen the timed steps.
     lib.set_flags(KV_FLAG_TIMING_ATTN)
     for _ in range(args.warmup):
         restore()
@@ -350,7 +350,7 @@ def main():
     same_launch = (args.workload == "mla128" and args.rho == 0 and not args.retained and args.n_chunks == 0
                    and args.fetch_cus == 0 and args.fetch_wgs == 0)
     roofline["traffic"] = attn_traffic(attn_bytes / n_attn_live) if same_launch else None
-    roofline["timing"] = "HIP events around every attention launch during the timed steps"
+    roofline["timing"] = "HIP events bound to every attention launch (its start and end) during the timed steps"
     rooflines["sparse_attn"]["traffic"] = roofline["traffic"]
     # host-link bytes from the IO read counter: rows of the shared prefix that
     # two requests of a chunk both miss can be served on the GPU side

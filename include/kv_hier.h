@@ -84,8 +84,8 @@ enum {
   KV_FLAG_TIMING = 1,    /* time every kernel with HIP events (kv_hier_stats ms_*) */
   KV_FLAG_POISON = 2,    /* debug: fill a staging-arena chunk with NaN between its last readers
                             and its next fetch (and a dynamic pool at create)            */
-  KV_FLAG_TIMING_ATTN = 4, /* time only the attention (and split-combine) launches: the
-                              events then sit on no stream that gates the host fetch   */
+  KV_FLAG_TIMING_ATTN = 4, /* time only the attention (and split-combine) launches, with
+                              events bound to the launches (no marker on any stream)   */
   KV_FLAG_SERIAL = 8,     /* measurement: the step's attention starts only after its whole
                              host fetch, so it runs alone on the GPU (slower steps)     */
   KV_FLAG_SYNC_BACKUP = 16, /* measurement: commit's host backup runs on the caller's stream,
