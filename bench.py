@@ -799,8 +799,8 @@ def cpu_baseline(w, hists, hl, sis, n_req_sample, n_groups_sample):
     from workloads import make_hot_warm_set
     from workloads.load import prefill_rows
 
-    # the GPU machine gives each GPU a share of 16 host threads, whatever the
-    # affinity mask shows: the oracle's worker pool is sized to that share
+    # the host gives each GPU a share of 16 threads, whatever the affinity
+    # mask shows: the oracle's worker pool is sized to that share
     online = len(os.sched_getaffinity(0))
     cores = min(online, CPU_SHARE_THREADS)
     reqs = list(range(min(n_req_sample, w.n_req)))

@@ -24,8 +24,8 @@ Hierarchy" (arXiv 2610.13708), referred to below as "the paper":
 Everything is plain Python containers (sets, dicts, sorted lists) walked in
 the paper's order; attention is the C reference in ``attn_ref.c``.
 
-Readings where the pages leave a step open.  One numbering R1-R26 covers
-every reading of this build; the ones the oracle follows are listed here and
+Readings where the pages leave a step open.  One numbering R1-R27 covers
+every reading taken of the pages; the ones the oracle follows are listed here and
 in ``residency.py`` (R17-R21, dynamic residency):
   R1 a list entry e of query j is a valid history selection iff 0 <= e < n_r
      (n_r = causal position of the anchor); -1 is a pad; anything else is

@@ -23,8 +23,8 @@ Hierarchy" (arXiv 2610.13708):
     capacity.
   - Figure 2 / §3.2: resolution consults the ready optional map first.
 
-Readings where the pages leave a step open (one numbering R1-R26 covers
-every reading of this build; R1-R10, R24 and R26 are in ``model.py``):
+Readings where the pages leave a step open (one numbering R1-R27 covers
+every reading taken of the pages; R1-R10, R24, R26 and R27 are in ``model.py``):
   R17 the pool holds M pages of P rows; an admitted request's required
       allocations (hot cache, tail, staging) are charged against M in pages
       but occupy no pool page; optional pages occupy pool pages.  Eq. (3)
