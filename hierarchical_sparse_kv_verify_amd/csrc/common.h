@@ -50,6 +50,12 @@ struct PlanArgs {
   int has_resident;          // 0: the resident map holds no row (its lookups are skipped)
   int chunk_words;           // bitmap words per row chunk (rows per chunk = 32 * chunk_words)
   int sort_cap;              // power of two >= B
+  // the step's own ring write (eq. 10), done by the plan's workgroups: row j of
+  // request r goes to ring slot r*Rd + causal[r][j] % Rd for causal >= 0
+  // (ring_rows null: nothing written)
+  const uint4* ring_rows;    // [N][Q][row16]
+  uint4* ring;               // [N*Rd][row16]
+  int row16;
 };
 size_t plan_lds_bytes(int Q, int k, int B, int chunk_words, int sort_cap);
 // union, probe, staging positions, locations (everything the fetch needs);

@@ -96,6 +96,15 @@ __global__ __launch_bounds__(kThreads) void plan_resolve_kernel(PlanArgs a) {
   const int32_t* cp = a.causal + size_t(r) * Q;
   const int32_t* tk = a.topk + size_t(r) * QK;
   int32_t* loc = a.loc + size_t(r) * QK;
+  // this step's ring rows (nothing in the plan reads them: no barrier)
+  if (a.ring_rows) {
+    for (int i = tid; i < Q * a.row16; i += kThreads) {
+      const int j = i / a.row16, c = i - j * a.row16;
+      const int pos = cp[j];
+      if (pos >= 0)
+        a.ring[(size_t(r) * a.Rd + pos % a.Rd) * a.row16 + c] = a.ring_rows[(size_t(r) * Q + j) * a.row16 + c];
+    }
+  }
   const int n_raw = cp[0];
   if (n_raw < 0) {  // inactive request: no selections, nothing resolved
     for (int i = tid; i < QK; i += kThreads) loc[i] = -1;

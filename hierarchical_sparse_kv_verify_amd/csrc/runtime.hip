@@ -1292,7 +1292,9 @@ static int verify_step_impl(kv_hier_t* h, int g, const void* queries, const int3
   G.calls += 1;
 
   int ti = -1;
-  if (ring_rows) {       // null: the source's producer already wrote this step's rows (a Reindex consumer)
+  // null ring_rows: the source's producer already wrote this step's rows (a
+  // Reindex consumer); a leader's plan writes them itself (below)
+  if (ring_rows && !lead) {
     ti = time_begin(h, K_RING, g, s);
     HIPCHK(h, launch_ring_write(static_cast<const uint4*>(ring_rows), causal_pos, reinterpret_cast<uint4*>(G.ring),
                                 N, c.q_max, h->Rd, h->row16, s));
@@ -1347,6 +1349,9 @@ static int verify_step_impl(kv_hier_t* h, int g, const void* queries, const int3
     pa.t = G.t;
     pa.chunk_words = h->chunk_words;
     pa.sort_cap = h->sort_cap;
+    pa.ring_rows = static_cast<const uint4*>(ring_rows);
+    pa.ring = reinterpret_cast<uint4*>(G.ring);
+    pa.row16 = h->row16;
     {
       const LaunchEv le = launch_events(h, K_PLAN, g, h->ev_planned);
       HIPCHK(h, launch_plan(pa, h->plan_lds, s, le.start, le.stop));
