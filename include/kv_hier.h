@@ -175,7 +175,8 @@ typedef struct {
   int64_t sel_resident;
   int64_t sel_hot;
   int64_t sel_miss;         /* missing selections (sum over queries)                     */
-  /* kernel time in ms summed over timed calls (KV_FLAG_TIMING), and launch counts */
+  /* kernel time in ms summed over timed calls (KV_FLAG_TIMING), and launch counts
+     (a leader's ring write runs inside its plan and is counted there)          */
   double ms_ring, ms_plan, ms_gather, ms_attn, ms_combine, ms_promote, ms_victims;
   int64_t n_ring, n_plan, n_gather, n_attn, n_combine, n_promote, n_victims;
   int64_t union_tail;       /* distinct rows resolved from the tail (the ring)           */
