@@ -90,7 +90,7 @@ class Info(ctypes.Structure):
                [(n, ctypes.c_int64) for n in ("bytes_hot", "bytes_staging", "bytes_ring", "bytes_maps",
                                               "bytes_resident", "bytes_host")] + \
                [("attn_splits", ctypes.c_int32), ("attn_head_groups", ctypes.c_int32),
-                ("plan_rows_per_pass", ctypes.c_int32)]
+                ("plan_rows_per_pass", ctypes.c_int32), ("attn_reuse_head_groups", ctypes.c_int32)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

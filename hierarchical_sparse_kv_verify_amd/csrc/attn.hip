@@ -650,6 +650,372 @@ __global__ __launch_bounds__(C::NT, 1) void attn_kernel(AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Narrow rows (144 elements: K = all 144, V = the first 128) above 32 heads.
+// One workgroup = one query x HB 32-head blocks (2: 64 heads, or 4: 128
+// heads, each row then gathered once per query) x one key split.  2*HB waves
+// = HB head blocks x two row halves: wave (hb, h) takes rows 32h..32h+31 of every 64-row tile over the
+// whole key width (its heads' Q fragments stay in registers), so its scores
+// are complete in its own accumulators.  The softmax runs in registers (the
+// 32 rows of a head sit in lanes l and l+32) and the probabilities go from
+// the accumulators straight into the B operand of O^T = V^T P^T; the V^T
+// fragments are read in the same row order (rows 4hi..4hi+3 and 8+4hi..+3 of
+// each 16-row k-step).  Tiles go from memory to LDS by DMA, two tiles ahead,
+// in a chunk-major layout: chunk c of tile row rho sits in 16-byte slot
+// c*64 + ((rho + c) & 63), so that the K reads (32 rows of one chunk) and the
+// transposed V reads (4 rows x 4 chunks per half-wave) hit every bank once.
+// One barrier per tile.  Each half keeps its own (m, l, O); half 1 hands them
+// to half 0 through LDS at the end.  Sum order depends only on list order and
+// split boundaries.
+template <int D_QK_, int V_OFF_, int D_V_, int ROW_, int HB_>
+struct NCfg {
+  static constexpr int D_QK = D_QK_, V_OFF = V_OFF_, D_V = D_V_, ROW = ROW_;
+  static constexpr int HB = HB_;               // 32-head blocks
+  static constexpr int NW = 2 * HB;            // waves: head block w % HB, row half w / HB
+  static constexpr int NT = NW * 64;
+  static constexpr int T = 64;                 // rows per tile
+  static constexpr int KST = D_QK / 16;        // 16-dim k-steps over the key width
+  static constexpr int DVB = D_V / 32;         // 32-dim value blocks (a wave holds all value dims)
+  static constexpr int RCH = ROW / 8;          // 16-byte chunks per row
+  static constexpr int TBUF = RCH * T * 8;     // elements per tile buffer (chunk-major, unpadded)
+  static constexpr int NBUF = 3;
+  // DMA instructions per wave and tile: the chunk columns 16/NW of every row,
+  // a 1/(NW/2) share of chunk column 16 or 17, the codes
+  static constexpr int NCOL = 16 / NW;
+  static constexpr int NVM = NCOL + 2;
+  static constexpr size_t LDS_K = size_t(NBUF) * TBUF * 2;
+  static constexpr size_t LDS_C = size_t(3) * NW * 64 * 4;      // per wave, three 64-entry code slots
+  // value blocks of O handed over per merge phase (16 registers x 64 lanes x
+  // 4 B per block and head block, in the tile buffers)
+  static constexpr int DPH = size_t(HB) * DVB * 4096 <= LDS_K ? DVB : (size_t(HB) * 2 * 4096 <= LDS_K ? 2 : 1);
+  static constexpr size_t LDS_ML = size_t(HB) * 32 * 2 * 4;
+  static constexpr size_t LDS = LDS_K + LDS_C + LDS_ML;
+  static_assert(D_QK % 16 == 0 && D_V % 32 == 0 && ROW % 8 == 0, "shape");
+  static_assert(V_OFF % 8 == 0 && V_OFF + D_V <= ROW && D_QK <= ROW, "row layout");
+  // the DMA split: chunk columns w, w+NW, .. below 16 per wave, columns 16
+  // and 17 in shares of 64/(NW/2) rows
+  static_assert((NW == 8 || NW == 4) && RCH == 18, "DMA split");
+  static_assert(DVB % DPH == 0, "merge");
+  static_assert(LDS <= 160 * 1024, "LDS");
+};
+
+// Element offset of (tile row rho, chunk c) in a chunk-major tile buffer.
+__device__ __forceinline__ int narrow_slot(int rho, int c) { return (c * 64 + ((rho + c) & 63)) * 8; }
+
+// DMA of one 64-row tile into buffer dst.  Lane l holds the code of tile row
+// l; the instruction for chunk c moves row (l - c) & 63 in lane l (its
+// address taken from that lane), landing in slot c*64 + l.  Wave w of NW
+// moves chunks w, w+NW, .. below 16 of every row and the slots
+// 64/(NW/2) * (w/2) .. +64/(NW/2)-1 of chunk 16 + (w & 1): 16/NW + 1
+// instructions.  Returns the tile's live-row mask.
+template <class C>
+__device__ __forceinline__ uint64_t dma_narrow_tile(uint16_t* dst, const RowCtx& ctx, int code, int w, int lane) {
+  const uint64_t live = __builtin_amdgcn_ballot_w64(code >= 0);
+  const uintptr_t my = row_addr<C::ROW>(ctx, code);
+  const int mlo = static_cast<int>(static_cast<uint32_t>(my));
+  const int mhi = static_cast<int>(static_cast<uint32_t>(my >> 32));
+  auto src_row = [&](int c) {
+    const int src = (lane - c) & 63;
+    return (uintptr_t(uint32_t(__shfl(mhi, src, 64))) << 32) | uint32_t(__shfl(mlo, src, 64));
+  };
+#pragma unroll
+  for (int u = 0; u < C::NCOL; ++u) {
+    const int c = w + C::NW * u;
+    dma16(src_row(c) + size_t(c) * 16, dst + c * 64 * 8);
+  }
+  const int c = 16 + (w & 1);
+  const uintptr_t ga = src_row(c) + size_t(c) * 16;
+  if (lane / (128 / C::NW) == (w >> 1)) dma16(ga, dst + c * 64 * 8);
+  return live;
+}
+
+// DMA of the raw codes of tile t (64 rows) into this wave's slot.
+__device__ __forceinline__ void dma_narrow_codes(int32_t* slot, const RowCtx& c, int t, int lane) {
+  dma4(reinterpret_cast<uintptr_t>(c.loc + min(t * 64 + lane, c.k - 1)), slot);
+}
+
+template <class C>
+__global__ __launch_bounds__(C::NT, 1) void attn_narrow_kernel(AttnArgs a) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  uint16_t* Kb = reinterpret_cast<uint16_t*>(lds);
+  float* Om = reinterpret_cast<float*>(lds);                     // merge area (tile buffers, after the loop)
+  int32_t* Cs = reinterpret_cast<int32_t*>(lds + C::LDS_K);      // code slots
+  float* Mm = reinterpret_cast<float*>(lds + C::LDS_K + C::LDS_C);   // [HB][32] running max of half 1
+  float* Ml = Mm + C::HB * 32;                                   // [HB][32] normaliser of half 1
+
+  const int nreq = a.r1 - a.r0;
+  const int per_req = a.Q * a.head_groups * a.splits;
+  const int b = blockIdx.x;
+  const int rr = ((b >> 3) / per_req) * 8 + (b & 7);
+  if (rr >= nreq) return;
+  const int sub = (b >> 3) % per_req;
+  const int j = sub / (a.head_groups * a.splits);
+  const int hg = (sub / a.splits) % a.head_groups;
+  const int sp = sub % a.splits;
+  const int r = a.r0 + rr;
+  const int qi = r * a.Q + j;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hb = w % C::HB, h = w / C::HB;
+  const int hl = hb * 32 + (lane & 31);
+  const int head = hg * 32 * C::HB + hl;
+  const size_t blk = (size_t(qi - a.r0 * a.Q) * a.head_groups + hg) * a.splits + sp;
+  const int hi_half = lane >> 5;
+
+  const int p_j = a.causal[qi];
+  if (p_j < 0) {  // inactive query: zero output (the combine pass does it when split)
+    if (a.splits == 1 && h == 0 && head < a.H) {
+      uint16_t* op = a.out + (size_t(qi) * a.H + head) * C::D_V;
+      for (int d = hi_half; d < C::D_V / 4; d += 2) *reinterpret_cast<uint2*>(op + d * 4) = make_uint2(0, 0);
+    }
+    return;
+  }
+  const int n_r = a.causal[size_t(r) * a.Q];
+  int lo = a.ring_lo[r];
+  lo = max(lo, p_j - a.W + 1);
+  lo = max(lo, 0);
+  if (a.block_only) lo = max(lo, n_r);
+  const int n_ring = p_j >= lo ? p_j - lo + 1 : 0;
+
+  RowCtx ctx;
+  ctx.loc = reinterpret_cast<gint32*>(reinterpret_cast<uintptr_t>(a.loc + size_t(qi) * a.k));
+  ctx.k = a.k;
+  ctx.n_total = a.k + n_ring;
+  ctx.Rd = a.Rd;
+  ctx.ring_row0 = r * a.Rd + lo % a.Rd;
+  ctx.ring_end = (r + 1) * a.Rd;
+  ctx.hot = reinterpret_cast<uintptr_t>(a.hot);
+  ctx.d_staging = reinterpret_cast<uintptr_t>(a.staging) - ctx.hot;
+  ctx.d_resident = reinterpret_cast<uintptr_t>(a.resident) - ctx.hot;
+  ctx.d_ring = reinterpret_cast<uintptr_t>(a.ring) - ctx.hot;
+  ctx.zero = reinterpret_cast<uintptr_t>(a.zero);
+
+  const int n_tiles = (ctx.n_total + C::T - 1) / C::T;
+  const int tb = int((long long)n_tiles * sp / a.splits);
+  const int te = int((long long)n_tiles * (sp + 1) / a.splits);
+
+  // Q fragments over the whole key width: B operand of S^T = K Q^T
+  bf16x8 qreg[C::KST];
+  {
+    const uint16_t* qp = a.q + (size_t(qi) * a.H + head) * C::D_QK + hi_half * 8;
+#pragma unroll
+    for (int ks = 0; ks < C::KST; ++ks) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (head < a.H) v = gload16(reinterpret_cast<uintptr_t>(qp + ks * 16));
+      qreg[ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  f32x16 O[C::DVB];
+#pragma unroll
+  for (int d = 0; d < C::DVB; ++d)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) O[d][i] = 0.f;
+  float m_run = kNegBig, l_run = 0.f;
+  const float sl2 = a.scale_log2;
+
+  // tile x lives in buffer (x - tb) mod 3, its codes in slot (x - tb) mod 3
+  int32_t* cs_w = Cs + w * 64;
+  auto cslot = [&](int x) { return cs_w + ((x - tb) % 3) * (C::NW * 64); };
+  // prologue: the codes of tb, tb+1 loaded beside the Q fragments, one wait
+  // for both (the Q registers are then complete for the whole loop); DMA of
+  // tiles tb, tb+1 and of the codes of tb+2, tb+3; tile tb and the codes of
+  // tb+2 landed before the first tile
+  dma_narrow_codes(cslot(tb), ctx, tb, lane);
+  dma_narrow_codes(cslot(tb + 1), ctx, tb + 1, lane);
+  __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0)
+  uint64_t live_cur = dma_narrow_tile<C>(Kb, ctx, final_code(ctx, tb * C::T + lane, cslot(tb)[lane]), w, lane);
+  dma_narrow_codes(cslot(tb + 2), ctx, tb + 2, lane);
+  uint64_t live_n1 = dma_narrow_tile<C>(Kb + C::TBUF, ctx, final_code(ctx, (tb + 1) * C::T + lane, cslot(tb + 1)[lane]),
+                                        w, lane);
+  dma_narrow_codes(cslot(tb + 3), ctx, tb + 3, lane);
+  lds_vm_barrier<C::NVM>();
+
+  // per-lane parts of the LDS offsets: K fragment rows 32h + lane%32, chunk
+  // 2ks + hi; V^T rows 32h + 16ks2 + 4(gq/2) + s/4 (+8), chunks c0 + d
+  const int krow = 32 * h + (lane & 31);
+  int vrow, vc0, vsub;
+  {
+    const int gq = (lane >> 4) & 3, sl = lane & 15, aq = sl & 3;
+    vrow = 32 * h + (gq >> 1) * 4 + (sl >> 2);
+    vc0 = C::V_OFF / 8 + ((gq & 1) * 2 + (aq >> 1)) * C::DVB;
+    vsub = (aq & 1) * 4;
+  }
+  uint64_t live_n2 = 0;
+
+  auto tile = [&](int t, auto pconst) {
+    constexpr int P = decltype(pconst)::value;       // (t - tb) mod 3: buffer of tile t
+    const uint16_t* kb = Kb + P * C::TBUF;
+    // the codes of tile t+2 (landed before the last barrier), then this
+    // tile's K fragments: their LDS latency passes while the next DMA is
+    // issued (LDS reads complete in order, so the codes come first)
+    const int raw2 = (cs_w + ((P + 2) % 3) * (C::NW * 64))[lane];
+    bf16x8 kf[C::KST];
+#pragma unroll
+    for (int ks = 0; ks < C::KST; ++ks)
+      kf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + narrow_slot(krow, 2 * ks + hi_half)));
+    // DMA of tile t+2 into the buffer of tile t-1 (its readers passed the
+    // last barrier) and of the codes of tile t+4 into the slot of t+1;
+    // unconditional, so that every wave keeps NVM instructions per tile
+    // (positions past the range read the zero row and are never used)
+    {
+      live_n2 = dma_narrow_tile<C>(Kb + ((P + 2) % 3) * C::TBUF, ctx, final_code(ctx, (t + 2) * C::T + lane, raw2), w,
+                                   lane);
+      dma_narrow_codes(cs_w + ((P + 1) % 3) * (C::NW * 64), ctx, t + 4, lane);
+    }
+
+    // scores of this wave's 32 rows x 32 heads
+    f32x16 acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < C::KST; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qreg[ks], acc, 0, 0, 0);
+    // V^T fragments, read while the scores are finished and exponentiated:
+    // k-step ks2 covers rows 16ks2 + {4hi..4hi+3, 8+4hi..8+4hi+3}, the rows
+    // whose probabilities this lane holds
+    bf16x8 vfr[2][C::DVB];
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+      for (int d = 0; d < C::DVB; ++d) {
+        const int c = vc0 + d;
+        const uint16_t* vp0 = kb + narrow_slot(vrow + 16 * ks2, c) + vsub;
+        const uint16_t* vp1 = kb + narrow_slot(vrow + 16 * ks2 + 8, c) + vsub;
+        const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp0));
+        const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp1));
+        vfr[ks2][d] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    // register i holds tile row 32h + 8(i/4) + 4hi + i%4 of head lane%32;
+    // dead rows (pads, positions past the window) only in a tile whose live
+    // mask says so (wave-uniform test)
+    const uint32_t lvh = static_cast<uint32_t>(live_cur >> (32 * h));
+    float sc[16];
+    if (lvh == 0xFFFFFFFFu) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[i] = acc[i];
+    } else {
+      const uint32_t lv = lvh >> (4 * hi_half);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[i] = (lv >> (8 * (i / 4) + i % 4)) & 1u ? acc[i] : -INFINITY;
+    }
+    // the scale is positive, so the lane's largest scaled score is its
+    // largest raw score times the scale (rounding is monotone)
+    float mx = sc[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
+    if (__builtin_amdgcn_ballot_w64(mx * sl2 > m_run + kRescaleLog2) != 0) {
+      // a score exceeds its head's running max by more than 2^8: raise the
+      // max of that head (both lanes of the pair take the pair's tile max)
+      const float mq = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
+      if (mq > m_run + kRescaleLog2) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run - mq);
+        l_run *= alpha;
+        m_run = mq;
+#pragma unroll
+        for (int d = 0; d < C::DVB; ++d)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) O[d][i] *= alpha;
+      }
+    }
+    float ps = 0.f;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], sl2, -m_run));
+      ps += p;
+      pb[i / 8][i % 8] = static_cast<__bf16>(p);
+    }
+    l_run += ps;
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+      for (int d = 0; d < C::DVB; ++d) O[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[ks2][d], pb[ks2], O[d], 0, 0, 0);
+    live_cur = live_n1;
+    live_n1 = live_n2;
+    // tile t+1 and the codes of t+3 landed in every wave (the NVM
+    // instructions of this tile stay in flight); this tile's readers done
+    lds_vm_barrier<C::NVM>();
+  };
+  for (int t = tb; t < te; t += 3) {
+    tile(t, std::integral_constant<int, 0>{});
+    if (t + 1 < te) tile(t + 1, std::integral_constant<int, 1>{});
+    if (t + 2 < te) tile(t + 2, std::integral_constant<int, 2>{});
+  }
+  // no DMA outlives the loop, in any wave, before the tile buffers take the merge
+  __builtin_amdgcn_s_waitcnt(0x0070);              // vmcnt(0)
+  __syncthreads();
+
+  // merge the halves: half 1 hands (m, l, O) to half 0 through LDS
+  const float l2 = l_run + __shfl_xor(l_run, 32, 64);
+  if (h == 1 && lane < 32) {
+    Mm[hb * 32 + lane] = m_run;
+    Ml[hb * 32 + lane] = l2;
+  }
+  float m_tot = m_run, l_tot = l2, a0 = 1.f, a1 = 0.f;
+#pragma unroll
+  for (int ph = 0; ph < C::DVB / C::DPH; ++ph) {
+    if (h == 1) {
+#pragma unroll
+      for (int dd = 0; dd < C::DPH; ++dd)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) Om[((hb * C::DPH + dd) * 16 + i) * 64 + lane] = O[ph * C::DPH + dd][i];
+    }
+    __syncthreads();
+    if (h == 0) {
+      if (ph == 0) {
+        const float m1 = Mm[hb * 32 + (lane & 31)], l1 = Ml[hb * 32 + (lane & 31)];
+        m_tot = fmaxf(m_run, m1);
+        a0 = __builtin_amdgcn_exp2f(m_run - m_tot);
+        a1 = __builtin_amdgcn_exp2f(m1 - m_tot);
+        l_tot = l2 * a0 + l1 * a1;
+      }
+#pragma unroll
+      for (int dd = 0; dd < C::DPH; ++dd)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          O[ph * C::DPH + dd][i] = O[ph * C::DPH + dd][i] * a0 + Om[((hb * C::DPH + dd) * 16 + i) * 64 + lane] * a1;
+    }
+    __syncthreads();
+  }
+  if (h != 0) return;
+
+  // O^T register i of block d holds value dim (i/4)*8*DVB + d*8 + hi*4 + i%4
+  if (a.splits == 1) {
+    if (head < a.H) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      uint16_t* op = a.out + (size_t(qi) * a.H + head) * C::D_V + hi_half * 4;
+#pragma unroll
+      for (int d = 0; d < C::DVB; ++d)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          uint16_t h4[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            h4[e] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(O[d][g4 * 4 + e] * inv));
+          uint2 pk;
+          pk.x = uint32_t(h4[0]) | (uint32_t(h4[1]) << 16);
+          pk.y = uint32_t(h4[2]) | (uint32_t(h4[3]) << 16);
+          *reinterpret_cast<uint2*>(op + g4 * 8 * C::DVB + d * 8) = pk;
+        }
+    }
+  } else {
+    float* po = a.part_o + (blk * 32 * C::HB + hl) * C::D_V + hi_half * 4;
+#pragma unroll
+    for (int d = 0; d < C::DVB; ++d)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *reinterpret_cast<float4*>(po + g4 * 8 * C::DVB + d * 8) =
+            make_float4(O[d][g4 * 4 + 0], O[d][g4 * 4 + 1], O[d][g4 * 4 + 2], O[d][g4 * 4 + 3]);
+    if (hi_half == 0) {
+      float* pm = a.part_ml + (blk * 32 * C::HB + hl) * 2;
+      pm[0] = m_tot;
+      pm[1] = l_tot;
+    }
+  }
+}
+
 // Merge of key splits: out = sum_s 2^(m_s-m) O_s / sum_s 2^(m_s-m) l_s, the
 // sums in split order.  One 256-thread block per (query, head group, 8 heads):
 // 32 threads per head, each over float4 groups of value dims 128g + 4(t mod
@@ -715,6 +1081,12 @@ hipError_t set_lds_limit() {
                              hipFuncAttributeMaxDynamicSharedMemorySize, int(C::LDS));
 }
 
+template <class C>
+hipError_t set_narrow_lds_limit() {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(attn_narrow_kernel<C>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, int(C::LDS));
+}
+
 // Events, when given, are bound to the launch (they complete with it and time
 // its own start and end); with nothing to launch they are recorded in place.
 hipError_t no_launch(hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
@@ -743,6 +1115,15 @@ hipError_t launch_cfg(const AttnArgs& a, hipStream_t s, hipEvent_t ev_start, hip
   return launch_with(attn_kernel<C>, dim3(unsigned(blocks)), dim3(C::NT), C::LDS, s, ev_start, ev_stop, a);
 }
 
+template <class C>
+hipError_t launch_narrow(const AttnArgs& a, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
+  const int nreq = a.r1 - a.r0;
+  if (nreq <= 0) return no_launch(s, ev_start, ev_stop);
+  const int per_req = a.Q * a.head_groups * a.splits;
+  const long long blocks = (long long)((nreq + 7) / 8) * 8 * per_req;
+  return launch_with(attn_narrow_kernel<C>, dim3(unsigned(blocks)), dim3(C::NT), C::LDS, s, ev_start, ev_stop, a);
+}
+
 }  // namespace
 
 hipError_t attn_init_attributes() {
@@ -751,7 +1132,8 @@ hipError_t attn_init_attributes() {
   if (e == hipSuccess) e = set_lds_limit<Cfg<128, 128, 128, 256, 1>>();
   if (e == hipSuccess) e = set_lds_limit<Cfg<128, 128, 128, 256, 2>>();
   if (e == hipSuccess) e = set_lds_limit<Cfg<144, 0, 128, 144, 1>>();
-  if (e == hipSuccess) e = set_lds_limit<Cfg<144, 0, 128, 144, 2>>();
+    if (e == hipSuccess) e = set_narrow_lds_limit<NCfg<144, 0, 128, 144, 4>>();
+  if (e == hipSuccess) e = set_narrow_lds_limit<NCfg<144, 0, 128, 144, 2>>();
   return e;
 }
 
@@ -761,11 +1143,23 @@ bool attn_layout_supported(int row_elems, int d_qk, int v_off, int d_v) {
          (row_elems == 144 && d_qk == 144 && v_off == 0 && d_v == 128);
 }
 
-int attn_heads_per_wg(int H) { return H <= 32 ? 32 : 64; }
+// Heads of one workgroup: one 32-head block up to 32 heads, else two; rows of
+// 144 elements take four blocks (two waves each) above 64 heads, so that each
+// query's rows are gathered once.
+// Heads of one workgroup: one 32-head block up to 32 heads, else two.  Rows
+// of 144 elements above 64 heads take the narrow-row kernel with four blocks
+// (each query's rows gathered once) when the launch still has at least 256
+// workgroups; with fewer, two blocks per workgroup keep every CU busy (the
+// 128-head workgroup is one per CU and would leave CUs idle).
+int attn_heads_per_wg(int H, int row_elems, int64_t queries) {
+  if (H <= 32) return 32;
+  if (row_elems == 144 && H > 64 && queries * ((H + 127) / 128) >= 256) return 128;
+  return 64;
+}
 
 hipError_t launch_attn(const AttnArgs& a, int row_elems, int d_qk, int v_off, int d_v, hipStream_t s,
                        hipEvent_t ev_start, hipEvent_t ev_stop) {
-  const int hpw = attn_heads_per_wg(a.H);
+  const int hpw = a.hpw;
   if (row_elems == 576 && d_qk == 576 && v_off == 0 && d_v == 512) {
     if (hpw == 32) return launch_cfg<Cfg<576, 0, 512, 576, 1>>(a, s, ev_start, ev_stop);
     return launch_cfg<Cfg<576, 0, 512, 576, 2>>(a, s, ev_start, ev_stop);
@@ -776,7 +1170,8 @@ hipError_t launch_attn(const AttnArgs& a, int row_elems, int d_qk, int v_off, in
   }
   if (row_elems == 144 && d_qk == 144 && v_off == 0 && d_v == 128) {
     if (hpw == 32) return launch_cfg<Cfg<144, 0, 128, 144, 1>>(a, s, ev_start, ev_stop);
-    return launch_cfg<Cfg<144, 0, 128, 144, 2>>(a, s, ev_start, ev_stop);
+    if (hpw == 128) return launch_narrow<NCfg<144, 0, 128, 144, 4>>(a, s, ev_start, ev_stop);
+    return launch_narrow<NCfg<144, 0, 128, 144, 2>>(a, s, ev_start, ev_stop);
   }
   return hipErrorInvalidValue;
 }
@@ -784,7 +1179,7 @@ hipError_t launch_attn(const AttnArgs& a, int row_elems, int d_qk, int v_off, in
 hipError_t launch_attn_combine(const AttnArgs& a, int d_v, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
   const int nreq = a.r1 - a.r0;
   if (nreq <= 0 || a.splits <= 1) return no_launch(s, ev_start, ev_stop);
-  const int hpw = attn_heads_per_wg(a.H);
+  const int hpw = a.hpw;
   const dim3 grid(unsigned(((nreq + 7) / 8) * 8 * a.Q * a.head_groups * (hpw / 8)));
   if (d_v == 512) {
     if (hpw == 32) return launch_with(combine_kernel<512, 1>, grid, dim3(256), 0, s, ev_start, ev_stop, a);
@@ -792,6 +1187,7 @@ hipError_t launch_attn_combine(const AttnArgs& a, int d_v, hipStream_t s, hipEve
   }
   if (d_v == 128) {
     if (hpw == 32) return launch_with(combine_kernel<128, 1>, grid, dim3(256), 0, s, ev_start, ev_stop, a);
+    if (hpw == 128) return launch_with(combine_kernel<128, 4>, grid, dim3(256), 0, s, ev_start, ev_stop, a);
     return launch_with(combine_kernel<128, 2>, grid, dim3(256), 0, s, ev_start, ev_stop, a);
   }
   return hipErrorInvalidValue;

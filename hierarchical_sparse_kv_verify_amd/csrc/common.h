@@ -134,11 +134,13 @@ struct AttnArgs {
   int N, Q, k, H, W, Rd, block_only;
   int r0, r1;                 // request range of this launch
   int splits, head_groups;
+  int hpw;                    // heads per workgroup of this launch: 32, 64 or 128 (attn_heads_per_wg)
   float scale_log2;           // softmax scale * log2(e)
 };
 // supported layouts; returns hipErrorInvalidValue for others
 bool attn_layout_supported(int row_elems, int d_qk, int v_off, int d_v);
-int attn_heads_per_wg(int H);
+// heads per attention workgroup for a launch over `queries` queries
+int attn_heads_per_wg(int H, int row_elems, int64_t queries);
 // ev_start / ev_stop as for launch_miss_gather
 hipError_t launch_attn(const AttnArgs& a, int row_elems, int d_qk, int v_off, int d_v, hipStream_t s,
                        hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);

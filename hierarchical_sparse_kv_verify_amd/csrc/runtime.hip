@@ -175,12 +175,13 @@ struct kv_hier {
   float* part_o = nullptr;
   uint16_t* zero_row = nullptr;   // one all-zero row: target of masked attention reads
   float* part_ml = nullptr;
-  size_t step_part_blocks = 0;      // split-key partial blocks of the largest chunk launch of a step
+  size_t step_part_heads = 0;       // split-key partial slots (blocks x heads per block) of the largest chunk launch of a step
   unsigned char* scratch_dev = nullptr;   // this device's copy of the static scratch array
   bool no_alloc_call = false;       // inside kv_hier_verify_step_static: take no events, allocate nothing
-  int splits = 1, head_groups = 1, n_chunks = 1;   // splits: the largest of chunk_splits
-  int all_splits = 1;               // key splits of one launch over every request (Reuse layers)
-  std::vector<int> chunk_lo, chunk_splits;
+  int splits = 1, head_groups = 1, n_chunks = 1;   // the largest of chunk_splits / of the chunks' head groups
+  // key splits and heads per workgroup of one launch over every request (Reuse layers)
+  int all_splits = 1, all_hpw = 64;
+  std::vector<int> chunk_lo, chunk_splits, chunk_hpw;
   int chunk_words = 0, sort_cap = 1;
   size_t plan_lds = 0;
   hipStream_t side = nullptr;       // host fetch
@@ -795,7 +796,8 @@ static int create_impl(kv_hier* h) {
   // (nothing overlaps it); below a full wave a chunk needs key splits and a
   // merge, which cost more than the shorter tail saves.
   if (c.n_chunks == 0 && N >= 64) {
-    const int64_t hgroups = (c.n_heads + attn_heads_per_wg(c.n_heads) - 1) / attn_heads_per_wg(c.n_heads);
+    const int hpw = attn_heads_per_wg(c.n_heads, c.row_elems, int64_t(N / 8) * c.q_max);
+    const int64_t hgroups = (c.n_heads + hpw - 1) / hpw;
     const bool halve = int64_t(N / 8) * c.q_max * hgroups >= 256;
     const std::vector<int> eighths = halve ? std::vector<int>{0, 2, 4, 6, 7, 8} : std::vector<int>{0, 2, 4, 6, 8};
     for (int x : eighths) h->chunk_lo.push_back(int(int64_t(N) * x / 8));
@@ -805,35 +807,42 @@ static int create_impl(kv_hier* h) {
   }
   h->n_chunks = int(h->chunk_lo.size()) - 1;
   {
-    // key splits per chunk: about 256 workgroups per launch (the combine pass
-    // merges the splits); partials are indexed from the chunk's first request
-    const int hpw = attn_heads_per_wg(c.n_heads);
-    h->head_groups = (c.n_heads + hpw - 1) / hpw;
+    // heads per workgroup and key splits per launch: about 256 workgroups
+    // per launch (the combine pass merges the splits); partials are indexed
+    // from the launch's first request, 32*HB heads per block
     const int tiles = (c.topk + c.ring_window + 31) / 32;
-    size_t blocks = 0;
+    size_t slots = 0;
     h->splits = 1;
+    h->head_groups = 1;
     auto split_for = [&](int64_t wgs) {
       int s = wgs < 256 ? int(std::min<int64_t>(8, std::max<int64_t>(1, 256 / std::max<int64_t>(1, wgs)))) : 1;
       return std::max(1, std::min(s, tiles / 4));
     };
     for (int ch = 0; ch < h->n_chunks; ++ch) {
-      const int64_t wgs = int64_t(h->chunk_lo[ch + 1] - h->chunk_lo[ch]) * c.q_max * h->head_groups;
+      const int64_t queries = int64_t(h->chunk_lo[ch + 1] - h->chunk_lo[ch]) * c.q_max;
+      const int hpw = attn_heads_per_wg(c.n_heads, c.row_elems, queries);
+      const int hg = (c.n_heads + hpw - 1) / hpw;
+      const int64_t wgs = queries * hg;
       const int s = split_for(wgs);
       h->chunk_splits.push_back(s);
+      h->chunk_hpw.push_back(hpw);
       h->splits = std::max(h->splits, s);
-      if (s > 1) blocks = std::max(blocks, size_t(wgs) * s);
+      h->head_groups = std::max(h->head_groups, hg);
+      if (s > 1) slots = std::max(slots, size_t(wgs) * s * hpw);
     }
-    h->step_part_blocks = blocks;
+    h->step_part_heads = slots;
     {
       // a Reuse layer has no fetch to overlap: one launch over every request
-      const int64_t wgs = int64_t(N) * c.q_max * h->head_groups;
+      const int64_t queries = int64_t(N) * c.q_max;
+      h->all_hpw = attn_heads_per_wg(c.n_heads, c.row_elems, queries);
+      const int64_t wgs = queries * ((c.n_heads + h->all_hpw - 1) / h->all_hpw);
       h->all_splits = split_for(wgs);
       h->splits = std::max(h->splits, h->all_splits);
-      if (h->all_splits > 1) blocks = std::max(blocks, size_t(wgs) * h->all_splits);
+      if (h->all_splits > 1) slots = std::max(slots, size_t(wgs) * h->all_splits * h->all_hpw);
     }
-    if (blocks > 0) {
-      rc = dev_alloc(h, &h->part_o, blocks * hpw * c.d_v, &h->bytes_maps);
-      if (!rc) rc = dev_alloc(h, &h->part_ml, blocks * hpw * 2, &h->bytes_maps);
+    if (slots > 0) {
+      rc = dev_alloc(h, &h->part_o, slots * c.d_v, &h->bytes_maps);
+      if (!rc) rc = dev_alloc(h, &h->part_ml, slots * 2, &h->bytes_maps);
       if (rc) return rc;
     }
   }
@@ -1056,6 +1065,7 @@ int kv_hier_info_get(kv_hier_t* h, kv_hier_info* out) {
   out->bytes_host = h->bytes_host;
   out->attn_splits = h->splits;
   out->attn_head_groups = h->head_groups;
+  out->attn_reuse_head_groups = (h->cfg.n_heads + h->all_hpw - 1) / h->all_hpw;
   out->plan_rows_per_pass = h->chunk_words * 32;
   return KV_OK;
 }
@@ -1420,7 +1430,7 @@ static int verify_step_impl(kv_hier_t* h, int g, const void* queries, const int3
   if (h->no_alloc_call) {
     // the same partials, in this device's static scratch (size checked before any work)
     at.part_o = reinterpret_cast<float*>(h->scratch_dev);
-    at.part_ml = at.part_o + h->step_part_blocks * size_t(attn_heads_per_wg(c.n_heads)) * c.d_v;
+    at.part_ml = at.part_o + h->step_part_heads * size_t(c.d_v);
   }
   at.N = N;
   at.Q = c.q_max;
@@ -1429,7 +1439,6 @@ static int verify_step_impl(kv_hier_t* h, int g, const void* queries, const int3
   at.W = c.ring_window;
   at.Rd = h->Rd;
   at.block_only = c.ring_block_only ? 1 : 0;
-  at.head_groups = h->head_groups;
   const float scale = c.softmax_scale > 0.f ? c.softmax_scale : 1.0f / std::sqrt(float(c.d_qk));
   at.scale_log2 = scale * 1.4426950408889634f;
   // The hot slots promoted by this group's previous step are complete before
@@ -1441,6 +1450,8 @@ static int verify_step_impl(kv_hier_t* h, int g, const void* queries, const int3
     at.r0 = h->chunk_lo[ch];
     at.r1 = h->chunk_lo[ch + 1];
     at.splits = h->chunk_splits[ch];
+    at.hpw = h->chunk_hpw[ch];
+    at.head_groups = (c.n_heads + at.hpw - 1) / at.hpw;
     // the leader's first chunk was fetched on this stream
     if (!(lead && ch == 0)) HIPCHK(h, hipStreamWaitEvent(s, h->ev_fetched[G.member][ch], 0));
     if ((rc = attend(h, g, at, s))) return rc;
@@ -1490,8 +1501,7 @@ int kv_hier_verify_step_static(kv_hier_t* h, int g, const void* queries, const i
   DeviceGuard dg(h);
   if (!h) return KV_EINVAL;
   if (int rc = refuse_if_broken(h)) return rc;
-  const size_t need = h->step_part_blocks * size_t(attn_heads_per_wg(h->cfg.n_heads)) *
-                      (size_t(h->cfg.d_v) + 2) * sizeof(float);
+  const size_t need = h->step_part_heads * (size_t(h->cfg.d_v) + 2) * sizeof(float);
   if (need > kStaticScratchBytes)
     return fail(h, KV_EINVAL,
                 "split-key partials of this handle's steps take %zu bytes, over the %zu-byte static scratch", need,
@@ -1543,7 +1553,6 @@ static int verify_reuse_impl(kv_hier_t* h, int g, const void* queries, const int
   at.W = c.ring_window;
   at.Rd = h->Rd;
   at.block_only = c.ring_block_only ? 1 : 0;
-  at.head_groups = h->head_groups;
   const float scale = c.softmax_scale > 0.f ? c.softmax_scale : 1.0f / std::sqrt(float(c.d_qk));
   at.scale_log2 = scale * 1.4426950408889634f;
   // the selection's ring rows, staged rows and lists are complete once its
@@ -1552,6 +1561,8 @@ static int verify_reuse_impl(kv_hier_t* h, int g, const void* queries, const int
   at.r0 = 0;
   at.r1 = c.n_req;
   at.splits = h->all_splits;
+  at.hpw = h->all_hpw;
+  at.head_groups = (c.n_heads + at.hpw - 1) / at.hpw;
   int rc2 = attend(h, g, at, s);
   if (rc2) return rc2;
   // the arena is released once this reader and the step's own readers and

@@ -199,11 +199,13 @@ typedef struct {
   int32_t n_chunks;
   int64_t bytes_hot, bytes_staging, bytes_ring, bytes_maps, bytes_resident, bytes_host;
   int32_t attn_splits;      /* the largest key split count of a chunk (1: none)          */
-  int32_t attn_head_groups; /* 64-head (or one 32-head) workgroups per query             */
+  int32_t attn_head_groups; /* attention workgroups per query of a request-chunk launch
+                               (the largest over the chunks): 32, 64 or 128 heads each   */
   int32_t plan_rows_per_pass; /* history rows the resolution's LDS row bitmap covers at once:
                                a longer history is resolved in ceil(n_r / this) passes
                                over row ranges (the q_max*topk location codes share the
                                bitmap's LDS)                                             */
+  int32_t attn_reuse_head_groups; /* the same for a launch over every request (Reuse)      */
 } kv_hier_info;
 
 /* Creates a handle ("Adaptive DHiSparse" §2.2 fixed-cache offloading and

@@ -158,16 +158,22 @@ def test_mla_two_groups_two_steps(n_chunks, fetch_cus):
     pair.lib.close()
 
 
-@pytest.mark.parametrize("n_heads,n_chunks", [(128, 2), (16, 1), (64, 3)])
-def test_288_byte_rows_two_groups_two_steps(n_heads, n_chunks):
+@pytest.mark.parametrize("n_heads,n_chunks,head_groups", [(128, 2, 2), (16, 1, 1), (64, 3, 1), (96, 2, 2),
+                                                          (256, 2, 4), (48, 1, 1)])
+def test_288_byte_rows_two_groups_two_steps(n_heads, n_chunks, head_groups):
     """Rows of 144 bf16 (288 B, the bytes per missed selection of the pages'
     DeepSeek configuration, Table 3): K = all 144 elements, V = the first 128.
-    The key width is no multiple of the four waves' 16-dim k-steps (the last
-    wave of a head block takes none) and a row's 18 chunks leave gather lanes
-    idle.  Two groups, two steps with a commit, key splits at this size."""
+    Up to 32 heads the four waves of a head block split the key width (nine
+    16-dim k-steps: the last wave takes none) and a row's 18 chunks leave
+    gather lanes idle; above, the narrow-row kernel takes 64 heads per
+    workgroup at this size (two head blocks x two row halves, the last block
+    partly masked at 48 and 96 heads), rows moved by DMA in the chunk-major
+    layout, pads and the ragged last tile masked.  Two groups, two steps with
+    a commit, key splits at this size."""
     w = _mla_small(row_elems=144, d_qk=144, v_off=0, d_v=128, n_heads=n_heads)
     pair = build_pair(w, lib_kw=dict(n_chunks=n_chunks))
     assert pair.lib.info["attn_splits"] > 1
+    assert pair.lib.info["attn_head_groups"] == head_groups, pair.lib.info
     n = pair.hist_len.copy()
     for step in range(2):
         sis = []

@@ -144,3 +144,26 @@ def test_reuse_on_follower_layers():
         _check_reuse(pair, g, make_step_inputs(w, g, 9, pair.hist_len).queries, sis[g].causal_pos,
                      "reuse g%d" % g)
     pair.lib.close()
+
+
+@pytest.mark.parametrize("n_heads", [128, 96])
+def test_rows288_128_head_workgroups_step_and_reuse(n_heads):
+    """Launches of at least 256 workgroups over 288-B rows take one workgroup
+    of 128 heads per query (four head blocks x two row halves, each row
+    gathered once; 96 heads leave the last block masked): 32 requests x 8
+    queries as one request chunk, a resolving step and a Reuse layer over its
+    selection, against the oracle; pads, invalid entries and ragged tiles."""
+    w = _mla_small(n_req=32, n_groups=1, row_elems=144, d_qk=144, v_off=0, d_v=128, n_heads=n_heads,
+                   hist_lo=1500, hist_hi=2000, hist_cap=2100, prefix_len=1024, topk=256, hot_slots=512,
+                   ring_window=48)
+    pair = build_pair(w, lib_kw=dict(n_chunks=1))
+    info = pair.lib.info
+    assert info["attn_head_groups"] == 1 and info["attn_reuse_head_groups"] == 1, info
+    assert info["attn_splits"] == 1, info
+    si = make_step_inputs(w, 0, 0, pair.hist_len)
+    res = pair.orc.verify_step(0, si.topk, si.causal_pos, si.queries, si.block_rows, n_threads=8)
+    out = _resolve(pair, 0, si.queries, si.topk, si.causal_pos, si.block_rows)
+    compare_step(pair, 0, si, res, out)
+    compare_counts(pair, 0, res)
+    _check_reuse(pair, 0, make_step_inputs(w, 0, 1, pair.hist_len).queries, si.causal_pos, "reuse 128-head")
+    pair.lib.close()
