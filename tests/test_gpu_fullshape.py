@@ -96,3 +96,29 @@ def test_full_size_mla512_sampled():
     assert last["overflow"] > last["promoted"]
     assert 0.3 < last["union_miss"] / last["union_rows"] < 0.45
     pair.lib.close()
+
+
+@pytest.mark.timeout(600)
+def test_full_size_ds_shared_select_and_reuse_sampled():
+    """The shared-source measurement's shape: 128 requests x ~100K rows of 288 B
+    (one prefix), 128 heads, Q = 4, k = 512, B = 2048, W = 64.  A selecting
+    layer over four 32-request chunks (64 heads per attention workgroup, 256
+    workgroups per chunk) and a Reuse layer over all 128 requests (128 heads
+    per workgroup, each row gathered once per query), sampled requests of
+    every chunk against the oracle."""
+    from tests.pair import assert_close
+    from tests.test_gpu_reuse import _reuse
+    w = shrink(WORKLOADS["ds_shared"], n_groups=1, n_arenas=1)
+    reqs = [0, 40, 77, 101, 127]
+    pair = build_pair(w, oracle_requests=reqs)
+    info = pair.lib.info
+    _check_layout(pair, [0, 32, 64, 96, 128])
+    assert info["attn_splits"] == 1 and info["attn_head_groups"] == 2 and info["attn_reuse_head_groups"] == 1, info
+    si = make_step_inputs(w, 0, 0, pair.hist_len)
+    _check_group(pair, 0, si, reqs, (0, 3))
+    q = make_step_inputs(w, 0, 1, pair.hist_len).queries
+    ref = pair.orc.verify_reuse(0, q, attend={(r, j) for r in reqs for j in (0, 1, 3)}, n_threads=16)
+    got = _reuse(pair, 0, q, si.causal_pos)
+    for (r, j), v in ref.items():
+        assert_close(got[r, j], v, "ds_shared reuse r=%d j=%d" % (r, j))
+    pair.lib.close()
