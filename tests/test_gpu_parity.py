@@ -254,14 +254,21 @@ def test_mla_one_head_block_split_keys(n_heads):
     pair.lib.close()
 
 
-@pytest.mark.parametrize("topk,window", [(8, 8), (40, 16), (3, 64)])
-def test_mla_short_lists(topk, window):
-    """Absorbed-MLA rows with lists and windows that fill one partial tile, or
-    two with a ragged second one: the tile pipeline's first tiles are also its
-    last (DMA of tiles past the range reads the zero row)."""
-    w = _mla_small(n_req=3, n_groups=1, q_max=2, topk=topk, ring_window=window, ring_page=8,
-                   hot_slots=64, var_k=True)
-    pair = build_pair(w)
+@pytest.mark.parametrize("topk,window,rows,n_req", [(8, 8, 576, 3), (40, 16, 576, 3), (3, 64, 576, 3),
+                                                    (8, 8, 144, 3), (40, 16, 144, 3), (3, 64, 144, 3),
+                                                    (50, 20, 144, 32), (3, 64, 144, 32)])
+def test_mla_short_lists(topk, window, rows, n_req):
+    """Lists and windows that fill one partial tile, or two with a ragged
+    second one: the tile pipeline's first tiles are also its last (DMA of
+    tiles past the range reads the zero row).  Absorbed-MLA rows, and 288-B
+    rows at 128 heads (64-head workgroups with key splits at 3 requests;
+    128-head workgroups at 32 requests x 8 queries)."""
+    lay = {} if rows == 576 else dict(row_elems=144, d_qk=144, v_off=0, d_v=128, n_heads=128)
+    w = _mla_small(n_req=n_req, n_groups=1, q_max=2 if n_req == 3 else 8, topk=topk, ring_window=window,
+                   ring_page=8, hot_slots=64, var_k=True, **lay)
+    pair = build_pair(w, lib_kw=dict(n_chunks=1) if n_req == 32 else None)
+    if n_req == 32:
+        assert pair.lib.info["attn_head_groups"] == 1, pair.lib.info
     for step in range(2):
         si = make_step_inputs(w, 0, step, pair.hist_len)
         res = pair.orc.verify_step(0, si.topk, si.causal_pos, si.queries, si.block_rows, n_threads=8)
