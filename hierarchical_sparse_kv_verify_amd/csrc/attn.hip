@@ -653,10 +653,12 @@ __global__ __launch_bounds__(C::NT, 1) void attn_kernel(AttnArgs a) {
 // ---------------------------------------------------------------------------
 // Narrow rows (144 elements: K = all 144, V = the first 128) above 32 heads.
 // One workgroup = one query x HB 32-head blocks (2: 64 heads, or 4: 128
-// heads, each row then gathered once per query) x one key split.  2*HB waves
-// = HB head blocks x two row halves: wave (hb, h) takes rows 32h..32h+31 of every 64-row tile over the
-// whole key width (its heads' Q fragments stay in registers), so its scores
-// are complete in its own accumulators.  The softmax runs in registers (the
+// heads, each row then gathered once per query) x one key split.  A wave
+// takes one head block and RB of the two 32-row blocks of every 64-row tile
+// (RB = 1: two waves per head block, one per row half, 4 waves at 64 heads;
+// RB = 2: one wave per head block, 4 waves at 128 heads, two workgroups per
+// CU) over the whole key width (its heads' Q fragments stay in registers),
+// so its scores are complete in its own accumulators.  The softmax runs in registers (the
 // 32 rows of a head sit in lanes l and l+32) and the probabilities go from
 // the accumulators straight into the B operand of O^T = V^T P^T; the V^T
 // fragments are read in the same row order (rows 4hi..4hi+3 and 8+4hi..+3 of
@@ -664,14 +666,17 @@ __global__ __launch_bounds__(C::NT, 1) void attn_kernel(AttnArgs a) {
 // in a chunk-major layout: chunk c of tile row rho sits in 16-byte slot
 // c*64 + ((rho + c) & 63), so that the K reads (32 rows of one chunk) and the
 // transposed V reads (4 rows x 4 chunks per half-wave) hit every bank once.
-// One barrier per tile.  Each half keeps its own (m, l, O); half 1 hands them
-// to half 0 through LDS at the end.  Sum order depends only on list order and
-// split boundaries.
-template <int D_QK_, int V_OFF_, int D_V_, int ROW_, int HB_>
+// One barrier per tile.  With two waves per head block each half keeps its
+// own (m, l, O) and half 1 hands them to half 0 through LDS at the end.  Sum
+// order depends only on list order and split boundaries.
+template <int D_QK_, int V_OFF_, int D_V_, int ROW_, int HB_, int RB_>
 struct NCfg {
   static constexpr int D_QK = D_QK_, V_OFF = V_OFF_, D_V = D_V_, ROW = ROW_;
   static constexpr int HB = HB_;               // 32-head blocks
-  static constexpr int NW = 2 * HB;            // waves: head block w % HB, row half w / HB
+  static constexpr int RB = RB_;               // 32-row blocks of a tile per wave
+  static constexpr int NH = 2 / RB;            // waves per head block
+  static constexpr int NW = NH * HB;           // waves: head block w % HB, row half w / HB
+  static constexpr int MINB = RB == 2 ? 2 : 1; // workgroups per CU the registers are sized for
   static constexpr int NT = NW * 64;
   static constexpr int T = 64;                 // rows per tile
   static constexpr int KST = D_QK / 16;        // 16-dim k-steps over the key width
@@ -688,13 +693,14 @@ struct NCfg {
   // value blocks of O handed over per merge phase (16 registers x 64 lanes x
   // 4 B per block and head block, in the tile buffers)
   static constexpr int DPH = size_t(HB) * DVB * 4096 <= LDS_K ? DVB : (size_t(HB) * 2 * 4096 <= LDS_K ? 2 : 1);
-  static constexpr size_t LDS_ML = size_t(HB) * 32 * 2 * 4;
+  static constexpr size_t LDS_ML = NH > 1 ? size_t(HB) * 32 * 2 * 4 : 0;
   static constexpr size_t LDS = LDS_K + LDS_C + LDS_ML;
+  static_assert(RB == 1 || RB == 2, "row blocks");
   static_assert(D_QK % 16 == 0 && D_V % 32 == 0 && ROW % 8 == 0, "shape");
   static_assert(V_OFF % 8 == 0 && V_OFF + D_V <= ROW && D_QK <= ROW, "row layout");
   // the DMA split: chunk columns w, w+NW, .. below 16 per wave, columns 16
   // and 17 in shares of 64/(NW/2) rows
-  static_assert((NW == 8 || NW == 4) && RCH == 18, "DMA split");
+  static_assert((NW == 8 || NW == 4 || NW == 2) && RCH == 18, "DMA split");
   static_assert(DVB % DPH == 0, "merge");
   static_assert(LDS <= 160 * 1024, "LDS");
 };
@@ -735,7 +741,7 @@ __device__ __forceinline__ void dma_narrow_codes(int32_t* slot, const RowCtx& c,
 }
 
 template <class C>
-__global__ __launch_bounds__(C::NT, 1) void attn_narrow_kernel(AttnArgs a) {
+__global__ __launch_bounds__(C::NT, C::MINB) void attn_narrow_kernel(AttnArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
   uint16_t* Kb = reinterpret_cast<uint16_t*>(lds);
   float* Om = reinterpret_cast<float*>(lds);                     // merge area (tile buffers, after the loop)
@@ -831,13 +837,14 @@ __global__ __launch_bounds__(C::NT, 1) void attn_narrow_kernel(AttnArgs a) {
   dma_narrow_codes(cslot(tb + 3), ctx, tb + 3, lane);
   lds_vm_barrier<C::NVM>();
 
-  // per-lane parts of the LDS offsets: K fragment rows 32h + lane%32, chunk
-  // 2ks + hi; V^T rows 32h + 16ks2 + 4(gq/2) + s/4 (+8), chunks c0 + d
-  const int krow = 32 * h + (lane & 31);
+  // per-lane parts of the LDS offsets in row block b = h*RB + rb: K fragment
+  // rows 32b + lane%32, chunk 2ks + hi; V^T rows 32b + 16ks2 + 4(gq/2) + s/4
+  // (+8), chunks c0 + d
+  const int krow = lane & 31;
   int vrow, vc0, vsub;
   {
     const int gq = (lane >> 4) & 3, sl = lane & 15, aq = sl & 3;
-    vrow = 32 * h + (gq >> 1) * 4 + (sl >> 2);
+    vrow = (gq >> 1) * 4 + (sl >> 2);
     vc0 = C::V_OFF / 8 + ((gq & 1) * 2 + (aq >> 1)) * C::DVB;
     vsub = (aq & 1) * 4;
   }
@@ -850,10 +857,13 @@ __global__ __launch_bounds__(C::NT, 1) void attn_narrow_kernel(AttnArgs a) {
     // tile's K fragments: their LDS latency passes while the next DMA is
     // issued (LDS reads complete in order, so the codes come first)
     const int raw2 = (cs_w + ((P + 2) % 3) * (C::NW * 64))[lane];
+    auto kfrag = [&](int rb, int ks) {
+      return __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const uint4*>(kb + narrow_slot(32 * (h * C::RB + rb) + krow, 2 * ks + hi_half)));
+    };
     bf16x8 kf[C::KST];
 #pragma unroll
-    for (int ks = 0; ks < C::KST; ++ks)
-      kf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + narrow_slot(krow, 2 * ks + hi_half)));
+    for (int ks = 0; ks < C::KST; ++ks) kf[ks] = kfrag(0, ks);
     // DMA of tile t+2 into the buffer of tile t-1 (its readers passed the
     // last barrier) and of the codes of tile t+4 into the slot of t+1;
     // unconditional, so that every wave keeps NVM instructions per tile
@@ -864,45 +874,61 @@ __global__ __launch_bounds__(C::NT, 1) void attn_narrow_kernel(AttnArgs a) {
       dma_narrow_codes(cs_w + ((P + 1) % 3) * (C::NW * 64), ctx, t + 4, lane);
     }
 
-    // scores of this wave's 32 rows x 32 heads
-    f32x16 acc;
+    // scores of this wave's row blocks x 32 heads
+    // (the second block's K fragments replace the first's as they are used)
+    f32x16 acc[C::RB];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    for (int rb = 0; rb < C::RB; ++rb) {
 #pragma unroll
-    for (int ks = 0; ks < C::KST; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qreg[ks], acc, 0, 0, 0);
+      for (int i = 0; i < 16; ++i) acc[rb][i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < C::KST; ++ks) {
+        acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qreg[ks], acc[rb], 0, 0, 0);
+        if (rb + 1 < C::RB) kf[ks] = kfrag(rb + 1, ks);
+      }
+    }
     // V^T fragments, read while the scores are finished and exponentiated:
-    // k-step ks2 covers rows 16ks2 + {4hi..4hi+3, 8+4hi..8+4hi+3}, the rows
-    // whose probabilities this lane holds
+    // k-step ks2 covers rows 16ks2 + {4hi..4hi+3, 8+4hi..8+4hi+3} of the
+    // block, the rows whose probabilities this lane holds
+    auto vfrag = [&](int rb, int ks2, int d) {
+      const int c = vc0 + d;
+      const int row = 32 * (h * C::RB + rb) + vrow + 16 * ks2;
+      const uint16_t* vp0 = kb + narrow_slot(row, c) + vsub;
+      const uint16_t* vp1 = kb + narrow_slot(row + 8, c) + vsub;
+      const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp0));
+      const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp1));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
     bf16x8 vfr[2][C::DVB];
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2)
 #pragma unroll
-      for (int d = 0; d < C::DVB; ++d) {
-        const int c = vc0 + d;
-        const uint16_t* vp0 = kb + narrow_slot(vrow + 16 * ks2, c) + vsub;
-        const uint16_t* vp1 = kb + narrow_slot(vrow + 16 * ks2 + 8, c) + vsub;
-        const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp0));
-        const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp1));
-        vfr[ks2][d] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-    // register i holds tile row 32h + 8(i/4) + 4hi + i%4 of head lane%32;
-    // dead rows (pads, positions past the window) only in a tile whose live
-    // mask says so (wave-uniform test)
-    const uint32_t lvh = static_cast<uint32_t>(live_cur >> (32 * h));
-    float sc[16];
-    if (lvh == 0xFFFFFFFFu) {
+      for (int d = 0; d < C::DVB; ++d) vfr[ks2][d] = vfrag(0, ks2, d);
+    // register i of block b holds tile row 32b + 8(i/4) + 4hi + i%4 of head
+    // lane%32; dead rows (pads, positions past the window) only in a tile
+    // whose live mask says so (wave-uniform test)
+    const uint64_t lvw = C::RB == 2 ? live_cur : (live_cur >> (32 * h)) & 0xFFFFFFFFull;
+    float sc[C::RB][16];
+    if (lvw == (C::RB == 2 ? ~0ull : 0xFFFFFFFFull)) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sc[i] = acc[i];
+      for (int rb = 0; rb < C::RB; ++rb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[rb][i] = acc[rb][i];
     } else {
-      const uint32_t lv = lvh >> (4 * hi_half);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sc[i] = (lv >> (8 * (i / 4) + i % 4)) & 1u ? acc[i] : -INFINITY;
+      for (int rb = 0; rb < C::RB; ++rb) {
+        const uint32_t lv = static_cast<uint32_t>(lvw >> (32 * rb)) >> (4 * hi_half);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[rb][i] = (lv >> (8 * (i / 4) + i % 4)) & 1u ? acc[rb][i] : -INFINITY;
+      }
     }
     // the scale is positive, so the lane's largest scaled score is its
     // largest raw score times the scale (rounding is monotone)
-    float mx = sc[0];
+    float mx = sc[0][0];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
+    for (int rb = 0; rb < C::RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[rb][i]);
     if (__builtin_amdgcn_ballot_w64(mx * sl2 > m_run + kRescaleLog2) != 0) {
       // a score exceeds its head's running max by more than 2^8: raise the
       // max of that head (both lanes of the pair take the pair's tile max)
@@ -918,20 +944,28 @@ __global__ __launch_bounds__(C::NT, 1) void attn_narrow_kernel(AttnArgs a) {
       }
     }
     float ps = 0.f;
-    bf16x8 pb[2];
+    bf16x8 pb[C::RB][2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], sl2, -m_run));
-      ps += p;
-      pb[i / 8][i % 8] = static_cast<__bf16>(p);
-    }
+    for (int rb = 0; rb < C::RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[rb][i], sl2, -m_run));
+        ps += p;
+        pb[rb][i / 8][i % 8] = static_cast<__bf16>(p);
+      }
     l_run += ps;
 
-    // O^T += V^T P^T
+    // O^T += V^T P^T (the second block's V^T fragments replace the first's
+    // as they are used)
 #pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2)
+    for (int rb = 0; rb < C::RB; ++rb)
 #pragma unroll
-      for (int d = 0; d < C::DVB; ++d) O[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[ks2][d], pb[ks2], O[d], 0, 0, 0);
+      for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+        for (int d = 0; d < C::DVB; ++d) {
+          O[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[ks2][d], pb[rb][ks2], O[d], 0, 0, 0);
+          if (rb + 1 < C::RB) vfr[ks2][d] = vfrag(rb + 1, ks2, d);
+        }
     live_cur = live_n1;
     live_n1 = live_n2;
     // tile t+1 and the codes of t+3 landed in every wave (the NVM
@@ -945,41 +979,44 @@ __global__ __launch_bounds__(C::NT, 1) void attn_narrow_kernel(AttnArgs a) {
   }
   // no DMA outlives the loop, in any wave, before the tile buffers take the merge
   __builtin_amdgcn_s_waitcnt(0x0070);              // vmcnt(0)
-  __syncthreads();
+  if constexpr (C::NH == 2) __syncthreads();
 
-  // merge the halves: half 1 hands (m, l, O) to half 0 through LDS
   const float l2 = l_run + __shfl_xor(l_run, 32, 64);
-  if (h == 1 && lane < 32) {
-    Mm[hb * 32 + lane] = m_run;
-    Ml[hb * 32 + lane] = l2;
-  }
-  float m_tot = m_run, l_tot = l2, a0 = 1.f, a1 = 0.f;
-#pragma unroll
-  for (int ph = 0; ph < C::DVB / C::DPH; ++ph) {
-    if (h == 1) {
-#pragma unroll
-      for (int dd = 0; dd < C::DPH; ++dd)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) Om[((hb * C::DPH + dd) * 16 + i) * 64 + lane] = O[ph * C::DPH + dd][i];
+  float m_tot = m_run, l_tot = l2;
+  if constexpr (C::NH == 2) {
+    // merge the halves: half 1 hands (m, l, O) to half 0 through LDS
+    if (h == 1 && lane < 32) {
+      Mm[hb * 32 + lane] = m_run;
+      Ml[hb * 32 + lane] = l2;
     }
-    __syncthreads();
-    if (h == 0) {
-      if (ph == 0) {
-        const float m1 = Mm[hb * 32 + (lane & 31)], l1 = Ml[hb * 32 + (lane & 31)];
-        m_tot = fmaxf(m_run, m1);
-        a0 = __builtin_amdgcn_exp2f(m_run - m_tot);
-        a1 = __builtin_amdgcn_exp2f(m1 - m_tot);
-        l_tot = l2 * a0 + l1 * a1;
+    float a0 = 1.f, a1 = 0.f;
+#pragma unroll
+    for (int ph = 0; ph < C::DVB / C::DPH; ++ph) {
+      if (h == 1) {
+#pragma unroll
+        for (int dd = 0; dd < C::DPH; ++dd)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) Om[((hb * C::DPH + dd) * 16 + i) * 64 + lane] = O[ph * C::DPH + dd][i];
       }
+      __syncthreads();
+      if (h == 0) {
+        if (ph == 0) {
+          const float m1 = Mm[hb * 32 + (lane & 31)], l1 = Ml[hb * 32 + (lane & 31)];
+          m_tot = fmaxf(m_run, m1);
+          a0 = __builtin_amdgcn_exp2f(m_run - m_tot);
+          a1 = __builtin_amdgcn_exp2f(m1 - m_tot);
+          l_tot = l2 * a0 + l1 * a1;
+        }
 #pragma unroll
-      for (int dd = 0; dd < C::DPH; ++dd)
+        for (int dd = 0; dd < C::DPH; ++dd)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          O[ph * C::DPH + dd][i] = O[ph * C::DPH + dd][i] * a0 + Om[((hb * C::DPH + dd) * 16 + i) * 64 + lane] * a1;
+          for (int i = 0; i < 16; ++i)
+            O[ph * C::DPH + dd][i] = O[ph * C::DPH + dd][i] * a0 + Om[((hb * C::DPH + dd) * 16 + i) * 64 + lane] * a1;
+      }
+      __syncthreads();
     }
-    __syncthreads();
+    if (h != 0) return;
   }
-  if (h != 0) return;
 
   // O^T register i of block d holds value dim (i/4)*8*DVB + d*8 + hi*4 + i%4
   if (a.splits == 1) {
@@ -1132,8 +1169,8 @@ hipError_t attn_init_attributes() {
   if (e == hipSuccess) e = set_lds_limit<Cfg<128, 128, 128, 256, 1>>();
   if (e == hipSuccess) e = set_lds_limit<Cfg<128, 128, 128, 256, 2>>();
   if (e == hipSuccess) e = set_lds_limit<Cfg<144, 0, 128, 144, 1>>();
-    if (e == hipSuccess) e = set_narrow_lds_limit<NCfg<144, 0, 128, 144, 4>>();
-  if (e == hipSuccess) e = set_narrow_lds_limit<NCfg<144, 0, 128, 144, 2>>();
+  if (e == hipSuccess) e = set_narrow_lds_limit<NCfg<144, 0, 128, 144, 2, 1>>();
+  if (e == hipSuccess) e = set_narrow_lds_limit<NCfg<144, 0, 128, 144, 4, 2>>();
   return e;
 }
 
@@ -1170,8 +1207,8 @@ hipError_t launch_attn(const AttnArgs& a, int row_elems, int d_qk, int v_off, in
   }
   if (row_elems == 144 && d_qk == 144 && v_off == 0 && d_v == 128) {
     if (hpw == 32) return launch_cfg<Cfg<144, 0, 128, 144, 1>>(a, s, ev_start, ev_stop);
-    if (hpw == 128) return launch_narrow<NCfg<144, 0, 128, 144, 4>>(a, s, ev_start, ev_stop);
-    return launch_narrow<NCfg<144, 0, 128, 144, 2>>(a, s, ev_start, ev_stop);
+    if (hpw == 128) return launch_narrow<NCfg<144, 0, 128, 144, 4, 2>>(a, s, ev_start, ev_stop);
+    return launch_narrow<NCfg<144, 0, 128, 144, 2, 1>>(a, s, ev_start, ev_stop);
   }
   return hipErrorInvalidValue;
 }
