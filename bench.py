@@ -744,16 +744,17 @@ def measure_h2d(torch, mib=512, reps=3):
     return best
 
 
-def _counter_ratio(profile, key, source):
+def _counter_ratio(profile, key, sources):
     """A counter-measured bytes-per-algorithmic-byte ratio from a committed
-    rocprofv3 summary (its ``traffic:`` line), or None when the kernel's source
-    file changed since the counters were taken."""
+    rocprofv3 summary (its ``traffic:`` line), or None when a source file the
+    counted traffic depends on changed since the counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", profile)
-    src = os.path.join(ROOT, "hierarchical_sparse_kv_verify_amd", "csrc", source)
     try:
         text = open(path).read()
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        digests = {os.path.splitext(src)[0] + "_sha256": hashlib.sha256(
+            open(os.path.join(ROOT, "hierarchical_sparse_kv_verify_amd", "csrc", src), "rb").read()).hexdigest()
+            for src in sources}
     except OSError:
         return None
     vals = {}
@@ -762,8 +763,7 @@ def _counter_ratio(profile, key, source):
             for kv in ln[len("traffic:"):].split():
                 k, _, v = kv.partition("=")
                 vals[k] = v
-    tag = os.path.splitext(source)[0] + "_sha256"
-    if vals.get(tag) != digest or key not in vals:
+    if key not in vals or any(vals.get(tag) != d for tag, d in digests.items()):
         return None
     return float(vals[key])
 
@@ -771,14 +771,15 @@ def _counter_ratio(profile, key, source):
 def attn_traffic(algo_bytes_per_launch):
     """HBM bytes per attention launch of the default mla128 step: DRAM reads +
     writes from the TCC counters (profiles/sparse_attn_mla128_traffic.md)."""
-    r = _counter_ratio("sparse_attn_mla128_traffic.md", "bytes_per_algo_byte", "attn.hip")
+    # the walk order of the lists (the order kernel) sets how much the L2 serves
+    r = _counter_ratio("sparse_attn_mla128_traffic.md", "bytes_per_algo_byte", ("attn.hip", "plan.hip"))
     return None if r is None else round(r * algo_bytes_per_launch, 1)
 
 
 def link_traffic(algo_bytes_per_launch):
     """Host-link bytes per fetch launch of the default mla128 step: the TCC IO
     read counter (profiles/miss_gather_mla128_host_link.md)."""
-    r = _counter_ratio("miss_gather_mla128_host_link.md", "io_bytes_per_algo_byte", "copy.hip")
+    r = _counter_ratio("miss_gather_mla128_host_link.md", "io_bytes_per_algo_byte", ("copy.hip",))
     return None if r is None else round(r * algo_bytes_per_launch, 1)
 
 

@@ -70,7 +70,8 @@ class Counters(ctypes.Structure):
     _fields_ = ([(n, ctypes.c_int64) for n in COUNTER_FIELDS] +
                 [(n, ctypes.c_double) for n in TIMING_FIELDS] +
                 [(n, ctypes.c_int64) for n in TIMING_COUNTS] +
-                [(n, ctypes.c_int64) for n in TAIL_FIELDS])
+                [(n, ctypes.c_int64) for n in TAIL_FIELDS] +
+                [("ms_order", ctypes.c_double), ("n_order", ctypes.c_int64)])
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -90,7 +91,8 @@ class Info(ctypes.Structure):
                [(n, ctypes.c_int64) for n in ("bytes_hot", "bytes_staging", "bytes_ring", "bytes_maps",
                                               "bytes_resident", "bytes_host")] + \
                [("attn_splits", ctypes.c_int32), ("attn_head_groups", ctypes.c_int32),
-                ("plan_rows_per_pass", ctypes.c_int32), ("attn_reuse_head_groups", ctypes.c_int32)]
+                ("plan_rows_per_pass", ctypes.c_int32), ("attn_reuse_head_groups", ctypes.c_int32),
+                ("attn_row_order", ctypes.c_int32)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

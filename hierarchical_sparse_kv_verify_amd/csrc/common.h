@@ -41,6 +41,10 @@ struct PlanArgs {
   int32_t* victims;          // [N][Q*k]
   uint32_t* protect;         // [N][ceil(B/32)] slots holding a selected row (resolve -> victims)
   int32_t* loc;              // [N][Q][k]
+  // [N][Q][k] the same codes with each query's valid entries in ascending row
+  // order, then -1 (a query with a repeated row keeps its selection order;
+  // written by the order kernel)
+  int32_t* sloc;
   int32_t* req_info;         // [N][I_NUM]
   int64_t* req_counts;       // [N][C_NUM] last step
   unsigned long long* cum;   // [C_NUM] cumulative
@@ -58,6 +62,8 @@ struct PlanArgs {
   int row16;
 };
 size_t plan_lds_bytes(int Q, int k, int B, int chunk_words, int sort_cap);
+// LDS of the order kernel (row-ordered lists)
+size_t plan_order_lds_bytes(int Q, int k, int chunk_words);
 // union, probe, staging positions, locations (everything the fetch needs);
 // ev_start / ev_stop as for launch_miss_gather
 hipError_t launch_plan(const PlanArgs& a, size_t lds, hipStream_t s, hipEvent_t ev_start = nullptr,
@@ -67,6 +73,10 @@ hipError_t plan_init_attributes();
 hipError_t attn_init_attributes();
 // LRU victims, promotions and slot-table updates (after launch_plan)
 hipError_t launch_plan_victims(const PlanArgs& a, size_t lds, hipStream_t s);
+// each query's location codes in ascending row order (a.sloc), after the
+// plan; ev_start / ev_stop as for launch_plan
+hipError_t launch_plan_order(const PlanArgs& a, size_t lds, hipStream_t s, hipEvent_t ev_start = nullptr,
+                             hipEvent_t ev_stop = nullptr);
 
 // ---------------------------------------------------------------- copies
 struct HostRowSrc {

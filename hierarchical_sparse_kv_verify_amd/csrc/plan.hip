@@ -21,10 +21,15 @@
 // LRU victims run in a second kernel, off the path to the host fetch (the
 // fetch needs only the missing rows): the unselected slots' (last_used, slot)
 // keys are compacted in LDS and bitonic-sorted; keys are unique, so the order
-// is deterministic.
+// is deterministic.  A third kernel, beside the first fetch, writes each
+// query's location codes in ascending row order (the order the attention
+// walks, so that a request's queries meet their shared rows close together in
+// time and re-read them from the L2).
 #include "common.h"
 
 #include <hip/hip_ext.h>
+
+#include <algorithm>
 
 namespace kvh {
 namespace {
@@ -424,7 +429,167 @@ __global__ __launch_bounds__(kThreads) void plan_victims_kernel(PlanArgs a) {
   }
 }
 
+// Row order of every query's list: the valid entries' location codes sorted
+// by row id, then -1; a query that repeats a row keeps its selection order
+// (each repeat is its own term, and distinct rows alone would drop it).  One
+// 1024-thread workgroup per request.  Per row chunk (as in the resolution):
+// the union bitmap and its word prefix table give each entry's rank in the
+// union; each query marks its ranks in a bitmap of its own, whose prefix
+// table places its rows; the codes (the union's, in rank order) go to an LDS
+// staging copy of the request's lists, written out once, coalesced.
+__global__ __launch_bounds__(kThreads) void plan_order_kernel(PlanArgs a) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int Q = a.Q, k = a.k, QK = Q * k, L = a.L;
+  const int CW = a.chunk_words, CB = CW * 32;
+  const int QW = (min(QK, CB) + 31) / 32;
+
+  uint32_t* bitmap = reinterpret_cast<uint32_t*>(lds);
+  uint16_t* wpre = reinterpret_cast<uint16_t*>(lds + align16(size_t(CW) * 4));
+  int32_t* stage = reinterpret_cast<int32_t*>(lds + align16(size_t(CW) * 4) + align16(size_t(CW) * 2));
+  unsigned char* q0 = lds + region_a_bytes(QK, CW);
+  uint32_t* qbits = reinterpret_cast<uint32_t*>(q0);
+  uint16_t* qpre = reinterpret_cast<uint16_t*>(q0 + align16(size_t(Q) * QW * 4));
+  int* qbase = reinterpret_cast<int*>(q0 + align16(size_t(Q) * QW * 4) + align16(size_t(Q) * QW * 2));
+  int* qcnt = qbase + Q;            // entries of the current chunk
+  int* qflag = qcnt + Q;            // 1: the query repeats a row
+  int* scratch = qflag + Q;         // block scan (kWaves + 1)
+
+  const int32_t* cp = a.causal + size_t(r) * Q;
+  const int32_t* tk = a.topk + size_t(r) * QK;
+  const int32_t* loc = a.loc + size_t(r) * QK;
+  const int32_t* uloc = a.union_loc + size_t(r) * QK;
+  int32_t* sloc = a.sloc + size_t(r) * QK;
+  const int n_raw = cp[0];
+  if (n_raw < 0) {  // inactive request
+    for (int i = tid; i < QK; i += kThreads) sloc[i] = -1;
+    return;
+  }
+  const int n_src = n_raw / a.m;
+  const int n_r = n_src < L ? n_src : L;
+  uint32_t amask = 0;
+  for (int j = 0; j < Q; ++j) amask |= (cp[j] >= 0 ? 1u : 0u) << j;
+  const bool held = QK <= kBatch * kThreads;
+  int hv[kBatch];
+  if (held) {
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int i = tid + b * kThreads;
+      hv[b] = i < QK ? tk[i] : -1;
+    }
+  }
+  if (tid < Q) qbase[tid] = qflag[tid] = 0;
+  const int WPT = (CW + kThreads - 1) / kThreads;
+  int union_base = 0;
+  for (int c0 = 0; c0 < n_r; c0 += CB) {
+    const int c1 = min(c0 + CB, n_r);
+    for (int w = tid; w < CW; w += kThreads) bitmap[w] = 0;
+    if (tid < Q) qcnt[tid] = 0;
+    __syncthreads();
+    // the chunk's union: one bit per selected row
+    for (int i0 = tid; i0 < QK; i0 += kBatch * kThreads) {
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const int i = i0 + b * kThreads;
+        if (i >= QK || !((amask >> (i / k)) & 1u)) continue;
+        const int e = held ? hv[b] : tk[i];
+        if (e >= c0 && e < c1) atomicOr(&bitmap[(e - c0) >> 5], 1u << ((e - c0) & 31));
+      }
+    }
+    __syncthreads();
+    // word prefix table: the rank of a row in the chunk's union
+    const int wb = tid * WPT, we = min(wb + WPT, CW);
+    int mine = 0;
+    for (int w = wb; w < we; ++w) mine += __popc(bitmap[w]);
+    int chunk_union;
+    int run = block_exclusive_scan(mine, scratch, &chunk_union);
+    for (int w = wb; w < we; ++w) {
+      wpre[w] = static_cast<uint16_t>(run);
+      run += __popc(bitmap[w]);
+    }
+    const int qw = (chunk_union + 31) / 32;
+    for (int x = tid; x < Q * qw; x += kThreads) qbits[(x / qw) * QW + x % qw] = 0;
+    __syncthreads();
+    // each query's ranks, and its entries in the chunk (one ballot per wave
+    // and batch when the wave's entries belong to one query)
+    for (int i0 = tid; i0 < QK; i0 += kBatch * kThreads) {
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const int i = i0 + b * kThreads;
+        if (i >= QK) continue;
+        const int j = i / k;
+        const int e = held ? hv[b] : tk[i];
+        const bool in = ((amask >> j) & 1u) && e >= c0 && e < c1;
+        if (in) {
+          const int o = e - c0, w = o >> 5;
+          const int rank = wpre[w] + __popc(bitmap[w] & ((1u << (o & 31)) - 1u));
+          atomicOr(&qbits[j * QW + (rank >> 5)], 1u << (rank & 31));
+        }
+        const int i_w = i - lane;
+        const int j0 = i_w / k, j1 = min(i_w + 63, QK - 1) / k;
+        if (j0 == j1) {
+          const int n = __popcll(__builtin_amdgcn_ballot_w64(in));
+          if (lane == 0 && n) atomicAdd(&qcnt[j0], n);
+        } else if (in) {
+          atomicAdd(&qcnt[j], 1);
+        }
+      }
+    }
+    __syncthreads();
+    // each query's word prefix table (one wave per query); more entries than
+    // distinct rows: a repeated row
+    for (int j = wv; j < Q; j += kWaves) {
+      int carry = 0;
+      for (int w0 = 0; w0 < qw; w0 += 64) {
+        const int w = w0 + lane;
+        const int c = w < qw ? __popc(qbits[j * QW + w]) : 0;
+        int x = c;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const int y = __shfl_up(x, d, 64);
+          if (lane >= d) x += y;
+        }
+        if (w < qw) qpre[j * QW + w] = static_cast<uint16_t>(carry + x - c);
+        carry += __shfl(x, 63, 64);
+      }
+      if (lane == 0) {
+        if (qcnt[j] > carry) qflag[j] = 1;
+        qcnt[j] = carry;           // the chunk's distinct rows of the query
+      }
+    }
+    __syncthreads();
+    // each query's rows of the chunk at its next positions in rank (= row)
+    // order, codes from the union's list (rank order)
+    for (int x = tid; x < Q * qw; x += kThreads) {
+      const int j = x / qw, w = x - j * qw;
+      uint32_t bits = qbits[j * QW + w];
+      int32_t* dst = stage + j * k + qbase[j] + qpre[j * QW + w];
+      const int32_t* src = uloc + union_base + w * 32;
+      while (bits) {
+        const int b = __ffs(bits) - 1;
+        bits &= bits - 1;
+        *dst++ = src[b];
+      }
+    }
+    __syncthreads();
+    if (tid < Q) qbase[tid] += qcnt[tid];
+    union_base += chunk_union;
+  }
+  __syncthreads();
+  for (int i = tid; i < QK; i += kThreads) {
+    const int j = i / k;
+    sloc[i] = qflag[j] ? loc[i] : (i - j * k < qbase[j] ? stage[i] : -1);
+  }
+}
+
 }  // namespace
+
+size_t plan_order_lds_bytes(int Q, int k, int chunk_words) {
+  const int QW = (std::min(Q * k, chunk_words * 32) + 31) / 32;
+  return region_a_bytes(Q * k, chunk_words) + align16(size_t(Q) * QW * 4) + align16(size_t(Q) * QW * 2) +
+         size_t(Q) * 3 * 4 + size_t(kWaves + 1) * 4;
+}
 
 size_t plan_lds_bytes(int Q, int k, int B, int chunk_words, int sort_cap) {
   const int pwords = (B + 31) / 32;
@@ -439,6 +604,9 @@ hipError_t plan_init_attributes() {
   if (e == hipSuccess)
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(plan_victims_kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(plan_order_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   return e;
 }
 
@@ -447,6 +615,15 @@ hipError_t launch_plan(const PlanArgs& a, size_t lds, hipStream_t s, hipEvent_t 
     hipExtLaunchKernelGGL(plan_resolve_kernel, dim3(a.N), dim3(kThreads), uint32_t(lds), s, ev_start, ev_stop, 0, a);
   } else {
     hipLaunchKernelGGL(plan_resolve_kernel, dim3(a.N), dim3(kThreads), lds, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_plan_order(const PlanArgs& a, size_t lds, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
+  if (ev_start || ev_stop) {
+    hipExtLaunchKernelGGL(plan_order_kernel, dim3(a.N), dim3(kThreads), uint32_t(lds), s, ev_start, ev_stop, 0, a);
+  } else {
+    hipLaunchKernelGGL(plan_order_kernel, dim3(a.N), dim3(kThreads), lds, s, a);
   }
   return hipGetLastError();
 }

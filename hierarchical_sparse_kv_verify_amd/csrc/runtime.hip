@@ -78,7 +78,7 @@ unsigned char* scratch_on_device(int device, hipError_t* err) {
   return addr[device];
 }
 
-enum TimedKind { K_RING = 0, K_PLAN, K_GATHER, K_ATTN, K_COMBINE, K_PROMOTE, K_VICTIMS, K_NUM };
+enum TimedKind { K_RING = 0, K_PLAN, K_GATHER, K_ATTN, K_COMBINE, K_PROMOTE, K_VICTIMS, K_ORDER, K_NUM };
 
 struct Group {
   int leader = 0;                   // group whose plan this group uses (itself unless a follower)
@@ -95,6 +95,7 @@ struct Group {
   int32_t* ring_lo = nullptr;
   int32_t *union_rows = nullptr, *union_loc = nullptr, *miss_rows = nullptr, *victims = nullptr;
   int32_t *loc = nullptr, *req_info = nullptr;
+  int32_t* sloc = nullptr;          // the codes in each query's row order (row_order handles)
   uint32_t* protect = nullptr;      // [N][ceil(B/32)] slots protected by this step's hits
   hipEvent_t ev_done = nullptr;     // copy-backs of the group's last step finished
   bool done_recorded = false;
@@ -183,6 +184,8 @@ struct kv_hier {
   int all_splits = 1, all_hpw = 64;
   std::vector<int> chunk_lo, chunk_splits, chunk_hpw;
   int chunk_words = 0, sort_cap = 1;
+  bool row_order = false;           // the order kernel writes row-ordered lists, which the attention walks
+  size_t order_lds = 0;
   size_t plan_lds = 0;
   hipStream_t side = nullptr;       // host fetch
   hipStream_t work = nullptr;       // the rest of the step when CUs are partitioned (else null)
@@ -495,6 +498,7 @@ void free_all(kv_hier* h) {
     if (G.ev_done) (void)hipEventDestroy(G.ev_done);
     if (G.ev_sel) (void)hipEventDestroy(G.ev_sel);
     (void)hipFree(G.loc);
+    (void)hipFree(G.sloc);
     (void)hipFree(G.req_info);
     (void)hipFree(G.req_counts);
     (void)hipFree(G.cum);
@@ -779,6 +783,13 @@ static int create_impl(kv_hier* h) {
     h->chunk_words = int(cw);
     h->plan_lds = plan_lds_bytes(c.q_max, c.topk, B, h->chunk_words, sc);
     if (h->plan_lds > 160 * 1024) return fail(h, KV_EUNSUPPORTED, "plan LDS %zu", h->plan_lds);
+    // the row-ordered lists (the order kernel's per-query bitmaps beside the
+    // resolution's row chunk); without them the attention walks the
+    // selection order
+    // (they are ordered before the attention through the fetches on the fetch
+    // stream, so a handle with one request chunk has none)
+    h->order_lds = plan_order_lds_bytes(c.q_max, c.topk, h->chunk_words);
+    h->row_order = h->order_lds <= 160 * 1024;
   }
   // the plan and attention kernels take more than 64 KB of dynamic LDS (set
   // per device: every handle sets it on its own)
@@ -806,6 +817,7 @@ static int create_impl(kv_hier* h) {
     for (int i = 0; i <= nch; ++i) h->chunk_lo.push_back(int(int64_t(N) * i / nch));
   }
   h->n_chunks = int(h->chunk_lo.size()) - 1;
+  if (h->n_chunks < 2) h->row_order = false;
   {
     // heads per workgroup and key splits per launch: about 256 workgroups
     // per launch (the combine pass merges the splits); partials are indexed
@@ -869,6 +881,7 @@ static int create_impl(kv_hier* h) {
     if ((rc = dev_alloc(h, &G.victims, NQK, &h->bytes_maps))) return rc;
     if ((rc = dev_alloc(h, &G.protect, size_t(N) * ((c.hot_slots + 31) / 32), &h->bytes_maps))) return rc;
     if ((rc = dev_alloc(h, &G.loc, NQK, &h->bytes_maps))) return rc;
+    if (h->row_order && (rc = dev_alloc(h, &G.sloc, NQK, &h->bytes_maps))) return rc;
     if ((rc = dev_alloc(h, &G.req_info, size_t(N) * I_NUM, &h->bytes_maps))) return rc;
     if ((rc = dev_alloc(h, &G.req_counts, size_t(N) * C_NUM, &h->bytes_maps))) return rc;
     if ((rc = dev_alloc(h, &G.cum, size_t(C_NUM), &h->bytes_maps))) return rc;
@@ -1066,6 +1079,7 @@ int kv_hier_info_get(kv_hier_t* h, kv_hier_info* out) {
   out->attn_splits = h->splits;
   out->attn_head_groups = h->head_groups;
   out->attn_reuse_head_groups = (h->cfg.n_heads + h->all_hpw - 1) / h->all_hpw;
+  out->attn_row_order = h->row_order ? 1 : 0;
   out->plan_rows_per_pass = h->chunk_words * 32;
   return KV_OK;
 }
@@ -1348,6 +1362,7 @@ static int verify_step_impl(kv_hier_t* h, int g, const void* queries, const int3
     pa.victims = G.victims;
     pa.protect = G.protect;
     pa.loc = G.loc;
+    pa.sloc = h->row_order ? G.sloc : nullptr;
     pa.req_info = G.req_info;
     pa.req_counts = G.req_counts;
     pa.cum = G.cum;
@@ -1376,6 +1391,18 @@ static int verify_step_impl(kv_hier_t* h, int g, const void* queries, const int3
     ti = time_begin(h, K_VICTIMS, g, h->aux);
     HIPCHK(h, launch_plan_victims(pa, h->plan_lds, h->aux));
     time_end(h, ti, h->aux);
+    // the row-ordered lists on the fetch stream, ahead of every fetch issued
+    // there: they run beside the first chunk's fetch, and the attention of
+    // every chunk fetched there (all but the leader's first) is ordered after
+    // them through its fetch.  A wait of the caller's stream for a kernel on
+    // the copy-back stream instead slowed every later attention launch by a
+    // quarter (127 -> 159 us at the 128-request shape).
+    if (h->row_order) {
+      HIPCHK(h, hipStreamWaitEvent(h->side, h->ev_planned, 0));
+      ti = time_begin(h, K_ORDER, g, h->side);
+      HIPCHK(h, launch_plan_order(pa, h->order_lds, h->side));
+      time_end(h, ti, h->side);
+    }
 
     // host fetch of every chunk, for this group and then for every follower
     // layer of its plan (one selection starts the transfers of all of them;
@@ -1452,6 +1479,10 @@ static int verify_step_impl(kv_hier_t* h, int g, const void* queries, const int3
     at.splits = h->chunk_splits[ch];
     at.hpw = h->chunk_hpw[ch];
     at.head_groups = (c.n_heads + at.hpw - 1) / at.hpw;
+    // the row-ordered lists, for every chunk fetched on the fetch stream
+    // (after them); the leader's first chunk, fetched here right after the
+    // plan, walks the selection order
+    at.loc = h->row_order && !(lead && ch == 0) ? P.sloc : P.loc;
     // the leader's first chunk was fetched on this stream
     if (!(lead && ch == 0)) HIPCHK(h, hipStreamWaitEvent(s, h->ev_fetched[G.member][ch], 0));
     if ((rc = attend(h, g, at, s))) return rc;
@@ -1735,6 +1766,8 @@ int kv_hier_stats(kv_hier_t* h, int g, kv_hier_counters* cum, kv_hier_counters* 
       o->n_combine = G.nt[K_COMBINE];
       o->n_promote = G.nt[K_PROMOTE];
       o->n_victims = G.nt[K_VICTIMS];
+      o->ms_order = G.ms[K_ORDER];
+      o->n_order = G.nt[K_ORDER];
     }
   };
   if (cum) {

@@ -181,6 +181,8 @@ typedef struct {
   int64_t n_ring, n_plan, n_gather, n_attn, n_combine, n_promote, n_victims;
   int64_t union_tail;       /* distinct rows resolved from the tail (the ring)           */
   int64_t sel_tail;         /* selections resolved from the tail                         */
+  double ms_order;          /* the row-ordered lists (timed as the kernels above)        */
+  int64_t n_order;
 } kv_hier_counters;
 
 /* Per-request lists of the last verify_step of a group (kv_hier_last_lists).
@@ -206,6 +208,13 @@ typedef struct {
                                over row ranges (the q_max*topk location codes share the
                                bitmap's LDS)                                             */
   int32_t attn_reuse_head_groups; /* the same for a launch over every request (Reuse)      */
+  int32_t attn_row_order;   /* 1: the attention of every request chunk but a leader's
+                               first (and of Reuse layers) walks each query's rows in
+                               ascending row order, written after the resolution beside the
+                               first fetch from its selection-order locations (a query that
+                               repeats a row keeps its selection order); 0: selection order
+                               everywhere (one request chunk, or the per-query bitmaps do
+                               not fit one workgroup's LDS)                              */
 } kv_hier_info;
 
 /* Creates a handle ("Adaptive DHiSparse" §2.2 fixed-cache offloading and

@@ -422,11 +422,16 @@ def test_ring_block_only_reading():
     pair.lib.close()
 
 
-def test_outputs_bitwise_identical_across_cache_states():
+@pytest.mark.parametrize("n_chunks", [1, 3])
+def test_outputs_bitwise_identical_across_cache_states(n_chunks):
+    """The sum order depends only on the lists: cold, warm and resident caches
+    give bitwise identical outputs, also where the attention walks the
+    row-ordered lists (every request chunk but the first)."""
     w = _mla_small(n_groups=1, var_k=False)
     outs, misses, unions = [], [], []
     for warm, rho in ((False, 0.0), (True, 0.0), (True, 0.5)):
-        pair = build_pair(w, warm=warm, rho=rho, with_oracle=False)
+        pair = build_pair(w, warm=warm, rho=rho, with_oracle=False, lib_kw=dict(n_chunks=n_chunks))
+        assert pair.lib.info["attn_row_order"] == (1 if n_chunks > 1 else 0), pair.lib.info
         si = make_step_inputs(w, 0, 0, pair.hist_len)
         outs.append(run_lib_step(pair, 0, si))
         _, last = pair.lib.stats(0)
@@ -646,20 +651,27 @@ def test_compressed_source_rounds():
     pair.lib.close()
 
 
-@pytest.mark.parametrize("layout", ["tiny", "mla"])
+@pytest.mark.parametrize("layout", ["tiny", "mla", "mla_chunks"])
 def test_repeated_entries_within_a_list(layout):
     """Reading R2: a row selected twice by one query is two terms of its
     softmax (eq. 12 gives every entry a location), while the union holds it
     once and the host fetch copies it once.  Repeats are planted in the
     generated lists (the generator draws distinct entries): within a query,
-    across the two halves of one list and at both ends."""
+    across the two halves of one list and at both ends.  With three request
+    chunks the attention of chunks 1 and 2 walks the row-ordered lists, and a
+    query with repeats keeps its selection order (repeats planted in every
+    other query there, so both kinds meet in one step)."""
     w = _tiny(n_req=2) if layout == "tiny" else _mla_small(n_groups=1, n_req=3)
-    pair = build_pair(w)
+    pair = build_pair(w, lib_kw=dict(n_chunks=3) if layout == "mla_chunks" else None)
+    if layout == "mla_chunks":
+        assert pair.lib.info["attn_row_order"] == 1, pair.lib.info
     si = make_step_inputs(w, 0, 0, pair.hist_len)
     rng = np.random.default_rng(7)
     planted = 0
     for r in range(w.n_req):
         for j in range(int(si.k_active[r])):
+            if layout == "mla_chunks" and j % 2 == 1:
+                continue
             lst = si.topk[r, j]
             valid = np.flatnonzero((lst >= 0) & (lst < int(pair.hist_len[r])))
             src = rng.choice(valid, size=min(12, valid.size // 2), replace=False)
