@@ -56,18 +56,30 @@ __global__ __launch_bounds__(64) void miss_gather_kernel(HostRowSrc src, const i
   }
 }
 
+// Staged rows copied into their victim slots with the fetch's 32-bit
+// incremental indices: the kernel stays within 16 VGPRs, so a promote wave and
+// a fetch wave together fit beside two attention waves on one SIMD.  (Each
+// attention wave holds 240 of the SIMD's 512 registers; with a wider promote
+// wave, a CU whose SIMD already carries a fetch wave cannot take its attention
+// workgroup until the promote ends, and the whole launch waits for it.)
 __global__ __launch_bounds__(256) void promote_kernel(const uint4* __restrict__ staging,
                                                       const int32_t* __restrict__ victims,
                                                       const int32_t* __restrict__ req_info,
                                                       uint4* __restrict__ hot, int QK, int B, int row16, int r0) {
   const int r = r0 + blockIdx.y;
   const int n = req_info[r * I_NUM + I_NPROMOTE];
-  const size_t total = size_t(n) * row16;
-  const size_t stride = size_t(gridDim.x) * blockDim.x;
-  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
-    const int row = static_cast<int>(i / row16), c = static_cast<int>(i % row16);
-    const int slot = victims[size_t(r) * QK + row];
-    hot[(size_t(r) * B + slot) * row16 + c] = staging[(size_t(r) * QK + row) * row16 + c];
+  const int32_t* vic = victims + size_t(r) * QK;
+  const uint4* src = staging + size_t(r) * QK * row16;
+  uint4* dst = hot + size_t(r) * B * row16;
+  const int stride = gridDim.x * blockDim.x;
+  const int drow = stride / row16, dc = stride - drow * row16;
+  const int i0 = blockIdx.x * blockDim.x + threadIdx.x;
+  int row = i0 / row16, c = i0 - row * row16;
+  while (row < n) {
+    dst[size_t(vic[row]) * row16 + c] = src[size_t(row) * row16 + c];
+    row += drow;
+    c += dc;
+    if (c >= row16) { c -= row16; ++row; }
   }
 }
 
