@@ -651,6 +651,467 @@ __global__ __launch_bounds__(C::NT, 1) void attn_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Rows of 72 16-byte chunks (absorbed MLA: K = all 576 elements, V = the
+// first 512) at 64 heads per workgroup: a wave-specialised pipeline with one
+// barrier per 32-row tile.
+//  - four score waves own 16 heads each over the whole key width (their Q
+//    fragments stay in registers): S^T = K Q^T with v_mfma_f32_16x16x32_bf16,
+//    tile rows in M and heads in N, so the 32 scores of a head are complete
+//    in four lanes of one wave and no partial scores cross waves.  The
+//    online softmax runs there (per head; the max is raised lazily as
+//    above), and the probabilities go to LDS as bf16 P^T together with each
+//    head's rescale factor and a per-wave flag.
+//  - four product waves own a quarter of the value width for all 64 heads:
+//    O^T += V^T P^T with v_mfma_f32_32x32x16_bf16, V^T through
+//    ds_read_b64_tr_b16 in the layout above.
+//  - score waves work on tile t+1 while product waves fold tile t into O; a
+//    wave of each kind sits on every SIMD, so the products of one overlap the
+//    fragment reads and softmax of the other.
+//  - tiles reach LDS by DMA in the head-region / swizzled-tail layout above,
+//    four buffers: tile t+3 is issued while tiles t+1 (scores) and t
+//    (products) are read, giving each tile two tile-times to land.  The first
+//    product wave DMAs the location codes into a shared ring of slots, four
+//    tiles ahead.
+template <int D_QK_, int V_OFF_, int D_V_, int ROW_>
+struct WCfg {
+  static constexpr int D_QK = D_QK_, V_OFF = V_OFF_, D_V = D_V_, ROW = ROW_;
+  static constexpr int NS = 4;                 // score waves (16 heads each)
+  static constexpr int NP = 4;                 // product waves (a quarter of the value width each)
+  static constexpr int NW = NS + NP;
+  static constexpr int NT = NW * 64;
+  static constexpr int KST = D_QK / 32;        // 32-dim k-steps of the score products
+  static constexpr int DVB = D_V / NP / 32;    // 32-dim value blocks of one product wave
+  static constexpr int RCH = ROW / 8;          // 16-byte chunks per row
+  static constexpr int DPW = TILE / NP;        // tile rows DMA'd by one product wave
+  static constexpr int HSTR = 520;             // head-region row stride (elements)
+  static constexpr int TAILO = TILE * HSTR;    // tail region (chunks 64..71)
+  static constexpr int BSTR = TAILO + TILE * 64;
+  static constexpr int RSTR = HSTR;
+  static constexpr int NBUF = 4;
+  static constexpr int PSTR = TILE + 8;        // P^T row stride (elements): 20 banks
+  static constexpr int NVM = DPW + 1;          // DMA instructions per product wave and tile
+  static constexpr size_t LDS_K = size_t(NBUF) * BSTR * 2;
+  static constexpr size_t LDS_P = size_t(2) * 64 * PSTR * 2;   // two P^T slots
+  static constexpr size_t LDS_A = size_t(2) * 64 * 4;          // rescale factors per slot; (m, l) at the end
+  static constexpr size_t LDS_F = 16;                          // rescale flags: a byte per score wave and slot
+  static constexpr size_t LDS_C = size_t(4) * 64 * 4;          // code slots (lanes l, l+32: row l)
+  static constexpr size_t LDS = LDS_K + LDS_P + LDS_A + LDS_F + LDS_C;
+  static_assert(D_QK % 32 == 0 && D_V % (NP * 32) == 0 && RCH == 72 && DPW == 8, "shape");
+  static_assert(V_OFF % 8 == 0 && V_OFF + D_V <= ROW && D_QK <= ROW, "row layout");
+  static_assert(LDS <= 160 * 1024, "LDS");
+};
+
+// Score k-step ks of lane quarter g: first chunk of the k-step's head-region
+// block, the quarter's chunk, and the row permutation of the A fragment.
+__host__ __device__ constexpr int ws_base(int ks) { return 16 * (ks / 4) + 2 * (ks % 4); }
+__device__ __forceinline__ int ws_chunk(int ks, int g) {
+  return ks < 16 ? ws_base(ks) + ((g & 1) << 3) + (g >> 1) : 64 + 4 * (ks - 16) + g;
+}
+__device__ __forceinline__ int ws_row(int m) { return m ^ (((m >> 3) & 1) << 2); }
+
+// max / sum over lanes l and l^16 (l^32) without LDS: the gfx950 lane swaps
+// return (lower lane's value, upper lane's value) in every lane of the pair
+__device__ __forceinline__ float max_x16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_x32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_x16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_x32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Tile DMA by a product wave wp: rows wp*DPW .. +DPW-1 of the tile, one
+// instruction per row for chunks 0..63 and one for their chunks 64..71 (lane:
+// row lane/8, slot lane%8).  Row bases are taken by readlane from the lanes
+// holding the rows' codes; the tail instruction's base is selected from them.
+template <class C>
+struct WsDma {
+  uintptr_t base[C::DPW];
+  uintptr_t tail;
+};
+template <class C>
+__device__ __forceinline__ void ws_dma_prepare(WsDma<C>& d, const RowCtx& ctx, int code, int wp, int lane) {
+  const uintptr_t my = row_addr<C::ROW>(ctx, code);
+  const int mlo = static_cast<int>(static_cast<uint32_t>(my));
+  const int mhi = static_cast<int>(static_cast<uint32_t>(my >> 32));
+#pragma unroll
+  for (int u = 0; u < C::DPW; ++u)
+    d.base[u] = (uintptr_t(uint32_t(__builtin_amdgcn_readlane(mhi, wp * C::DPW + u))) << 32) |
+                uint32_t(__builtin_amdgcn_readlane(mlo, wp * C::DPW + u));
+  const int rs = lane >> 3;
+  uintptr_t tb = d.base[0];
+#pragma unroll
+  for (int u = 1; u < C::DPW; ++u) tb = rs == u ? d.base[u] : tb;
+  d.tail = tb + size_t(64 + ((lane & 7) ^ tail_swz(wp * C::DPW + rs))) * 16;
+}
+template <class C>
+__device__ __forceinline__ void ws_dma_row(const WsDma<C>& d, uint16_t* dst, int u, int wp, int lane) {
+  dma16(d.base[u] + size_t(lane) * 16, dst + (wp * C::DPW + u) * C::HSTR);
+}
+template <class C>
+__device__ __forceinline__ void ws_dma_tail(const WsDma<C>& d, uint16_t* dst, int wp) {
+  dma16(d.tail, dst + C::TAILO + wp * C::DPW * 64);
+}
+
+template <class C>
+__global__ __launch_bounds__(C::NT, 1) void attn_ws_kernel(AttnArgs a) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  uint16_t* Kb = reinterpret_cast<uint16_t*>(lds);
+  uint16_t* Pb = reinterpret_cast<uint16_t*>(lds + C::LDS_K);
+  float* Al = reinterpret_cast<float*>(lds + C::LDS_K + C::LDS_P);
+  uint32_t* Fl = reinterpret_cast<uint32_t*>(lds + C::LDS_K + C::LDS_P + C::LDS_A);
+  int32_t* Cs = reinterpret_cast<int32_t*>(lds + C::LDS_K + C::LDS_P + C::LDS_A + C::LDS_F);
+
+  const int nreq = a.r1 - a.r0;
+  const int per_req = a.Q * a.head_groups * a.splits;
+  const int b = blockIdx.x;
+  const int rr = ((b >> 3) / per_req) * 8 + (b & 7);
+  if (rr >= nreq) return;
+  const int sub = (b >> 3) % per_req;
+  const int j = sub / (a.head_groups * a.splits);
+  const int hg = (sub / a.splits) % a.head_groups;
+  const int sp = sub % a.splits;
+  const int r = a.r0 + rr;
+  const int qi = r * a.Q + j;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);      // wave-uniform: held in SGPRs
+  const bool score_wave = w < C::NS;
+  const int hi_half = lane >> 5;
+  const int dq = w - C::NS;                                    // product waves: value quarter
+  const int vq0 = dq * (C::D_V / C::NP);
+  const size_t blk = (size_t(qi - a.r0 * a.Q) * a.head_groups + hg) * a.splits + sp;   // from the chunk's start
+
+  const int p_j = a.causal[qi];
+  if (p_j < 0) {  // inactive query: zero output (the combine pass does it when split)
+    if (!score_wave && a.splits == 1) {
+      for (int hb = 0; hb < 2; ++hb) {
+        const int head = hg * 64 + hb * 32 + (lane & 31);
+        if (head < a.H) {
+          uint16_t* op = a.out + (size_t(qi) * a.H + head) * C::D_V + vq0;
+          for (int d = hi_half; d < C::D_V / C::NP / 4; d += 2)
+            *reinterpret_cast<uint2*>(op + d * 4) = make_uint2(0, 0);
+        }
+      }
+    }
+    return;
+  }
+  const int n_r = a.causal[size_t(r) * a.Q];
+  int lo = a.ring_lo[r];
+  lo = max(lo, p_j - a.W + 1);
+  lo = max(lo, 0);
+  if (a.block_only) lo = max(lo, n_r);
+  const int n_ring = p_j >= lo ? p_j - lo + 1 : 0;
+
+  RowCtx ctx;
+  ctx.loc = reinterpret_cast<gint32*>(reinterpret_cast<uintptr_t>(a.loc + size_t(qi) * a.k));
+  ctx.k = a.k;
+  ctx.n_total = a.k + n_ring;
+  ctx.Rd = a.Rd;
+  ctx.ring_row0 = r * a.Rd + lo % a.Rd;
+  ctx.ring_end = (r + 1) * a.Rd;
+  ctx.hot = reinterpret_cast<uintptr_t>(a.hot);
+  ctx.d_staging = reinterpret_cast<uintptr_t>(a.staging) - ctx.hot;
+  ctx.d_resident = reinterpret_cast<uintptr_t>(a.resident) - ctx.hot;
+  ctx.d_ring = reinterpret_cast<uintptr_t>(a.ring) - ctx.hot;
+  ctx.zero = reinterpret_cast<uintptr_t>(a.zero);
+
+  const int n_tiles = (ctx.n_total + TILE - 1) / TILE;
+  const int tb = int((long long)n_tiles * sp / a.splits);
+  const int te = int((long long)n_tiles * (sp + 1) / a.splits);
+  const int crow = lane & 31;                          // tile row whose code this lane holds
+  const float sl2 = a.scale_log2;
+
+  // tile t lives in buffer (t - tb) mod 4, its codes in slot (t - tb) mod 4,
+  // its probabilities in P^T slot (t - tb) mod 2
+  auto kbuf = [&](int t) { return Kb + ((t - tb) & 3) * C::BSTR; };
+  auto cslot = [&](int t) { return Cs + ((t - tb) & 3) * 64; };
+  // DMA of tile t (its codes landed): every wave moves RPW rows; tiles past
+  // the range read the zero row, so every wave keeps NVM instructions per tile
+  auto tile_code = [&](int t, int raw) { return t < te ? final_code(ctx, t * TILE + crow, raw) : -1; };
+
+  if (score_wave) {
+    // ---- score waves: heads hs of this wave.  A k-step's 32 dims are four
+    // 16-byte chunks, one per lane quarter g = lane/16: chunk ws_chunk(ks, g)
+    // (head region: 16(ks/4) + 2(ks%4) + {0, 8, 1, 9}[g]; tail: 64 + 4(ks-16)
+    // + g).  The A fragment (K) of lane l holds tile row 16rb + ws_row(l%16),
+    // where ws_row flips bit 2 of rows 8..15: with the chunk offsets this puts
+    // the 16 lanes of every LDS service group of a 16-byte read (lanes of
+    // equal bit 5 and equal parity of bits 2..4) on 16 distinct bank quads.
+    // The B fragment (Q) takes the same chunks.
+    const int g = lane >> 4;
+    const int hs = hg * 64 + w * 16 + (lane & 15);
+    bf16x8 qreg[C::KST];
+    {
+      const uint16_t* qp = a.q + (size_t(qi) * a.H + (hs < a.H ? hs : 0)) * C::D_QK;
+#pragma unroll
+      for (int ks = 0; ks < C::KST; ++ks) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (hs < a.H) v = gload16(reinterpret_cast<uintptr_t>(qp + ws_chunk(ks, g) * 8));
+        qreg[ks] = __builtin_bit_cast(bf16x8, v);
+      }
+    }
+    float m_run = kNegBig, l_run = 0.f;
+    // A fragment offsets: the head region (plus 8 ws_base(ks) per k-step)
+    // and the two tail k-steps
+    int koff[2], ktail[2][2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int row = rb * 16 + ws_row(lane & 15);
+      koff[rb] = row * C::HSTR + ws_chunk(0, g) * 8;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) ktail[rb][kt] = C::TAILO + row * 64 + (((kt * 4 + g) ^ tail_swz(row)) * 8);
+    }
+    // this lane's scores: D rows 4g + i of each 16-row block = tile rows
+    // 16rb + ws_row(4g) + i; P^T written there (head 16w + lane%16)
+    const int prow = ws_row(4 * g);
+    const int pw_off = (w * 16 + (lane & 15)) * C::PSTR + prow;
+
+    auto score_tile = [&](int t) {
+      const uint16_t* kb = kbuf(t);
+      const int ps = (t - tb) & 1;
+      const int code = final_code(ctx, t * TILE + crow, cslot(t)[lane]);
+      const uint32_t live = static_cast<uint32_t>(__builtin_amdgcn_ballot_w64(code >= 0));
+      typedef float f32x4 __attribute__((ext_vector_type(4)));
+      f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      // K fragments in batches of KB k-steps, the next batch's reads issued
+      // before this batch's products (12 reads in flight)
+      constexpr int KB = 6, NBT = C::KST / KB;
+      static_assert(C::KST % KB == 0, "k-step batches");
+      bf16x8 fr[2][2][KB];
+      auto load = [&](int bt, bf16x8 (&dst)[2][KB]) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int jj = 0; jj < KB; ++jj) {
+            const int ks = bt * KB + jj;
+            const int off = ks < 16 ? koff[rb] + ws_base(ks) * 8 : ktail[rb][ks - 16];
+            dst[rb][jj] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + off));
+          }
+      };
+      load(0, fr[0]);
+#pragma unroll
+      for (int bt = 0; bt < NBT; ++bt) {
+        if (bt + 1 < NBT) load(bt + 1, fr[(bt + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int jj = 0; jj < KB; ++jj)
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+            acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[bt & 1][rb][jj], qreg[bt * KB + jj], acc[rb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      float s[8];
+      float mt = -INFINITY;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = rb * 16 + prow + i;
+          s[rb * 4 + i] = (live >> row) & 1u ? acc[rb][i] * sl2 : -INFINITY;
+          mt = fmaxf(mt, s[rb * 4 + i]);
+        }
+      mt = max_x32(max_x16(mt));
+      const bool raise = mt > m_run + kRescaleLog2;
+      float alpha = 1.f;
+      if (raise) {
+        alpha = __builtin_amdgcn_exp2f(m_run - mt);
+        m_run = mt;
+        l_run *= alpha;
+      }
+      float ps_sum = 0.f;
+      uint16_t* pw = Pb + ps * (64 * C::PSTR) + pw_off;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[i] = __builtin_amdgcn_exp2f(s[rb * 4 + i] - m_run);
+          ps_sum += p[i];
+        }
+        uint2 pk;
+        pk.x = uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(p[0]))) |
+               (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(p[1]))) << 16);
+        pk.y = uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(p[2]))) |
+               (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(p[3]))) << 16);
+        *reinterpret_cast<uint2*>(pw + rb * 16) = pk;
+      }
+      l_run += ps_sum;
+      if (lane < 16) Al[ps * 64 + w * 16 + lane] = alpha;
+      const bool any = __builtin_amdgcn_ballot_w64(raise) != 0;
+      if (lane == 0) reinterpret_cast<uint8_t*>(Fl + ps)[w] = any ? 1 : 0;
+    };
+
+    // prologue: Q in registers, codes of tb..tb+2 (first product wave), then
+    // tiles tb..tb+2; scores of tile tb
+    __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0)
+    lds_barrier();
+    lds_barrier();                                   // tiles tb, tb+1 landed
+    if (tb < te) score_tile(tb);
+    lds_barrier();
+    for (int t = tb; t < te; ++t) {
+      if (t + 1 < te) score_tile(t + 1);
+      lds_barrier();
+    }
+    __builtin_amdgcn_s_waitcnt(0x0070);              // vmcnt(0): no DMA outlives the loop
+    __syncthreads();
+    // (m, l) of this wave's heads: the four lanes of a head in a fixed order
+    const float l2 = sum_x32(sum_x16(l_run));
+    if (lane < 16) {
+      Al[w * 16 + lane] = m_run;
+      Al[64 + w * 16 + lane] = l2;
+    }
+    __syncthreads();
+  } else {
+    // ---- product waves: value dims vq0 .. vq0 + D_V/NP - 1 of all 64 heads
+    f32x16 O[C::DVB][2];
+#pragma unroll
+    for (int d = 0; d < C::DVB; ++d)
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) O[d][hb][i] = 0.f;
+    int v_off;
+    {
+      const int gq = (lane >> 4) & 3, s4 = lane & 15, aq = s4 & 3;
+      const int row = (gq >> 1) * 8 + (s4 >> 2);
+      const int dim = C::V_OFF + vq0 + ((gq & 1) * 2 + (aq >> 1)) * (8 * C::DVB) + (aq & 1) * 4;
+      v_off = row * C::RSTR + dim;
+    }
+    const int pr_off = (lane & 31) * C::PSTR + hi_half * 8;
+
+    const int wp = dq;                               // product wave index: DMA rows wp*DPW ..
+    auto issue_all = [&](int t, int raw) {
+      WsDma<C> dm;
+      ws_dma_prepare<C>(dm, ctx, tile_code(t, raw), wp, lane);
+      uint16_t* dst = kbuf(t);
+      ws_dma_tail<C>(dm, dst, wp);
+#pragma unroll
+      for (int u = 0; u < C::DPW; ++u) ws_dma_row<C>(dm, dst, u, wp, lane);
+    };
+    // products of tile t, with the DMA of tile t+3 (codes raw3) issued between
+    // them, so that the address unit works while the matrix core does
+    auto product_tile = [&](int t, int raw3) {
+      const uint16_t* kb = kbuf(t);
+      const int ps = (t - tb) & 1;
+      WsDma<C> dm;
+      ws_dma_prepare<C>(dm, ctx, tile_code(t + 3, raw3), wp, lane);
+      uint16_t* dst = kbuf(t + 3);
+      if (Fl[ps] != 0) {
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          const float al = Al[ps * 64 + hb * 32 + (lane & 31)];
+#pragma unroll
+          for (int d = 0; d < C::DVB; ++d)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) O[d][hb][i] *= al;
+        }
+      }
+      const uint16_t* pr = Pb + ps * (64 * C::PSTR) + pr_off;
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2) {
+        bf16x8 vfr[C::DVB];
+#pragma unroll
+        for (int d = 0; d < C::DVB; ++d) {
+          const uint16_t* vp = kb + v_off + ks2 * 16 * C::RSTR + d * 8;
+          const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp));
+          const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 4 * C::RSTR));
+          vfr[d] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+        bf16x8 pbf[2];
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+          pbf[hb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(pr + hb * 32 * C::PSTR + ks2 * 16));
+        // 8 products; DMA instructions after products 0..4 (k-step 0: the
+        // tail and rows 0..3; k-step 1: rows 4..7)
+#pragma unroll
+        for (int x = 0; x < 2 * C::DVB; ++x) {
+          const int d = x >> 1, hb = x & 1;
+          O[d][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[d], pbf[hb], O[d][hb], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          if (ks2 == 0 && x == 0) ws_dma_tail<C>(dm, dst, wp);
+          if (ks2 == 0 && x >= 1 && x <= 4) ws_dma_row<C>(dm, dst, x - 1, wp, lane);
+          if (ks2 == 1 && x <= 3) ws_dma_row<C>(dm, dst, 4 + x, wp, lane);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
+
+    const bool coder = w == C::NS;                    // the wave that DMAs the codes
+    if (coder) {
+      dma_codes<C>(cslot(tb), ctx, tb, 0, lane);
+      dma_codes<C>(cslot(tb + 1), ctx, tb + 1, 0, lane);
+      dma_codes<C>(cslot(tb + 2), ctx, tb + 2, 0, lane);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0)
+    lds_barrier();
+    issue_all(tb, cslot(tb)[lane]);
+    issue_all(tb + 1, cslot(tb + 1)[lane]);
+    if (coder) dma_codes<C>(cslot(tb + 3), ctx, tb + 3, 0, lane);
+    issue_all(tb + 2, cslot(tb + 2)[lane]);
+    lds_vm_barrier<C::NVM>();                        // tiles tb, tb+1 and the codes of tb+3 landed
+    lds_barrier();                                   // scores of tile tb
+    for (int t = tb; t < te; ++t) {
+      const int raw3 = cslot(t + 3)[lane];
+      if (coder) dma_codes<C>(cslot(t + 4), ctx, t + 4, 0, lane);
+      product_tile(t, raw3);
+      lds_vm_barrier<C::NVM>();                      // tile t+2 and the codes of t+4 landed
+    }
+    __builtin_amdgcn_s_waitcnt(0x0070);              // vmcnt(0): no DMA outlives the loop
+    __syncthreads();
+    __syncthreads();                                 // (m, l) of every head in LDS
+
+    // O^T register i of block d holds value dim vq0 + (i/4)*8*DVB + d*8 + hi*4 + i%4
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const int hl = hb * 32 + (lane & 31);
+      const int head = hg * 64 + hl;
+      const float l_tot = Al[64 + hl];
+      if (a.splits == 1) {
+        if (head < a.H) {
+          const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+          uint16_t* op = a.out + (size_t(qi) * a.H + head) * C::D_V + vq0 + hi_half * 4;
+#pragma unroll
+          for (int d = 0; d < C::DVB; ++d)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              uint16_t h4[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                h4[e] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(O[d][hb][g4 * 4 + e] * inv));
+              uint2 pk;
+              pk.x = uint32_t(h4[0]) | (uint32_t(h4[1]) << 16);
+              pk.y = uint32_t(h4[2]) | (uint32_t(h4[3]) << 16);
+              *reinterpret_cast<uint2*>(op + g4 * 8 * C::DVB + d * 8) = pk;
+            }
+        }
+      } else {
+        float* po = a.part_o + (blk * 64 + hl) * C::D_V + vq0 + hi_half * 4;
+#pragma unroll
+        for (int d = 0; d < C::DVB; ++d)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4)
+            *reinterpret_cast<float4*>(po + g4 * 8 * C::DVB + d * 8) =
+                make_float4(O[d][hb][g4 * 4 + 0], O[d][hb][g4 * 4 + 1], O[d][hb][g4 * 4 + 2], O[d][hb][g4 * 4 + 3]);
+        if (dq == 0 && hi_half == 0) {
+          float* pm = a.part_ml + (blk * 64 + hl) * 2;
+          pm[0] = Al[hl];
+          pm[1] = l_tot;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Narrow rows (144 elements: K = all 144, V = the first 128) above 32 heads.
 // One workgroup = one query x HB 32-head blocks (2: 64 heads, or 4: 128
 // heads, each row then gathered once per query) x one key split.  A wave
@@ -1119,6 +1580,12 @@ hipError_t set_lds_limit() {
 }
 
 template <class C>
+hipError_t set_ws_lds_limit() {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(attn_ws_kernel<C>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, int(C::LDS));
+}
+
+template <class C>
 hipError_t set_narrow_lds_limit() {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(attn_narrow_kernel<C>),
                              hipFuncAttributeMaxDynamicSharedMemorySize, int(C::LDS));
@@ -1153,6 +1620,15 @@ hipError_t launch_cfg(const AttnArgs& a, hipStream_t s, hipEvent_t ev_start, hip
 }
 
 template <class C>
+hipError_t launch_ws(const AttnArgs& a, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
+  const int nreq = a.r1 - a.r0;
+  if (nreq <= 0) return no_launch(s, ev_start, ev_stop);
+  const int per_req = a.Q * a.head_groups * a.splits;
+  const long long blocks = (long long)((nreq + 7) / 8) * 8 * per_req;
+  return launch_with(attn_ws_kernel<C>, dim3(unsigned(blocks)), dim3(C::NT), C::LDS, s, ev_start, ev_stop, a);
+}
+
+template <class C>
 hipError_t launch_narrow(const AttnArgs& a, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
   const int nreq = a.r1 - a.r0;
   if (nreq <= 0) return no_launch(s, ev_start, ev_stop);
@@ -1165,7 +1641,7 @@ hipError_t launch_narrow(const AttnArgs& a, hipStream_t s, hipEvent_t ev_start, 
 
 hipError_t attn_init_attributes() {
   hipError_t e = set_lds_limit<Cfg<576, 0, 512, 576, 1>>();
-  if (e == hipSuccess) e = set_lds_limit<Cfg<576, 0, 512, 576, 2>>();
+  if (e == hipSuccess) e = set_ws_lds_limit<WCfg<576, 0, 512, 576>>();
   if (e == hipSuccess) e = set_lds_limit<Cfg<128, 128, 128, 256, 1>>();
   if (e == hipSuccess) e = set_lds_limit<Cfg<128, 128, 128, 256, 2>>();
   if (e == hipSuccess) e = set_lds_limit<Cfg<144, 0, 128, 144, 1>>();
@@ -1199,7 +1675,7 @@ hipError_t launch_attn(const AttnArgs& a, int row_elems, int d_qk, int v_off, in
   const int hpw = a.hpw;
   if (row_elems == 576 && d_qk == 576 && v_off == 0 && d_v == 512) {
     if (hpw == 32) return launch_cfg<Cfg<576, 0, 512, 576, 1>>(a, s, ev_start, ev_stop);
-    return launch_cfg<Cfg<576, 0, 512, 576, 2>>(a, s, ev_start, ev_stop);
+    return launch_ws<WCfg<576, 0, 512, 576>>(a, s, ev_start, ev_stop);
   }
   if (row_elems == 256 && d_qk == 128 && v_off == 128 && d_v == 128) {
     if (hpw == 32) return launch_cfg<Cfg<128, 128, 128, 256, 1>>(a, s, ev_start, ev_stop);
