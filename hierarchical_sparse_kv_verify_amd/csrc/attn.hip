@@ -909,17 +909,24 @@ __global__ __launch_bounds__(C::NT, 1) void attn_ws_kernel(AttnArgs a) {
             acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[bt & 1][rb][jj], qreg[bt * KB + jj], acc[rb], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
-      float s[8];
-      float mt = -INFINITY;
+      // tile max per head over the raw scores of live rows (the scale is
+      // positive, so it is applied to the max once); p = exp2(s*scale - m)
+      // with scale and max in one fma
+      float r[8];
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = rb * 16 + prow + i;
-          s[rb * 4 + i] = (live >> row) & 1u ? acc[rb][i] * sl2 : -INFINITY;
-          mt = fmaxf(mt, s[rb * 4 + i]);
-        }
-      mt = max_x32(max_x16(mt));
+        for (int i = 0; i < 4; ++i) r[rb * 4 + i] = acc[rb][i];
+      if (__builtin_expect(live != 0xFFFFFFFFu, 0)) {   // wave-uniform: a tile with masked rows
+        const uint32_t lmask = live >> prow;             // bits i and 16+i: rows prow+i, 16+prow+i
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (!((lmask >> (rb * 16 + i)) & 1u)) r[rb * 4 + i] = -INFINITY;
+      }
+      float mt = fmaxf(fmaxf(fmaxf(r[0], r[1]), fmaxf(r[2], r[3])), fmaxf(fmaxf(r[4], r[5]), fmaxf(r[6], r[7])));
+      mt = max_x32(max_x16(mt)) * sl2;
       const bool raise = mt > m_run + kRescaleLog2;
       float alpha = 1.f;
       if (raise) {
@@ -929,19 +936,21 @@ __global__ __launch_bounds__(C::NT, 1) void attn_ws_kernel(AttnArgs a) {
       }
       float ps_sum = 0.f;
       uint16_t* pw = Pb + ps * (64 * C::PSTR) + pw_off;
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      typedef float f32x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         float p[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          p[i] = __builtin_amdgcn_exp2f(s[rb * 4 + i] - m_run);
+          p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(r[rb * 4 + i], sl2, -m_run));
           ps_sum += p[i];
         }
+        const bf16x2 b01 = __builtin_convertvector(f32x2{p[0], p[1]}, bf16x2);
+        const bf16x2 b23 = __builtin_convertvector(f32x2{p[2], p[3]}, bf16x2);
         uint2 pk;
-        pk.x = uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(p[0]))) |
-               (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(p[1]))) << 16);
-        pk.y = uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(p[2]))) |
-               (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(p[3]))) << 16);
+        pk.x = __builtin_bit_cast(uint32_t, b01);
+        pk.y = __builtin_bit_cast(uint32_t, b23);
         *reinterpret_cast<uint2*>(pw + rb * 16) = pk;
       }
       l_run += ps_sum;
