@@ -817,7 +817,10 @@ static int create_impl(kv_hier* h) {
     for (int i = 0; i <= nch; ++i) h->chunk_lo.push_back(int(int64_t(N) * i / nch));
   }
   h->n_chunks = int(h->chunk_lo.size()) - 1;
-  if (h->n_chunks < 2) h->row_order = false;
+  // lists shorter than 1024 entries keep the selection order: there the order
+  // kernel, beside a short first fetch, costs more than the walk saves
+  // (measured on 288-B rows at k = 512)
+  if (h->n_chunks < 2 || c.topk < 1024) h->row_order = false;
   {
     // heads per workgroup and key splits per launch: about 256 workgroups
     // per launch (the combine pass merges the splits); partials are indexed

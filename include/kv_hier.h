@@ -213,8 +213,9 @@ typedef struct {
                                ascending row order, written after the resolution beside the
                                first fetch from its selection-order locations (a query that
                                repeats a row keeps its selection order); 0: selection order
-                               everywhere (one request chunk, or the per-query bitmaps do
-                               not fit one workgroup's LDS)                              */
+                               everywhere (one request chunk, lists of fewer than 1024
+                               entries, or the per-query bitmaps do not fit one
+                               workgroup's LDS)                                          */
 } kv_hier_info;
 
 /* Creates a handle ("Adaptive DHiSparse" §2.2 fixed-cache offloading and

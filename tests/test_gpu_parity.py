@@ -141,6 +141,7 @@ def _mla_small(**kw):
 def test_mla_two_groups_two_steps(n_chunks, fetch_cus):
     w = _mla_small()
     pair = build_pair(w, lib_kw=dict(n_chunks=n_chunks, fetch_cus=fetch_cus))
+    assert pair.lib.info["attn_row_order"] == 0, pair.lib.info    # 512-entry lists keep selection order
     n = pair.hist_len.copy()
     for step in range(2):
         sis = []
@@ -427,7 +428,7 @@ def test_outputs_bitwise_identical_across_cache_states(n_chunks):
     """The sum order depends only on the lists: cold, warm and resident caches
     give bitwise identical outputs, also where the attention walks the
     row-ordered lists (every request chunk but the first)."""
-    w = _mla_small(n_groups=1, var_k=False)
+    w = _mla_small(n_groups=1, var_k=False, topk=1024)
     outs, misses, unions = [], [], []
     for warm, rho in ((False, 0.0), (True, 0.0), (True, 0.5)):
         pair = build_pair(w, warm=warm, rho=rho, with_oracle=False, lib_kw=dict(n_chunks=n_chunks))
@@ -661,7 +662,8 @@ def test_repeated_entries_within_a_list(layout):
     chunks the attention of chunks 1 and 2 walks the row-ordered lists, and a
     query with repeats keeps its selection order (repeats planted in every
     other query there, so both kinds meet in one step)."""
-    w = _tiny(n_req=2) if layout == "tiny" else _mla_small(n_groups=1, n_req=3)
+    w = (_tiny(n_req=2) if layout == "tiny" else
+         _mla_small(n_groups=1, n_req=3, topk=1024) if layout == "mla_chunks" else _mla_small(n_groups=1, n_req=3))
     pair = build_pair(w, lib_kw=dict(n_chunks=3) if layout == "mla_chunks" else None)
     if layout == "mla_chunks":
         assert pair.lib.info["attn_row_order"] == 1, pair.lib.info
