@@ -883,8 +883,9 @@ __global__ __launch_bounds__(C::NT, 1) void attn_ws_kernel(AttnArgs a) {
       typedef float f32x4 __attribute__((ext_vector_type(4)));
       f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
       // K fragments in batches of KB k-steps, the next batch's reads issued
-      // before this batch's products (12 reads in flight)
-      constexpr int KB = 6, NBT = C::KST / KB;
+      // before this batch's products (batches of 1, 2 or 3 k-steps measure
+      // the same; 6 took 30 more registers and 5% longer, 9 another 10%)
+      constexpr int KB = 3, NBT = C::KST / KB;
       static_assert(C::KST % KB == 0, "k-step batches");
       bf16x8 fr[2][2][KB];
       auto load = [&](int bt, bf16x8 (&dst)[2][KB]) {
